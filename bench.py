@@ -1,0 +1,160 @@
+#!/usr/bin/env python3
+"""Benchmark of the SLA sparse-linear attention forward on one MI355X.
+
+A step is one sla_forward call (pool -> classify -> linear states ->
+marginal-state GEMM -> fused sparse+linear kernel) over the Wan2.1-1.3B 480p
+shaped workload: B=1, H=12, N=32760 (21x30x52 latent grid), d=128, bf16,
+5% critical / 10% negligible, synthetic seeded inputs resident in HBM.
+
+Printed: one JSON line.  `value` is effective TFLOP/s over the whole call,
+counting the method's work F = 4*64*64*d per critical block pair +
+4*64*d*d per query block with marginal blocks.  `roofline` is for the fused
+kernel, timed live with HIP events recorded on its stream; its algorithmic
+flops are the critical pairs plus 2*64*d*d per query block (phi(Q) times the
+marginal state; the projection is folded into the state kernel).
+`cpu_baseline` times the CPU oracle on a bounded sample (whole heads).
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def work(B, H, N, d, kc, kn):
+    Nb = -(-N // 64)
+    pairs = B * H * Nb * kc
+    marg_rows = B * H * Nb if kc + kn < Nb else 0
+    f_comp = 4 * 64 * 64 * d * pairs + 4 * 64 * d * d * marg_rows
+    f_fused = 4 * 64 * 64 * d * pairs + 2 * 64 * d * d * marg_rows
+    return f_comp, f_fused, pairs, marg_rows
+
+
+def cpu_baseline(inp, wl, rc, rn, heads):
+    import numpy as np
+    from oracle import oracle as orc
+    q, k, v = inp.q[:, :heads], inp.k[:, :heads], inp.v[:, :heads]
+    t0 = time.perf_counter()
+    res = orc.forward(q, k, v, inp.w, 64, rc, rn)
+    t = time.perf_counter() - t0
+    f_comp, _, _, _ = work(1, heads, wl.N, wl.d, res["k_c"], res["k_n"])
+    return {"value": round(f_comp / t / 1e12, 6), "unit": "TFLOP/s", "cores": orc.threads(),
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": "heads 0-%d of %d (every query block): pool, classify, sparse and linear "
+                      "branches in fp64; F counted as for the GPU line" % (heads - 1, wl.H),
+            "ms_per_call_extrapolated": round(t * 1e3 * wl.H / heads, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="named workload id (1 = Wan2.1 480p)")
+    ap.add_argument("--crit", type=float, default=None)
+    ap.add_argument("--negl", type=float, default=None)
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
+              "pipeline (heads would shard across GPUs with no exchange); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_video_sla_amd as sla
+    from sparse_attention_video_sla_amd import _lib
+    from sparse_attention_video_sla_amd.inputs import WORKLOADS, make_workload
+
+    wl = WORKLOADS[args.workload]
+    rc = args.crit if args.crit is not None else wl.fracs[0][0]
+    rn = args.negl if args.negl is not None else wl.fracs[0][1]
+    inp = make_workload(args.workload)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt) for x in (inp.q, inp.k, inp.v))
+    w = torch.from_numpy(inp.w).to(dev)
+    B, H, N, d = q.shape
+    Nb = -(-N // 64)
+    kc, kn = sla.counts(Nb, rc, rn)
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(sla.workspace_size(B, H, N, d, wl.dtype, rc, rn), dtype=torch.uint8, device=dev)
+
+    def step():
+        sla.forward(q, k, v, w, rc, rn, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L = _lib.load()
+    L.sla_set_stage_timing(1)
+    ms_buf = (ctypes.c_float * 5)()
+    calls = ctypes.c_int()
+    L.sla_stage_times(ms_buf, ctypes.byref(calls))          # drop anything recorded before
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.check(L.sla_stage_times(ms_buf, ctypes.byref(calls)))
+    L.sla_set_stage_timing(0)
+    stage_ms = {name: ms_buf[i] / max(calls.value, 1) for i, name in enumerate(_lib.STAGES)}
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    f_comp, f_fused, pairs, marg_rows = work(B, H, N, d, kc, kn)
+    value = f_comp / (ms * 1e-3) / 1e12
+    t_fused = stage_ms["fused"] * 1e-3
+    achieved = f_fused / t_fused / 1e12 if t_fused > 0 else 0.0
+    Lp = -(-(d * d + d) // 128) * 128
+    nbytes = {
+        "pool": 2 * B * H * N * d * 2 + 2 * B * H * Nb * d * 4,
+        "state": 2 * B * H * N * d * 2 + B * H * Nb * d * 64 * 2 + B * H * Nb * Lp * 2,
+        "assemble": B * H * Nb * (-(-Nb // 32) * 32) * 2 + 2 * B * H * Nb * Lp * 2,
+    }
+    stages = {}
+    for name in _lib.STAGES:
+        s = {"ms": round(stage_ms[name], 4)}
+        if name in nbytes and stage_ms[name] > 0:
+            s["GB/s"] = round(nbytes[name] / (stage_ms[name] * 1e-3) / 1e9, 1)
+        stages[name] = s
+    stages["assemble"]["TFLOP/s"] = round(2 * B * H * Nb * (-(-Nb // 32) * 32) * Lp / max(stage_ms["assemble"], 1e-9) / 1e9, 1)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; local sinusoid Q/K + noise, V ~ N(0,1))",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64,
+                   "crit_frac": rc, "negl_frac": rn, "k_c": kc, "k_n": kn, "parallelism": "none (1 GPU)"},
+        "mfma_frac_fused": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fused_kernel<bf16,f16,128,float>",
+                     "flops_per_launch": f_fused, "avg_launch_ms": round(stage_ms["fused"], 4)},
+        "stages": stages,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, wl, rc, rn, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

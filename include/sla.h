@@ -1,0 +1,133 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) SLA sparse-linear attention forward.
+ *
+ * The operation is the forward pass of SLA as described by the SLA article
+ * ("Tsinghua cracks the video generation stall ...", techwalker.com,
+ * section 3 "SLA's core mechanism"):
+ *   pool Q and K per block; score the compressed map P_c = softmax(Qbar Kbar^T/sqrt(d));
+ *   per query-block row label the key blocks critical (top crit_frac), negligible
+ *   (bottom negl_frac) or marginal (the rest); exact softmax attention over the
+ *   critical blocks; linear attention phi(Q)(phi(K)^T V) over the marginal blocks
+ *   followed by a d x d projection; negligible blocks skipped.
+ * The sparse part is one softmax over every attended key of the row (the
+ * normalisation of the block-sparse formula on the LVSA page, "method steps").
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors Q, K, V, O are row-major [B, H, N, d] (d fastest), contiguous,
+ *     16-byte aligned DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises; scratch memory comes only from the
+ *     caller's workspace.  Work is enqueued on `stream` (a hipStream_t; NULL
+ *     means the default stream) and runs asynchronously.
+ *   - N is the number of valid tokens.  Blocks are `block` consecutive tokens;
+ *     Nb = ceil(N / block); the last block may be ragged (n = N - (Nb-1)*block
+ *     tokens) and the library masks its pad positions itself.
+ *   - Supported: d in {64, 128}; block = 64; in_dtype F32 or BF16; out_dtype F32
+ *     or equal to in_dtype; 0 <= crit_frac, negl_frac <= 1, crit_frac +
+ *     negl_frac <= 1; B, H, N >= 1; Nb <= 2432 (N <= 155648).
+ *   - Counts per row: k_c = min(Nb, ceil(crit_frac*Nb - 1e-9)),
+ *     k_n = min(Nb - k_c, floor(negl_frac*Nb + 1e-9)).
+ *   - Ranking: one total order per row, score descending then block index
+ *     ascending; the first k_c blocks are critical, the last k_n negligible.
+ *     Scores are fp64 dot products (ascending channel order) of the float32
+ *     block means (fp64 sums in ascending token order / n, rounded once).
+ *   - Errors: invalid or unsupported arguments return a status before anything
+ *     is launched; a failed launch returns SLA_ERR_DEVICE.  sla_last_error()
+ *     gives a thread-local message for the last non-OK status of the thread.
+ *   - Inputs must be finite.  BF16 inputs: the linear branch stages values in
+ *     fp16, so |V| and |V W^T| must stay below 65504.
+ *   - Reentrant; the only mutable state is per thread (the error message and
+ *     the optional stage-timing events).  Results are deterministic run to run
+ *     (no atomics).
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SLA_OK = 0,
+    SLA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, fraction out of range */
+    SLA_ERR_UNSUPPORTED = 2,   /* valid but not implemented: d, block, dtype, Nb limit */
+    SLA_ERR_WORKSPACE = 3,     /* workspace_bytes smaller than sla_workspace_size() */
+    SLA_ERR_DEVICE = 4         /* HIP launch / runtime failure */
+} sla_status;
+
+typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
+
+/* Feature map of the linear branch: softmax over the d channels of each token
+ * (the SLA article, section 5, reports softmax beating ELU+1 and ReLU). */
+typedef enum { SLA_PHI_SOFTMAX = 0 } sla_phi;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int sla_version(void);
+
+/* Per-row counts k_c (critical) and k_n (negligible) for Nb key blocks and
+ * the given shares (SLA article, section 3: top 5% critical, bottom 10%
+ * negligible by default in the article).  Host only. */
+sla_status sla_counts(int Nb, double crit_frac, double negl_frac, int *k_c, int *k_n);
+
+/* Bytes of device workspace sla_forward needs for these arguments.  Host only. */
+sla_status sla_workspace_size(int B, int H, int N, int d, int block, sla_dtype in_dtype,
+                              double crit_frac, double negl_frac, size_t *bytes);
+
+/* Step 1 (SLA article, section 3: mean pooling of Q and K).
+ * q, k: [B,H,N,d] of in_dtype.  q_pool, k_pool: [B,H,Nb,d] float32 outputs,
+ * each the fp64 sum of the block's valid tokens in ascending order divided by
+ * their count, rounded once to float32. */
+sla_status sla_pool(const void *q, const void *k, sla_dtype in_dtype,
+                    int B, int H, int N, int d, int block,
+                    float *q_pool, float *k_pool, void *stream);
+
+/* Steps 2-3 (SLA article, section 3: compressed map and three-way labels).
+ * q_pool, k_pool: [B,H,Nb,d] float32 (from sla_pool).
+ * mask: [B,H,Nb,Nb] int8 output, +1 critical, 0 marginal, -1 negligible.
+ * crit_idx: [B,H,Nb,k_c] int32 output, critical block indices ascending
+ *   (may be NULL only when k_c == 0).
+ * excl_idx: nullable [B,H,Nb,k_c+k_n] int32 output, critical and negligible
+ *   indices together, ascending.
+ * p_c: nullable [B,H,Nb,Nb] float32 output, softmax_j(s_ij / sqrt(d)). */
+sla_status sla_classify(const float *q_pool, const float *k_pool,
+                        int B, int H, int Nb, int d, double crit_frac, double negl_frac,
+                        int8_t *mask, int32_t *crit_idx, int32_t *excl_idx, float *p_c,
+                        void *stream);
+
+/* The whole forward pass (SLA article, section 3; one fused attention kernel
+ * covers the three branches, with the learnable projection on the linear
+ * output).
+ * q, k, v: [B,H,N,d] of in_dtype.  w_proj: [d,d] float32, applied as x W^T
+ *   (row c of W produces output channel c), shared by all heads.
+ * out: [B,H,N,d] of out_dtype: O = O_sparse + O_linear W^T.
+ * mask_out: nullable [B,H,Nb,Nb] int8 copy of the labels.
+ * workspace: device memory of at least sla_workspace_size() bytes, 256-byte
+ *   aligned; its contents on entry do not matter and are clobbered. */
+sla_status sla_forward(const void *q, const void *k, const void *v, const float *w_proj,
+                       sla_dtype in_dtype, sla_dtype out_dtype,
+                       int B, int H, int N, int d, int block,
+                       double crit_frac, double negl_frac, sla_phi phi,
+                       void *out, int8_t *mask_out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage timing, for profiling.  While enabled on a thread, every sla_forward
+ * call of that thread records HIP events on its stream around each of its
+ * kernels: 0 pool, 1 classify, 2 state, 3 assemble, 4 fused (a stage that
+ * does not run records zero time).  sla_stage_times waits for the recorded
+ * events, writes the summed milliseconds per stage to ms[0..4] and the number
+ * of calls summed to *calls, and forgets them.  Events are created on first
+ * use and kept per thread.  Disabled by default. */
+#define SLA_NUM_STAGES 5
+sla_status sla_set_stage_timing(int enable);
+sla_status sla_stage_times(float *ms, int *calls);
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char *sla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

@@ -1,0 +1,144 @@
+"""SLA sparse-linear attention forward for MI355X (gfx950).
+
+Thin binding over the C ABI of libsla.so (include/sla.h): it checks tensor
+placement and layout, allocates outputs and workspace with torch on the
+current device, and passes raw pointers plus the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels.
+
+    out = forward(q, k, v, w, crit_frac=0.05, negl_frac=0.10)
+
+q, k, v: [B, H, N, d] bf16 or float32 on the GPU; w: [d, d] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "version", "SlaError"]
+
+SlaError = _lib.SlaError
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.SLA_BF16
+    if t.dtype == torch.float32:
+        return _lib.SLA_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_gpu(*ts) -> None:
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("tensors must be on the GPU")
+        if t.device != dev:
+            raise ValueError("tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def version() -> int:
+    return _lib.load().sla_version()
+
+
+def counts(Nb: int, crit_frac: float, negl_frac: float):
+    """(k_c, k_n): critical and negligible key blocks per query-block row."""
+    kc, kn = ctypes.c_int(), ctypes.c_int()
+    _lib.check(_lib.load().sla_counts(Nb, crit_frac, negl_frac, ctypes.byref(kc), ctypes.byref(kn)))
+    return kc.value, kn.value
+
+
+def workspace_size(B: int, H: int, N: int, d: int, dtype: str = "bf16", crit_frac: float = 0.05,
+                   negl_frac: float = 0.10, block: int = 64) -> int:
+    code = {"bf16": _lib.SLA_BF16, "f32": _lib.SLA_F32}[dtype]
+    n = ctypes.c_size_t()
+    _lib.check(_lib.load().sla_workspace_size(B, H, N, d, block, code, crit_frac, negl_frac, ctypes.byref(n)))
+    return n.value
+
+
+def pool(q, k, block: int = 64):
+    """Block means of q and k: two [B, H, Nb, d] float32 tensors."""
+    torch = _torch()
+    _check_gpu(q, k)
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must have one shape and dtype")
+    B, H, N, d = q.shape
+    Nb = -(-N // block)
+    qp = torch.empty((B, H, Nb, d), dtype=torch.float32, device=q.device)
+    kp = torch.empty_like(qp)
+    _lib.check(_lib.load().sla_pool(q.data_ptr(), k.data_ptr(), _dtype_code(q), B, H, N, d, block,
+                                    qp.data_ptr(), kp.data_ptr(), _stream_ptr(q.device)))
+    return qp, kp
+
+
+def classify(qp, kp, crit_frac: float = 0.05, negl_frac: float = 0.10, want_excl: bool = False,
+             want_pc: bool = False) -> dict:
+    """Labels of the compressed map: mask [B,H,Nb,Nb] int8 (+1/0/-1), the
+    ascending critical list [B,H,Nb,k_c] and optionally the excluded list and P_c."""
+    torch = _torch()
+    _check_gpu(qp, kp)
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape:
+        raise ValueError("pooled inputs must be float32 of one shape")
+    B, H, Nb, d = qp.shape
+    kc, kn = counts(Nb, crit_frac, negl_frac)
+    dev = qp.device
+    mask = torch.empty((B, H, Nb, Nb), dtype=torch.int8, device=dev)
+    crit = torch.empty((B, H, Nb, kc), dtype=torch.int32, device=dev)
+    excl = torch.empty((B, H, Nb, kc + kn), dtype=torch.int32, device=dev) if want_excl else None
+    pc = torch.empty((B, H, Nb, Nb), dtype=torch.float32, device=dev) if want_pc else None
+    _lib.check(_lib.load().sla_classify(qp.data_ptr(), kp.data_ptr(), B, H, Nb, d, crit_frac, negl_frac,
+                                        mask.data_ptr(), crit.data_ptr() if kc > 0 else None,
+                                        excl.data_ptr() if excl is not None and excl.numel() else None,
+                                        pc.data_ptr() if pc is not None else None, _stream_ptr(dev)))
+    out = dict(mask=mask, crit=crit, k_c=kc, k_n=kn)
+    if want_excl:
+        out["excl"] = excl
+    if want_pc:
+        out["pc"] = pc
+    return out
+
+
+def forward(q, k, v, w, crit_frac: float = 0.05, negl_frac: float = 0.10, block: int = 64,
+            out_dtype=None, return_mask: bool = False, workspace=None, out=None):
+    """SLA forward: O = sparse softmax attention over the critical blocks +
+    (linear attention over the marginal blocks) W^T.  Returns out [B,H,N,d]
+    (float32 by default) or (out, mask) with return_mask."""
+    torch = _torch()
+    _check_gpu(q, k, v, w)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one shape and dtype")
+    B, H, N, d = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (d, d):
+        raise ValueError("w must be float32 [d, d]")
+    in_code = _dtype_code(q)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_code = _lib.SLA_F32 if out_dtype == torch.float32 else _dtype_code(torch.empty(0, dtype=out_dtype))
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous [B,H,N,d] tensor of out_dtype on q's device")
+    Nb = -(-N // block)
+    mask = torch.empty((B, H, Nb, Nb), dtype=torch.int8, device=dev) if return_mask else None
+    need = workspace_size(B, H, N, d, "bf16" if in_code == _lib.SLA_BF16 else "f32", crit_frac, negl_frac, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.load().sla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(), in_code, out_code,
+                                       B, H, N, d, block, crit_frac, negl_frac, _lib.SLA_PHI_SOFTMAX,
+                                       out.data_ptr(), mask.data_ptr() if mask is not None else None,
+                                       workspace.data_ptr(), workspace.numel(), _stream_ptr(dev)))
+    return (out, mask) if return_mask else out

@@ -1,0 +1,280 @@
+// api.hip -- the extern "C" entry points of libsla (declared in include/sla.h).
+//
+// Host-side only: argument checks, per-row counts, workspace carving and the
+// launch sequence pool -> classify -> state -> assemble -> fused, all on the
+// caller's stream with no synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <array>
+#include <string>
+#include <vector>
+
+#include "../../include/sla.h"
+#include "sla_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sla_status fail(sla_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+sla_status fail(sla_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+sla_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return SLA_OK;
+    return fail(SLA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int MAX_NB = 2432;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+long round_up(long x, long m) { return (x + m - 1) / m * m; }
+
+sla_status counts_impl(long Nb, double rc, double rn, int *kc, int *kn) {
+    if (!(rc >= 0.0 && rc <= 1.0) || !(rn >= 0.0 && rn <= 1.0) || rc + rn > 1.0 + 1e-12)
+        return fail(SLA_ERR_INVALID_ARG, "fractions must lie in [0,1] and sum to at most 1 (got %g, %g)", rc, rn);
+    double c = ceil(rc * (double)Nb - 1e-9);
+    double n = floor(rn * (double)Nb + 1e-9);
+    if (c < 0) c = 0;
+    if (c > (double)Nb) c = (double)Nb;
+    if (n < 0) n = 0;
+    if (n > (double)Nb - c) n = (double)Nb - c;
+    *kc = (int)c;
+    *kn = (int)n;
+    return SLA_OK;
+}
+
+sla_status check_shape(int B, int H, int N, int d, int block) {
+    if (B < 1 || H < 1 || N < 1) return fail(SLA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+    if (d != 64 && d != 128) return fail(SLA_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", d);
+    if (block != 64) return fail(SLA_ERR_UNSUPPORTED, "block size %d not supported (64)", block);
+    const long Nb = (N + 63) / 64;
+    if (Nb > MAX_NB) return fail(SLA_ERR_UNSUPPORTED, "N = %d gives %ld blocks; at most %d are supported", N, Nb, MAX_NB);
+    return SLA_OK;
+}
+
+struct Layout {
+    size_t qp, kp, mask, crit, E, mcount, vt, hs, hhat, total;
+    int Nb, Nbc, Lp, kc, kn;
+};
+
+Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
+    Layout L;
+    const long BH = (long)B * H;
+    L.Nb = (N + 63) / 64;
+    L.Nbc = (int)round_up(L.Nb, 32);
+    L.Lp = (int)round_up((long)d * d + d, 128);
+    L.kc = kc;
+    L.kn = kn;
+    const size_t es = f32 ? 4 : 2;   // state / exclusion element size
+    const size_t ts = f32 ? 4 : 2;   // input element size
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    L.qp = take(sizeof(float) * BH * L.Nb * d);
+    L.kp = take(sizeof(float) * BH * L.Nb * d);
+    L.mask = take((size_t)BH * L.Nb * L.Nb);
+    L.crit = take(sizeof(int32_t) * BH * L.Nb * (kc > 0 ? kc : 1));
+    L.mcount = take(sizeof(int32_t) * BH * L.Nb);
+    const bool states = kc + kn < L.Nb;
+    L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
+    L.vt = take(kc > 0 ? ts * BH * L.Nb * d * 64 : 0);
+    L.hs = take(states ? es * BH * L.Nb * L.Lp : 0);
+    L.hhat = take(states ? es * BH * L.Nb * L.Lp : 0);
+    L.total = off;
+    return L;
+}
+
+// Per-thread stage timing (sla_set_stage_timing / sla_stage_times).
+struct StageTimer {
+    bool on = false;
+    std::vector<hipEvent_t> pool;      // created events, reused
+    size_t used = 0;
+    std::vector<std::array<hipEvent_t, SLA_NUM_STAGES + 1>> calls;
+
+    hipEvent_t next() {
+        if (used == pool.size()) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            pool.push_back(e);
+        }
+        return pool[used++];
+    }
+};
+thread_local StageTimer g_timer;
+
+// Records the boundary `b` (0..SLA_NUM_STAGES) of the current call.
+void mark_stage(std::array<hipEvent_t, SLA_NUM_STAGES + 1> *ev, int b, hipStream_t s) {
+    if (ev && (*ev)[b]) hipEventRecord((*ev)[b], s);
+}
+
+}  // namespace
+
+extern "C" {
+
+sla_status sla_set_stage_timing(int enable) {
+    g_timer.on = enable != 0;
+    return SLA_OK;
+}
+
+sla_status sla_stage_times(float *ms, int *calls) {
+    if (!ms || !calls) return fail(SLA_ERR_INVALID_ARG, "ms and calls must not be NULL");
+    for (int i = 0; i < SLA_NUM_STAGES; ++i) ms[i] = 0.f;
+    *calls = (int)g_timer.calls.size();
+    for (auto &ev : g_timer.calls) {
+        hipError_t e = hipEventSynchronize(ev[SLA_NUM_STAGES]);
+        if (e != hipSuccess) return device_status(e, "stage timing");
+        for (int i = 0; i < SLA_NUM_STAGES; ++i) {
+            float t = 0.f;
+            e = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+            if (e != hipSuccess) return device_status(e, "stage timing");
+            ms[i] += t;
+        }
+    }
+    g_timer.calls.clear();
+    g_timer.used = 0;
+    return SLA_OK;
+}
+
+int sla_version(void) { return 100; }
+
+const char *sla_last_error(void) { return g_err.c_str(); }
+
+sla_status sla_counts(int Nb, double crit_frac, double negl_frac, int *k_c, int *k_n) {
+    if (!k_c || !k_n) return fail(SLA_ERR_INVALID_ARG, "k_c and k_n must not be NULL");
+    if (Nb < 1) return fail(SLA_ERR_INVALID_ARG, "Nb must be >= 1 (got %d)", Nb);
+    return counts_impl(Nb, crit_frac, negl_frac, k_c, k_n);
+}
+
+sla_status sla_workspace_size(int B, int H, int N, int d, int block, sla_dtype in_dtype, double crit_frac,
+                              double negl_frac, size_t *bytes) {
+    if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
+    sla_status st = check_shape(B, H, N, d, block);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_F32 && in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "input dtype %d not supported", (int)in_dtype);
+    int kc, kn;
+    st = counts_impl((N + 63) / 64, crit_frac, negl_frac, &kc, &kn);
+    if (st != SLA_OK) return st;
+    *bytes = make_layout(B, H, N, d, in_dtype == SLA_F32, kc, kn).total;
+    return SLA_OK;
+}
+
+sla_status sla_pool(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
+                    float *q_pool, float *k_pool, void *stream) {
+    if (!q || !k || !q_pool || !k_pool) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    sla_status st = check_shape(B, H, N, d, block);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_F32 && in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "input dtype %d not supported", (int)in_dtype);
+    const int Nb = (N + 63) / 64;
+    return device_status(sla::launch_pool(in_dtype == SLA_BF16, d, q, k, q_pool, k_pool, (long)B * H, N, Nb, 64,
+                                          (hipStream_t)stream),
+                         "pool launch");
+}
+
+sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, int Nb, int d, double crit_frac,
+                        double negl_frac, int8_t *mask, int32_t *crit_idx, int32_t *excl_idx, float *p_c,
+                        void *stream) {
+    if (!q_pool || !k_pool || !mask) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    if (B < 1 || H < 1 || Nb < 1) return fail(SLA_ERR_INVALID_ARG, "B, H, Nb must be >= 1");
+    if (d != 64 && d != 128) return fail(SLA_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", d);
+    if (Nb > MAX_NB) return fail(SLA_ERR_UNSUPPORTED, "Nb = %d exceeds the supported %d", Nb, MAX_NB);
+    int kc, kn;
+    sla_status st = counts_impl(Nb, crit_frac, negl_frac, &kc, &kn);
+    if (st != SLA_OK) return st;
+    if (kc > 0 && !crit_idx) return fail(SLA_ERR_INVALID_ARG, "crit_idx must not be NULL when k_c > 0");
+    sla::ClassifyArgs a{};
+    a.qp = q_pool; a.kp = k_pool; a.BH = (long)B * H; a.Nb = Nb; a.D = d; a.kc = kc; a.kn = kn;
+    a.mask = mask; a.crit = crit_idx; a.excl = excl_idx; a.pc = p_c;
+    a.E = nullptr; a.Nbc = 0; a.mcount = nullptr; a.n_last = 64; a.e_is_f32 = false;
+    a.inv_sqrt_d = 1.0 / sqrt((double)d);
+    return device_status(sla::launch_classify(a, (hipStream_t)stream), "classify launch");
+}
+
+sla_status sla_forward(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
+                       sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                       double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !w_proj || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    sla_status st = check_shape(B, H, N, d, block);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_F32 && in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "input dtype %d not supported", (int)in_dtype);
+    if (out_dtype != SLA_F32 && out_dtype != in_dtype)
+        return fail(SLA_ERR_UNSUPPORTED, "output dtype must be F32 or the input dtype");
+    if (phi != SLA_PHI_SOFTMAX) return fail(SLA_ERR_UNSUPPORTED, "feature map %d not supported", (int)phi);
+    int kc, kn;
+    const int Nb = (N + 63) / 64;
+    st = counts_impl(Nb, crit_frac, negl_frac, &kc, &kn);
+    if (st != SLA_OK) return st;
+    const bool f32 = in_dtype == SLA_F32;
+    const Layout L = make_layout(B, H, N, d, f32, kc, kn);
+    if (!workspace && L.total > 0) return fail(SLA_ERR_INVALID_ARG, "null workspace");
+    if (workspace_bytes < L.total)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, L.total);
+    if (((uintptr_t)workspace & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    char *ws = (char *)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    const long BH = (long)B * H;
+    const bool states = kc + kn < Nb;
+    float *qp = (float *)(ws + L.qp), *kp = (float *)(ws + L.kp);
+    int8_t *mask = mask_out ? mask_out : (int8_t *)(ws + L.mask);
+    int32_t *crit = (int32_t *)(ws + L.crit);
+    int32_t *mcount = (int32_t *)(ws + L.mcount);
+
+    std::array<hipEvent_t, SLA_NUM_STAGES + 1> *ev = nullptr;
+    if (g_timer.on) {
+        std::array<hipEvent_t, SLA_NUM_STAGES + 1> set;
+        for (auto &e : set) e = g_timer.next();
+        g_timer.calls.push_back(set);
+        ev = &g_timer.calls.back();
+    }
+    mark_stage(ev, 0, s);
+    st = device_status(sla::launch_pool(!f32, d, q, k, qp, kp, BH, N, Nb, 64, s), "pool launch");
+    if (st != SLA_OK) return st;
+    mark_stage(ev, 1, s);
+
+    sla::ClassifyArgs ca{};
+    ca.qp = qp; ca.kp = kp; ca.BH = BH; ca.Nb = Nb; ca.D = d; ca.kc = kc; ca.kn = kn;
+    ca.mask = mask; ca.crit = crit; ca.excl = nullptr; ca.pc = nullptr;
+    ca.E = states ? (void *)(ws + L.E) : nullptr; ca.Nbc = L.Nbc;
+    ca.mcount = mcount; ca.n_last = N - 64 * (Nb - 1); ca.e_is_f32 = f32;
+    ca.inv_sqrt_d = 1.0 / sqrt((double)d);
+    st = device_status(sla::launch_classify(ca, s), "classify launch");
+    if (st != SLA_OK) return st;
+    mark_stage(ev, 2, s);
+
+    if (states || kc > 0) {
+        sla::StateArgs sa{};
+        sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp;
+        sa.vt = ws + L.vt; sa.hs = ws + L.hs; sa.do_states = states; sa.do_vt = kc > 0; sa.bf16_in = !f32;
+        st = device_status(sla::launch_state(sa, s), "state launch");
+        if (st != SLA_OK) return st;
+    }
+    mark_stage(ev, 3, s);
+    if (states) {
+        sla::AssembleArgs aa{};
+        aa.E = ws + L.E; aa.hs = ws + L.hs; aa.mcount = mcount; aa.hhat = ws + L.hhat;
+        aa.BH = BH; aa.Nb = Nb; aa.Nbc = L.Nbc; aa.Lp = L.Lp; aa.f32 = f32;
+        st = device_status(sla::launch_assemble(aa, s), "assemble launch");
+        if (st != SLA_OK) return st;
+    }
+    mark_stage(ev, 4, s);
+    sla::FusedArgs fa{};
+    fa.q = q; fa.k = k; fa.vt = ws + L.vt; fa.crit = crit; fa.kc = kc;
+    fa.hhat = ws + L.hhat; fa.mcount = states ? mcount : nullptr; fa.Lp = L.Lp;
+    fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
+    fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;
+    st = device_status(sla::launch_fused(fa, s), "fused launch");
+    mark_stage(ev, 5, s);
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// classify.hip -- compressed block scores and the three-way labels (SLA
+// article, section 3: the top share of each row's compressed map is critical
+// (+1), the bottom share negligible (-1), the rest marginal (0)).
+//
+// A workgroup of 8 waves owns R consecutive query-block rows of one head.
+//   1. Scores s_ij = sum_c Qbar_i[c] * Kbar_j[c] in fp64, ascending c, one
+//      thread per key block j with R rows kept in registers (the products of
+//      two float32 values are exact in fp64, so the fused multiply-add gives
+//      the same value as a separate multiply and add).  Rows go to LDS.
+//   2. One wave per row.  Each lane holds the order-preserving 64-bit keys of
+//      blocks j = lane + 64e.  The k-th largest key is found bit by bit from
+//      the top: a candidate prefix is kept when at least k keys are >= it
+//      (counted with ballots); the search stops early once exactly k keys are
+//      >= the prefix.  Ties on the threshold key are resolved by block index
+//      (lower index ranks higher), so the first k_c of the order (score desc,
+//      index asc) are critical and its last k_n negligible.  The bottom search
+//      runs on inverted keys with ties taken from the highest index down.
+//   3. The row's outputs: int8 labels, ascending critical list, optional
+//      ascending excluded list, optional P_c, and for the forward pass the
+//      0/1 exclusion row E (critical or negligible) used by the marginal-state
+//      GEMM and the number of marginal tokens of the row.
+#include "sla_device.h"
+#include "sla_launch.h"
+
+namespace sla {
+
+static constexpr int CL_THREADS = 512;
+
+__device__ __forceinline__ uint64_t order_key(double s) {
+    uint64_t b = (uint64_t)__double_as_longlong(s);
+    if (b == 0x8000000000000000ull) b = 0;              // -0 ranks like +0
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Key of block j for the search: the order key (inv = false) or its
+// complement (inv = true); 0 for lanes past the row end, which no candidate
+// (always >= 1) can reach.
+__device__ __forceinline__ uint64_t key_at(const double *s, int j, int Nb, bool inv) {
+    if (j >= Nb) return 0ull;
+    const uint64_t k = order_key(s[j]);
+    return inv ? ~k : k;
+}
+
+// Largest v with #{keys >= v} >= k (k >= 1); `exact` when that count is exactly k,
+// which lets the search stop as soon as the prefix separates k keys.
+__device__ uint64_t kth_largest(const double *s, int Nb, int ne, int lane, bool inv, int k, bool &exact) {
+    uint64_t lo = 0;
+    exact = false;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = lo | (1ull << bit);
+        int cnt = 0;
+        for (int e = 0; e < ne; ++e) cnt += __popcll(__ballot(key_at(s, lane + 64 * e, Nb, inv) >= cand));
+        if (cnt >= k) {
+            lo = cand;
+            if (cnt == k) { exact = true; break; }
+        }
+    }
+    return lo;
+}
+
+// Label +1 (inv = false, sign = 1) or -1 (inv = true, sign = -1) for the k
+// blocks ranked first by (key desc, index asc) / (inverted key desc, index desc).
+__device__ void mark(const double *s, int8_t *lab, int Nb, int ne, int lane, bool inv, int k, int8_t sign) {
+    bool exact;
+    const uint64_t t = kth_largest(s, Nb, ne, lane, inv, k, exact);
+    int need = 0;
+    if (!exact) {
+        int g = 0;
+        for (int e = 0; e < ne; ++e) g += __popcll(__ballot(key_at(s, lane + 64 * e, Nb, inv) > t));
+        need = k - g;
+    }
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const uint64_t gt = (lane == 63) ? 0ull : (~0ull << (lane + 1));
+    int run = 0;
+    for (int x = 0; x < ne; ++x) {
+        const int e = inv ? ne - 1 - x : x;      // ties: ascending index for +1, descending for -1
+        const int j = lane + 64 * e;
+        const uint64_t key = key_at(s, j, Nb, inv);
+        bool on = exact ? key >= t : key > t;
+        const uint64_t tie = __ballot(!exact && key == t);
+        if (!exact && key == t) on = run + __popcll(tie & (inv ? gt : lt)) < need;
+        run += __popcll(tie);
+        if (on && j < Nb) lab[j] = sign;
+    }
+}
+
+template <typename ES, int D, int R>
+__global__ __launch_bounds__(CL_THREADS) void classify_kernel(
+    const float *__restrict__ qp, const float *__restrict__ kp, int Nb, int kc, int kn,
+    int8_t *__restrict__ mask, int32_t *__restrict__ crit, int32_t *__restrict__ excl,
+    float *__restrict__ pc, ES *__restrict__ E, int Nbc, int32_t *__restrict__ mcount, int n_last,
+    double inv_sqrt_d) {
+    extern __shared__ double smem[];
+    double *qd = smem;                                        // [R][D]
+    double *sc = smem + R * D;                                // [R][Nb]
+    int8_t *labs = reinterpret_cast<int8_t *>(sc + R * Nb);   // [R][Nb]
+    const int tiles = (Nb + R - 1) / R;
+    const long bh = blockIdx.x / tiles;
+    const int i0 = (blockIdx.x % tiles) * R;
+    const int nr = min(R, Nb - i0);
+    const int tid = threadIdx.x;
+
+    for (int x = tid; x < R * D; x += CL_THREADS)
+        qd[x] = (x < nr * D) ? (double)qp[(bh * Nb + i0) * D + x] : 0.0;
+    for (int x = tid; x < R * Nb; x += CL_THREADS) labs[x] = 0;
+    __syncthreads();
+
+    for (int j = tid; j < Nb; j += CL_THREADS) {
+        const float *kj = kp + (bh * Nb + j) * D;
+        double acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0;
+#pragma unroll 2
+        for (int c = 0; c < D; c += 4) {
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(kj + c);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const double kd = (double)kv[u];
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = __builtin_fma(qd[r * D + c + u], kd, acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < nr) sc[r * Nb + j] = acc[r];
+    }
+    __syncthreads();
+
+    const int wave = tid >> 6, lane = tid & 63;
+    const int ne = (Nb + 63) >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int r = wave; r < nr; r += CL_THREADS / 64) {
+        const long row = bh * Nb + i0 + r;
+        const double *s = sc + r * Nb;
+        int8_t *lab = labs + r * Nb;
+        if (kc > 0) mark(s, lab, Nb, ne, lane, false, kc, 1);
+        if (kn > 0) mark(s, lab, Nb, ne, lane, true, kn, -1);
+        int run_c = 0, run_x = 0, n_marg = 0;
+        bool last_marg = false;
+        for (int e = 0; e < ne; ++e) {
+            const int j = lane + 64 * e;
+            const bool ok = j < Nb;
+            const int lb = ok ? lab[j] : 0;
+            if (ok) mask[row * Nb + j] = (int8_t)lb;
+            const uint64_t bc = __ballot(ok && lb == 1);
+            const int pc_pos = run_c + __popcll(bc & lt);
+            if (ok && lb == 1 && pc_pos < kc) crit[row * kc + pc_pos] = j;
+            run_c += __popcll(bc);
+            const uint64_t bx = __ballot(ok && lb != 0);
+            const int px_pos = run_x + __popcll(bx & lt);
+            if (excl && ok && lb != 0 && px_pos < kc + kn) excl[row * (kc + kn) + px_pos] = j;
+            run_x += __popcll(bx);
+            n_marg += __popcll(__ballot(ok && lb == 0));
+            if (ok && lb == 0 && j == Nb - 1) last_marg = true;
+            if (E && j < Nbc) E[row * Nbc + j] = from_f32<ES>((ok && lb != 0) ? 1.f : 0.f);
+        }
+        if (mcount) {
+            const bool lm = __ballot(last_marg) != 0ull;
+            if (lane == 0) mcount[row] = n_marg * 64 - (lm ? 64 - n_last : 0);
+        }
+        if (pc) {
+            double m = -__builtin_inf();
+            for (int j = lane; j < Nb; j += 64) m = fmax(m, s[j]);
+            for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+            double z = 0.0;
+            for (int j = lane; j < Nb; j += 64) z += exp((s[j] - m) * inv_sqrt_d);
+            for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+            for (int j = lane; j < Nb; j += 64) pc[row * Nb + j] = (float)(exp((s[j] - m) * inv_sqrt_d) / z);
+        }
+    }
+}
+
+template <typename ES, int D, int R>
+static hipError_t launch_cls_r(const ClassifyArgs &a, hipStream_t st) {
+    const size_t lds = classify_lds_bytes(R, D, a.Nb);
+    auto kern = classify_kernel<ES, D, R>;
+    hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    const long tiles = (a.Nb + R - 1) / R;
+    const unsigned grid = (unsigned)(a.BH * tiles);
+    kern<<<grid, CL_THREADS, lds, st>>>(a.qp, a.kp, a.Nb, a.kc, a.kn, a.mask, a.crit, a.excl, a.pc,
+                                        (ES *)a.E, a.Nbc, a.mcount, a.n_last, a.inv_sqrt_d);
+    return hipGetLastError();
+}
+
+template <typename ES, int D>
+static hipError_t launch_cls_d(const ClassifyArgs &a, hipStream_t st) {
+    const int R = classify_rows_per_group(a.Nb, D);
+    switch (R) {
+    case 8: return launch_cls_r<ES, D, 8>(a, st);
+    case 4: return launch_cls_r<ES, D, 4>(a, st);
+    case 2: return launch_cls_r<ES, D, 2>(a, st);
+    default: return launch_cls_r<ES, D, 1>(a, st);
+    }
+}
+
+size_t classify_lds_bytes(int R, int D, int Nb) {
+    return sizeof(double) * (size_t)R * (D + Nb) + (size_t)R * Nb;
+}
+
+int classify_rows_per_group(int Nb, int D) {
+    const size_t limit = 160 * 1024;
+    for (int R = 8; R > 1; R >>= 1)
+        if (classify_lds_bytes(R, D, Nb) <= limit) return R;
+    return 1;
+}
+
+hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st) {
+    if (a.e_is_f32) return a.D == 64 ? launch_cls_d<float, 64>(a, st) : launch_cls_d<float, 128>(a, st);
+    return a.D == 64 ? launch_cls_d<f16, 64>(a, st) : launch_cls_d<f16, 128>(a, st);
+}
+
+}  // namespace sla

@@ -1,0 +1,287 @@
+// fused.hip -- one kernel for the three branches of SLA (SLA article,
+// section 3: exact sparse FlashAttention over the critical blocks, linear
+// attention over the marginal ones, negligible ones skipped, all in one GPU
+// kernel, with the learnable projection on the linear output).
+//
+// One workgroup per query block i (64 query rows), 4 waves: wave (qh, kh)
+// owns query rows 32qh..32qh+31 and, of every critical key tile, keys
+// 32kh..32kh+31.
+//   Sparse part: the k_c critical key blocks of row i (ascending) are
+//   streamed through double-buffered LDS (K row-major, V pre-transposed by the
+//   state kernel).  Per tile, S^T = K Q^T on 32x32x16 MFMA (Q held in
+//   registers as the B operand), online softmax in the log2 domain with the
+//   1/sqrt(d) scale folded into one multiply-add, P^T converted to the input
+//   type straight from the accumulator, O^T += V^T P^T on MFMA.  Keys past N
+//   (ragged last block) score -inf.  The two key halves of a query half
+//   merge their (max, sum, O) at the end through LDS, one softmax over the
+//   union of all critical keys (block-sparse normalisation of the LVSA page).
+//   Linear part: phi(q) = softmax over channels from the Q registers;
+//   y = phi(q) Hhat_i^T on MFMA, divided by phi(q).Zhat_i.  Hhat_i already
+//   holds the projection W (folded into the block states).
+//   O = O_sparse + y, written once.
+// Workgroups are remapped so that each XCD (own L2) takes a contiguous run of
+// (head, query block): neighbouring query blocks share most critical tiles.
+#include "sla_device.h"
+#include "sla_launch.h"
+
+namespace sla {
+
+template <typename TO> __device__ __forceinline__ void store4(TO *p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<float>(float *p, float a, float b, float c, float d) {
+    f32x4 v = {a, b, c, d};
+    *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float b, float c, float d) {
+    v4<bf16> v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    __builtin_memcpy(p, &v, sizeof(v));
+}
+
+template <typename T, typename S, int D, typename TO>
+__global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                       const T *__restrict__ vt,
+                                                       const int32_t *__restrict__ crit, int kc,
+                                                       const S *__restrict__ hhat,
+                                                       const int32_t *__restrict__ mcount, int Lp,
+                                                       TO *__restrict__ out, long G, int per_xcd, int N,
+                                                       int Nb, float sl2) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int KSTR = D + EPC;            // K tile row stride (elements)
+    constexpr int VSTR = 64 + EPC;           // V^T tile row stride
+    constexpr int KT = 64 * KSTR, VT = D * VSTR;
+    constexpr int CPR_K = D / EPC, CPR_V = 64 / EPC;
+    constexpr int NK = 64 * CPR_K / 256, NV = D * CPR_V / 256;
+    constexpr int NS = D / 16;               // k-steps over channels
+    constexpr int NCT = D / 32;              // 32-channel tiles
+    constexpr int HT = D / 64;               // channel tiles per key half after the merge
+    constexpr float NEG_INF = -__builtin_inff();
+    __shared__ __attribute__((aligned(16))) T lds[2 * (KT + VT)];
+
+    const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (logical >= G) return;
+    const long bh = logical / Nb;
+    const int i = (int)(logical % Nb);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int qh = wave & 1, kh = wave >> 1;
+
+    // Q rows of this wave as B fragments: lane (q, h) holds channels 16s + 8h .. +7
+    const int qrow = 64 * i + 32 * qh + l32;
+    const bool qvalid = qrow < N;
+    v8<T> qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        qf[s] = qvalid ? ld8<T>(q + (bh * N + qrow) * (long)D + 16 * s + 8 * hh) : zero8<T>();
+
+    float m = NEG_INF, l = 0.f;
+    f32x16 o[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ct][r] = 0.f;
+
+    const int32_t *cl = crit + (bh * Nb + i) * (long)kc;
+    Chunk pk[NK], pv[NV];
+    auto gload = [&](int j) {
+        const T *kb = k + (bh * N + 64L * j) * D;
+        const T *vb = vt + (bh * Nb + j) * (long)D * 64;
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            const int ch = tid + 256 * u, row = ch / CPR_K, cc = ch % CPR_K;
+            pk[u] = (64 * j + row < N) ? ld_chunk(kb + (long)row * D + cc * EPC) : zero_chunk();
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int ch = tid + 256 * u, c = ch / CPR_V, cc = ch % CPR_V;
+            pv[u] = ld_chunk(vb + c * 64 + cc * EPC);
+        }
+    };
+    auto lstore = [&](int buf) {
+        T *Ks = lds + buf * (KT + VT);
+        T *Vs = Ks + KT;
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            const int ch = tid + 256 * u, row = ch / CPR_K, cc = ch % CPR_K;
+            st_chunk(Ks + row * KSTR + cc * EPC, pk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int ch = tid + 256 * u, c = ch / CPR_V, cc = ch % CPR_V;
+            st_chunk(Vs + c * VSTR + cc * EPC, pv[u]);
+        }
+    };
+
+    if (kc > 0) {
+        // list entries are clamped to [0, Nb) so that no index can leave the tensors
+        auto blk_at = [&](int n) { return min(max(cl[n], 0), Nb - 1); };
+        gload(blk_at(0));
+        lstore(0);
+        __syncthreads();
+        for (int n = 0; n < kc; ++n) {
+            const int j = blk_at(n);
+            if (n + 1 < kc) gload(blk_at(n + 1));
+            const T *Ks = lds + (n & 1) * (KT + VT);
+            const T *Vs = Ks + KT;
+            // S^T (keys 32kh.. of the tile x this wave's 32 queries)
+            f32x16 sacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) mma16(sacc, ld8<T>(Ks + (32 * kh + l32) * KSTR + 16 * s + 8 * hh), qf[s]);
+            if (64 * j + 64 > N) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 64 * j + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (key >= N) sacc[r] = NEG_INF;
+                }
+            }
+            float mx = sacc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+            mx = fmaxf(mx, shfl_xor32(mx));
+            const float mnew = fmaxf(m, mx * sl2);
+            const float msub = (mnew == NEG_INF) ? 0.f : mnew;
+            const float alpha = fast_exp2(m - msub);
+            l *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+            m = mnew;
+            v8<T> pb[2];
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[r], sl2, -msub));
+                ps += p;
+                pb[r >> 3][r & 7] = from_f32<T>(p);
+            }
+            l += ps;
+            // O^T (channels x queries) += V^T P^T over this wave's 32 keys, permuted k
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const T *vp = Vs + (32 * ct + l32) * VSTR + 32 * kh + 16 * ks + 4 * hh;
+                    mma16(o[ct], ld4x2<T>(vp, vp + 8), pb[ks]);
+                }
+            }
+            if (n + 1 < kc) lstore((n + 1) & 1);
+            __syncthreads();
+        }
+    }
+    l += shfl_xor32(l);
+
+    // merge the two key halves: wave kh keeps channel tiles [kh*HT, kh*HT+HT)
+    __syncthreads();
+    float *xb = reinterpret_cast<float *>(lds);
+    {
+        float *dst = xb + ((qh * 2 + (1 - kh)) * HT) * 16 * 64;
+#pragma unroll
+        for (int t = 0; t < HT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[(t * 16 + r) * 64 + lane] = o[(1 - kh) * HT + t][r];
+        float *ml = xb + 4 * HT * 16 * 64;
+        ml[((qh * 2 + kh) * 2 + 0) * 64 + lane] = m;
+        ml[((qh * 2 + kh) * 2 + 1) * 64 + lane] = l;
+    }
+    __syncthreads();
+    f32x16 os[HT];
+    {
+        const float *src = xb + ((qh * 2 + kh) * HT) * 16 * 64;
+        const float *ml = xb + 4 * HT * 16 * 64;
+        const float mp = ml[((qh * 2 + (1 - kh)) * 2 + 0) * 64 + lane];
+        const float lp = ml[((qh * 2 + (1 - kh)) * 2 + 1) * 64 + lane];
+        const float M = fmaxf(m, mp);
+        const float fs = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
+        const float fp = (mp == NEG_INF) ? 0.f : fast_exp2(mp - M);
+        const float L = l * fs + lp * fp;
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+        for (int t = 0; t < HT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                os[t][r] = (o[kh * HT + t][r] * fs + src[(t * 16 + r) * 64 + lane] * fp) * inv;
+    }
+
+    // linear part
+    const long rid = bh * Nb + i;
+    if (mcount != nullptr && mcount[rid] > 0) {
+        const S *hr = hhat + rid * (long)Lp;
+        constexpr float LOG2E = 1.4426950408889634f;
+        float mq = NEG_INF;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mq = fmaxf(mq, to_f32<T>(qf[s][e]));
+        mq = fmaxf(mq, shfl_xor32(mq));
+        float ex[NS][8];
+        float se = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ex[s][e] = fast_exp2((to_f32<T>(qf[s][e]) - mq) * LOG2E);
+                se += ex[s][e];
+            }
+        se += shfl_xor32(se);
+        const float inv_se = 1.f / se;
+        v8<S> ph[NS];
+        float den = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const v8<S> z = ld8<S>(hr + D * D + 16 * s + 8 * hh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[s][e] = from_f32<S>(ex[s][e] * inv_se);
+                den += to_f32<S>(ph[s][e]) * to_f32<S>(z[e]);
+            }
+        }
+        den += shfl_xor32(den);
+        const float rden = 1.f / den;
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            f32x16 y;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[r] = 0.f;
+            const int ct = kh * HT + t;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) mma16(y, ld8<S>(hr + (32 * ct + l32) * D + 16 * s + 8 * hh), ph[s]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) os[t][r] += y[r] * rden;
+        }
+    }
+
+    if (qvalid) {
+        TO *orow = out + (bh * N + qrow) * (long)D;
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            const int ct = kh * HT + t;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store4<TO>(orow + 32 * ct + 8 * g + 4 * hh, os[t][4 * g], os[t][4 * g + 1], os[t][4 * g + 2],
+                           os[t][4 * g + 3]);
+        }
+    }
+}
+
+template <typename T, typename S, int D, typename TO>
+static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
+    const long G = a.BH * a.Nb;
+    const int per = (int)((G + 7) / 8);
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+    fused_kernel<T, S, D, TO><<<(unsigned)(8L * per), 256, 0, st>>>(
+        (const T *)a.q, (const T *)a.k, (const T *)a.vt, a.crit, a.kc, (const S *)a.hhat, a.mcount, a.Lp,
+        (TO *)a.out, G, per, a.N, a.Nb, sl2);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
+    if (a.bf16_in) {
+        if (a.bf16_out)
+            return a.D == 64 ? launch_fused_t<bf16, f16, 64, bf16>(a, st) : launch_fused_t<bf16, f16, 128, bf16>(a, st);
+        return a.D == 64 ? launch_fused_t<bf16, f16, 64, float>(a, st) : launch_fused_t<bf16, f16, 128, float>(a, st);
+    }
+    return a.D == 64 ? launch_fused_t<float, float, 64, float>(a, st) : launch_fused_t<float, float, 128, float>(a, st);
+}
+
+}  // namespace sla

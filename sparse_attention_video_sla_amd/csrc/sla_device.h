@@ -1,0 +1,106 @@
+// sla_device.h -- device helpers shared by the gfx950 kernels of libsla.
+//
+// MFMA fragment convention used by every kernel (CDNA3/CDNA4 32x32 layouts):
+//   v_mfma_f32_32x32x16_{bf16,f16}: lane l supplies A[m = l%32][k = 8*(l/32) + e] and
+//   B[k = 8*(l/32) + e][n = l%32] for e = 0..7; the 16 accumulator registers r of
+//   lane l hold D[row = 8*(r/4) + 4*(l/32) + r%4][col = l%32].
+// A float "fragment" is the same 8 k-slots per lane fed to eight
+// v_mfma_f32_32x32x2f32 (instruction e uses slot e), which yields the same
+// 32x32 sum over 16 k values and the same accumulator layout.
+//
+// When the B operand of a product is taken from the accumulator of a previous
+// one (P^T after softmax, a projected tile), lane (n, h) holds the rows
+// {4h..4h+3, 8+4h..8+4h+3} of each 16-row group.  Any k order is valid as long
+// as A and B agree, so such products read A with that same permutation
+// ("permuted k"): slot e <-> k = 16s + (e < 4 ? 4h + e : 8 + 4h + e - 4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename E> struct V8;
+template <> struct V8<bf16> { typedef bf16 type __attribute__((ext_vector_type(8))); };
+template <> struct V8<f16> { typedef f16 type __attribute__((ext_vector_type(8))); };
+template <> struct V8<float> { typedef float type __attribute__((ext_vector_type(8))); };
+template <typename E> using v8 = typename V8<E>::type;
+
+template <typename E> struct V4;
+template <> struct V4<bf16> { typedef bf16 type __attribute__((ext_vector_type(4))); };
+template <> struct V4<f16> { typedef f16 type __attribute__((ext_vector_type(4))); };
+template <> struct V4<float> { typedef float type __attribute__((ext_vector_type(4))); };
+template <typename E> using v4 = typename V4<E>::type;
+
+// ---------------------------------------------------------------- MFMA wrappers
+__device__ __forceinline__ void mma16(f32x16 &acc, const v8<bf16> &a, const v8<bf16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16 &acc, const v8<f16> &a, const v8<f16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16 &acc, const v8<float> &a, const v8<float> &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+template <typename E> __device__ __forceinline__ float to_f32(E x) { return (float)x; }
+
+template <typename E, typename Src>
+__device__ __forceinline__ v8<E> cvt8(const Src &x) {
+    v8<E> r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = from_f32<E>((float)x[e]);
+    return r;
+}
+
+template <typename E> __device__ __forceinline__ v8<E> zero8() {
+    v8<E> r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = from_f32<E>(0.f);
+    return r;
+}
+
+// ---------------------------------------------------------------- 16-byte chunks
+struct alignas(16) Chunk { uint32_t w[4]; };
+
+__device__ __forceinline__ Chunk ld_chunk(const void *p) { return *reinterpret_cast<const Chunk *>(p); }
+__device__ __forceinline__ void st_chunk(void *p, const Chunk &c) { *reinterpret_cast<Chunk *>(p) = c; }
+__device__ __forceinline__ Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u; return c; }
+
+// 8 consecutive elements (16 or 32 bytes, 16-byte aligned)
+template <typename E> __device__ __forceinline__ v8<E> ld8(const E *p) {
+    v8<E> r;
+    __builtin_memcpy(&r, p, sizeof(r));
+    return r;
+}
+template <typename E> __device__ __forceinline__ v4<E> ld4(const E *p) {
+    v4<E> r;
+    __builtin_memcpy(&r, p, sizeof(r));
+    return r;
+}
+// 8 elements from two 4-element runs (the permuted-k A operand)
+template <typename E> __device__ __forceinline__ v8<E> ld4x2(const E *p0, const E *p1) {
+    v4<E> a = ld4(p0), b = ld4(p1);
+    v8<E> r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[e + 4] = b[e]; }
+    return r;
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace sla

@@ -1,0 +1,64 @@
+// sla_launch.h -- host-side launchers of the gfx950 kernels (internal to libsla).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+struct ClassifyArgs {
+    const float *qp, *kp;
+    long BH;
+    int Nb, D, kc, kn;
+    int8_t *mask;
+    int32_t *crit, *excl;
+    float *pc;
+    void *E;          // nullable [BH][Nb][Nbc] 0/1 exclusion rows (f16, or float for f32 inputs)
+    int Nbc;
+    int32_t *mcount;  // nullable [BH][Nb] marginal token count per row
+    int n_last;       // valid tokens of the last block
+    bool e_is_f32;
+    double inv_sqrt_d;
+};
+
+struct StateArgs {
+    const void *k, *v;
+    const float *w;
+    long BH;
+    int N, Nb, D, Lp;
+    void *vt;         // [BH][Nb][D][64] transposed V, in the input dtype
+    void *hs;         // [BH][Nb][Lp] per-block states (h'^T then z), scaled by 1/64
+    bool do_states, do_vt, bf16_in;
+};
+
+struct AssembleArgs {
+    const void *E, *hs;
+    const int32_t *mcount;
+    void *hhat;       // [BH][Nb][Lp] marginal states per query-block row
+    long BH;
+    int Nb, Nbc, Lp;
+    bool f32;
+};
+
+struct FusedArgs {
+    const void *q, *k, *vt;
+    const int32_t *crit;
+    int kc;
+    const void *hhat;
+    const int32_t *mcount;   // nullable: no marginal blocks anywhere
+    int Lp;
+    void *out;
+    long BH;
+    int N, Nb, D;
+    bool bf16_in, bf16_out;
+};
+
+hipError_t launch_pool(bool bf16_in, int D, const void *q, const void *k, float *qp, float *kp,
+                       long BH, int N, int Nb, int blk, hipStream_t st);
+int classify_rows_per_group(int Nb, int D);
+size_t classify_lds_bytes(int R, int D, int Nb);
+hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st);
+hipError_t launch_state(const StateArgs &a, hipStream_t st);
+hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st);
+hipError_t launch_fused(const FusedArgs &a, hipStream_t st);
+
+}  // namespace sla

@@ -15,16 +15,21 @@ Q and K are 0.5 * N(0,1) noise plus low-frequency sinusoids of (t, h, w) that
 Q and K of one head share, so that q.k peaks at nearby positions and attention
 is local.  V ~ N(0,1); the d x d projection W ~ N(0, 1/d).
 
-Random stream (numpy PCG64, seed = 1000 + config id for the named workloads):
-  1. frequencies  omega[h, axis, f] ~ U[0, 0.3)  (shape [H, 3, 8])
-  2. W            [d, d] ~ N(0, 1/d)
-  3. for b in B, for h in H:  eps_Q[b,h] [N,d], eps_K[b,h] [N,d], V[b,h] [N,d]
-All arithmetic is float64, rounded once to float32, then (bf16 workloads)
-rounded to bfloat16 with round-to-nearest-even.
+Random streams (numpy PCG64; seed = 1000 + config id for the named workloads):
+  root = PCG64(SeedSequence(seed)):
+    1. frequencies  omega[h, axis, f] ~ U[0, 0.3)  (shape [H, 3, 8])
+    2. W            [d, d] ~ N(0, 1/d)
+  head (b, h) = PCG64(SeedSequence(seed).spawn(B*H)[b*H + h]):
+    eps_Q [N,d], eps_K [N,d], V [N,d], each standard_normal(dtype=float32)
+Heads are independent streams, so they are generated in parallel threads.
+Q and K are formed in float64 from the float32 draws, rounded once to float32
+and then (bf16 workloads) rounded to bfloat16 with round-to-nearest-even.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional, Sequence, Tuple
 
 import numpy as np
@@ -75,11 +80,14 @@ WORKLOADS = {
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bfloat16 (ties to even), returned as float32 values."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u.astype(np.uint32) << 16).view(np.float32)
+    """float32 -> nearest bfloat16 (ties to even), returned as float32 values.
+    Finite inputs below the largest bfloat16 only."""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    bias = (u >> 16) & 1
+    bias += 0x7FFF
+    u += bias
+    u &= 0xFFFF0000
+    return u.view(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -147,35 +155,46 @@ def make_inputs(B: int, H: int, grid: Tuple[int, int, int], d: int, dtype: str =
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
-    rng = np.random.Generator(np.random.PCG64(seed))
+    ss = np.random.SeedSequence(seed)
+    rng = np.random.Generator(np.random.PCG64(ss))
     pos = grid_positions(grid)
     if n_tokens is not None:
         pos = pos[:n_tokens]
     N = pos.shape[0]
     omega = rng.uniform(0.0, FREQ_MAX, size=(H, 3, N_FREQ))
     w = (rng.standard_normal((d, d)) / np.sqrt(d)).astype(np.float32)
+    children = ss.spawn(B * H)
+    cos = sin = None
     if rope:
         cos, sin = rope_tables(pos, d)
     q = np.empty((B, H, N, d), np.float32)
     k = np.empty((B, H, N, d), np.float32)
     v = np.empty((B, H, N, d), np.float32)
     chan = np.arange(d) % (2 * 3 * N_FREQ)
-    for h in range(H):
+
+    def one_head(bh: int) -> None:
+        b, h = divmod(bh, H)
+        g = np.random.Generator(np.random.PCG64(children[bh]))
         feats = positional_features(pos, omega[h])[:, chan]     # [N, d]
-        for b in range(B):
-            eq = rng.standard_normal((N, d))
-            ek = rng.standard_normal((N, d))
-            vv = rng.standard_normal((N, d))
-            qh = NOISE * eq + feats
-            kh = NOISE * ek + feats
-            if rope:
-                qh = apply_rope(qh, cos, sin)
-                kh = apply_rope(kh, cos, sin)
-            q[b, h] = qh
-            k[b, h] = kh
-            v[b, h] = vv
-    if dtype == "bf16":
-        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+        eq = g.standard_normal((N, d), dtype=np.float32)
+        ek = g.standard_normal((N, d), dtype=np.float32)
+        vv = g.standard_normal((N, d), dtype=np.float32)
+        qh = NOISE * eq.astype(np.float64) + feats
+        kh = NOISE * ek.astype(np.float64) + feats
+        if rope:
+            qh = apply_rope(qh, cos, sin)
+            kh = apply_rope(kh, cos, sin)
+        q[b, h] = qh
+        k[b, h] = kh
+        v[b, h] = vv
+        if dtype == "bf16":
+            q[b, h] = round_bf16(q[b, h])
+            k[b, h] = round_bf16(k[b, h])
+            v[b, h] = round_bf16(v[b, h])
+
+    workers = max(1, min(16, os.cpu_count() or 1, B * H))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one_head, range(B * H)))
     return Inputs(q, k, v, w, dtype, grid)
 
 

@@ -1,0 +1,110 @@
+"""The C-ABI library: it loads, exports every symbol include/sla.h declares,
+and rejects bad arguments on the host before launching anything (no GPU
+needed for these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_video_sla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_video_sla_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sla_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_version(lib):
+    assert lib.sla_version() >= 100
+
+
+def test_counts(lib):
+    kc, kn = ctypes.c_int(), ctypes.c_int()
+    assert lib.sla_counts(512, 0.05, 0.10, ctypes.byref(kc), ctypes.byref(kn)) == _lib.SLA_OK
+    assert (kc.value, kn.value) == (26, 51)
+    assert lib.sla_counts(1857, 1.0, 0.0, ctypes.byref(kc), ctypes.byref(kn)) == _lib.SLA_OK
+    assert (kc.value, kn.value) == (1857, 0)
+    assert lib.sla_counts(512, 0.6, 0.5, ctypes.byref(kc), ctypes.byref(kn)) == _lib.SLA_ERR_INVALID_ARG
+    assert b"fractions" in lib.sla_last_error()
+
+
+def test_counts_match_golden(lib):
+    path = os.path.join(ROOT, "tests", "golden", "counts.txt")
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        Nb, rc, rn, ekc, ekn = line.split()
+        kc, kn = ctypes.c_int(), ctypes.c_int()
+        assert lib.sla_counts(int(Nb), float(rc), float(rn), ctypes.byref(kc), ctypes.byref(kn)) == 0
+        assert (kc.value, kn.value) == (int(ekc), int(ekn))
+
+
+def test_workspace_size(lib):
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(1, 12, 32760, 128, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n)) == 0
+    assert n.value > 0
+    big = n.value
+    assert lib.sla_workspace_size(1, 12, 32760, 128, 64, _lib.SLA_BF16, 1.0, 0.0, ctypes.byref(n)) == 0
+    assert n.value < big        # no marginal blocks: no linear states
+    assert lib.sla_workspace_size(1, 12, 32760, 96, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n)) == _lib.SLA_ERR_UNSUPPORTED
+    assert lib.sla_workspace_size(1, 12, 32760, 128, 32, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n)) == _lib.SLA_ERR_UNSUPPORTED
+    assert lib.sla_workspace_size(1, 12, 64 * 2433, 128, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n)) == _lib.SLA_ERR_UNSUPPORTED
+    assert lib.sla_workspace_size(0, 12, 100, 128, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n)) == _lib.SLA_ERR_INVALID_ARG
+    assert lib.sla_workspace_size(1, 1, 100, 128, 64, 7, 0.05, 0.10, ctypes.byref(n)) == _lib.SLA_ERR_UNSUPPORTED
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, ind=_lib.SLA_BF16, outd=_lib.SLA_F32, B=1, H=1, N=128, d=128,
+             block=64, rc=0.05, rn=0.10, phi=0, out=FAKE, mask=None, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.sla_forward(a["q"], a["k"], a["v"], a["w"], a["ind"], a["outd"], a["B"], a["H"], a["N"], a["d"],
+                           a["block"], a["rc"], a["rn"], a["phi"], a["out"], a["mask"], a["ws"], a["wsb"],
+                           a["stream"])
+
+
+def test_forward_rejects_before_launch(lib):
+    assert fwd(lib, q=None) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd(lib, out=None) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd(lib, d=32) == _lib.SLA_ERR_UNSUPPORTED
+    assert fwd(lib, block=128) == _lib.SLA_ERR_UNSUPPORTED
+    assert fwd(lib, N=0) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd(lib, rc=0.7, rn=0.4) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd(lib, rc=-0.1) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd(lib, phi=1) == _lib.SLA_ERR_UNSUPPORTED
+    assert fwd(lib, ind=_lib.SLA_F32, outd=_lib.SLA_BF16) == _lib.SLA_ERR_UNSUPPORTED
+    assert fwd(lib, wsb=16) == _lib.SLA_ERR_WORKSPACE
+    assert b"workspace" in lib.sla_last_error()
+    n = ctypes.c_size_t()
+    lib.sla_workspace_size(1, 1, 128, 128, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n))
+    assert fwd(lib, ws=FAKE + 8, wsb=n.value) == _lib.SLA_ERR_INVALID_ARG   # misaligned workspace
+
+
+def test_pool_classify_reject(lib):
+    assert lib.sla_pool(None, FAKE, _lib.SLA_BF16, 1, 1, 64, 128, 64, FAKE, FAKE, None) == _lib.SLA_ERR_INVALID_ARG
+    assert lib.sla_pool(FAKE, FAKE, _lib.SLA_BF16, 1, 1, 64, 100, 64, FAKE, FAKE, None) == _lib.SLA_ERR_UNSUPPORTED
+    assert lib.sla_classify(FAKE, FAKE, 1, 1, 8, 128, 0.5, 0.1, None, FAKE, None, None, None) == _lib.SLA_ERR_INVALID_ARG
+    assert lib.sla_classify(FAKE, FAKE, 1, 1, 8, 128, 0.5, 0.1, FAKE, None, None, None, None) == _lib.SLA_ERR_INVALID_ARG
+    assert lib.sla_classify(FAKE, FAKE, 1, 1, 2433, 128, 0.05, 0.1, FAKE, FAKE, None, None, None) == _lib.SLA_ERR_UNSUPPORTED

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: masks, critical lists and pooled means bit-exact; outputs for bf16
+inputs within max|d| <= 1e-2 and relative L2 <= 5e-3 of the fp64 oracle, for
+float32 inputs within 1e-5 (both).  Small cases compare every output row;
+the five named workloads compare every mask row and a seeded sample of
+query blocks (always including the first and the ragged last block).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from sparse_attention_video_sla_amd.inputs import WORKLOADS, make_inputs, make_workload, sample_query_blocks
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def sla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_video_sla_amd as sla
+    sla._lib.load()
+    return sla
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def gpu_forward(sla, inp, rc, rn, out_dtype=None):
+    q, k, v = dev(inp.q, inp.dtype), dev(inp.k, inp.dtype), dev(inp.v, inp.dtype)
+    w = torch.from_numpy(inp.w).to("cuda")
+    out, mask = sla.forward(q, k, v, w, rc, rn, out_dtype=out_dtype, return_mask=True)
+    torch.cuda.synchronize()
+    return out, mask
+
+
+TOL = {"bf16": (1e-2, 5e-3), "f32": (1e-5, 1e-5)}
+
+
+def compare_rows(out_gpu, res, N, dtype, extra_abs=None):
+    """out_gpu: [B,H,N,d] torch; res: oracle result with 'rows' and 'o'."""
+    B, H = out_gpu.shape[:2]
+    flat = out_gpu.reshape(B * H, N, -1)
+    diffs, refs = [], []
+    worst = 0.0
+    for r, (bh, i) in enumerate(res["rows"]):
+        n = min(64, N - 64 * i)
+        g = flat[bh, 64 * i:64 * i + n].float().cpu().numpy().astype(np.float64)
+        ref = res["o"][r, :n]
+        d = g - ref
+        tol = TOL[dtype][0] if extra_abs is None else TOL[dtype][0] + extra_abs * np.abs(ref)
+        bad = np.abs(d) > tol
+        assert not bad.any(), "row (bh=%d, block=%d): max|d| %.3g" % (bh, i, np.abs(d).max())
+        worst = max(worst, float(np.abs(d).max()))
+        diffs.append(d.ravel())
+        refs.append(ref.ravel())
+    d = np.concatenate(diffs)
+    ref = np.concatenate(refs)
+    rel = np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= TOL[dtype][1], "relative L2 %.3g" % rel
+    return worst, rel
+
+
+# ------------------------------------------------------------------ stage checks
+
+
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 1000), ("bf16", 64, 4096), ("f32", 64, 777), ("f32", 128, 200)])
+def test_pool_bit_exact(sla, dtype, d, N):
+    say("pool", dtype, d, N)
+    inp = make_inputs(2, 3, (1, 1, N), d, dtype, seed=11)
+    qp, kp = sla.pool(dev(inp.q, dtype), dev(inp.k, dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(qp.cpu().numpy(), orc.pool(inp.q))
+    assert np.array_equal(kp.cpu().numpy(), orc.pool(inp.k))
+
+
+@pytest.mark.parametrize("Nb,d,rc,rn", [(64, 64, 0.05, 0.10), (512, 128, 0.05, 0.10), (100, 128, 0.3, 0.3),
+                                        (70, 64, 0.0, 0.5), (33, 128, 1.0, 0.0), (1857, 128, 0.05, 0.10),
+                                        (2432, 64, 0.02, 0.01)])
+def test_classify_bit_exact(sla, Nb, d, rc, rn):
+    say("classify", Nb, d, rc, rn)
+    rng = np.random.default_rng(Nb)
+    qp = rng.standard_normal((1, 2, Nb, d)).astype(np.float32)
+    kp = rng.standard_normal((1, 2, Nb, d)).astype(np.float32)
+    ref = orc.classify(qp, kp, rc, rn, want_pc=True)
+    got = sla.classify(dev(qp, "f32"), dev(kp, "f32"), rc, rn, want_excl=True, want_pc=True)
+    torch.cuda.synchronize()
+    assert (got["k_c"], got["k_n"]) == (ref["k_c"], ref["k_n"])
+    assert np.array_equal(got["mask"].cpu().numpy(), ref["mask"])
+    assert np.array_equal(got["crit"].cpu().numpy(), ref["crit"])
+    excl = np.sort(np.concatenate([ref["crit"], ref["negl"]], axis=-1), axis=-1)
+    assert np.array_equal(got["excl"].cpu().numpy(), excl)
+    assert np.allclose(got["pc"].cpu().numpy(), ref["pc"], rtol=1e-5, atol=1e-9)
+
+
+def test_classify_ties(sla):
+    """Equal scores: the lower block index ranks higher at both ends."""
+    say("classify ties")
+    rng = np.random.default_rng(5)
+    kp = rng.standard_normal((1, 1, 200, 64)).astype(np.float32)
+    kp[0, 0, 100:150] = kp[0, 0, 10]          # 51 identical blocks
+    qp = rng.standard_normal((1, 1, 200, 64)).astype(np.float32)
+    qp[0, 0, :50] = 0.0                        # all-zero rows: every score ties at 0
+    for rc, rn in [(0.05, 0.10), (0.2, 0.3), (0.5, 0.5)]:
+        ref = orc.classify(qp, kp, rc, rn)
+        got = sla.classify(dev(qp, "f32"), dev(kp, "f32"), rc, rn)
+        torch.cuda.synchronize()
+        assert np.array_equal(got["mask"].cpu().numpy(), ref["mask"])
+        assert np.array_equal(got["crit"].cpu().numpy(), ref["crit"])
+
+
+# ------------------------------------------------------------------ forward, small
+
+
+SMALL = [
+    # B, H, N, d, dtype, rc, rn
+    (1, 2, 1000, 128, "bf16", 0.05, 0.10),
+    (1, 2, 4096, 128, "bf16", 0.25, 0.25),
+    (2, 1, 2000, 64, "bf16", 0.10, 0.20),
+    (1, 2, 777, 64, "f32", 0.2, 0.3),
+    (1, 1, 4096, 128, "f32", 0.05, 0.10),
+    (1, 3, 70, 128, "bf16", 0.5, 0.0),
+    (1, 1, 5000, 128, "bf16", 0.0, 0.5),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,rc,rn", SMALL)
+def test_forward_small(sla, B, H, N, d, dtype, rc, rn):
+    say("forward", B, H, N, d, dtype, rc, rn)
+    inp = make_inputs(B, H, (1, 1, N), d, dtype, seed=N + d)
+    out, mask = gpu_forward(sla, inp, rc, rn)
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, rc, rn)
+    assert np.array_equal(mask.cpu().numpy(), res["mask"])
+    worst, rel = compare_rows(out, res, N, dtype)
+    say("  max|d| %.3g rel %.3g" % (worst, rel))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_forward_dense_mode(sla, dtype, d):
+    """100% critical: dense softmax attention over the N valid tokens."""
+    say("dense", dtype, d)
+    N = 1000
+    inp = make_inputs(1, 2, (1, 1, N), d, dtype, seed=7)
+    out, mask = gpu_forward(sla, inp, 1.0, 0.0)
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, 1.0, 0.0)
+    assert np.all(mask.cpu().numpy() == 1)
+    compare_rows(out, res, N, dtype)
+
+
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 1000), ("f32", 64, 4096), ("bf16", 64, 333)])
+def test_forward_linear_mode(sla, dtype, d, N):
+    """0% critical, 0% negligible: linear attention over all tokens, projected."""
+    say("linear", dtype, d, N)
+    inp = make_inputs(1, 2, (1, 1, N), d, dtype, seed=8)
+    out, mask = gpu_forward(sla, inp, 0.0, 0.0)
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, 0.0, 0.0)
+    assert np.all(mask.cpu().numpy() == 0)
+    compare_rows(out, res, N, dtype)
+
+
+def test_value_offset_reaches_linear_branch(sla):
+    """V + v0 must move O by v0 + W v0 (the linear branch carries W v0)."""
+    say("value offset")
+    inp = make_inputs(1, 2, (4, 16, 16), 128, "bf16", seed=21)
+    inp.v = (np.clip(np.round(inp.v * 8), -32, 32) / 8).astype(np.float32)   # V and V + v0 exact in bf16
+    v0 = ((np.arange(128) % 16) - 8).astype(np.float32) / 4
+    out0, _ = gpu_forward(sla, inp, 0.05, 0.10)
+    inp.v = inp.v + v0
+    out1, _ = gpu_forward(sla, inp, 0.05, 0.10)
+    shift = v0.astype(np.float64) + inp.w.astype(np.float64) @ v0.astype(np.float64)
+    d = (out1.double() - out0.double()).cpu().numpy() - shift
+    assert np.abs(d).max() < 2e-2
+
+
+def test_bf16_output(sla):
+    say("bf16 out")
+    N = 1500
+    inp = make_inputs(1, 2, (1, 1, N), 128, "bf16", seed=3)
+    out, _ = gpu_forward(sla, inp, 0.1, 0.1, out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, 0.1, 0.1)
+    compare_rows(out, res, N, "bf16", extra_abs=2.0 ** -8)
+
+
+def test_deterministic(sla):
+    say("determinism")
+    inp = make_inputs(1, 4, (4, 20, 20), 128, "bf16", seed=4)
+    a, ma = gpu_forward(sla, inp, 0.05, 0.10)
+    b, mb = gpu_forward(sla, inp, 0.05, 0.10)
+    assert torch.equal(a, b) and torch.equal(ma, mb)
+
+
+# ------------------------------------------------------------------ named workloads, full size
+
+
+def run_workload(sla, cid, per_head, fracs=None, sample_seed=77):
+    wl = WORKLOADS[cid]
+    say("workload", cid, wl.name)
+    inp = make_workload(cid)
+    N, Nb = wl.N, -(-wl.N // 64)
+    qp, kp = orc.pool(inp.q), orc.pool(inp.k)
+    for rc, rn in (fracs or wl.fracs):
+        say("  fractions", rc, rn)
+        cls = orc.classify(qp, kp, rc, rn)
+        out, mask = gpu_forward(sla, inp, rc, rn)
+        assert np.array_equal(mask.cpu().numpy(), cls["mask"]), "mask mismatch"
+        rows = sample_query_blocks(wl.B, wl.H, Nb, per_head, sample_seed, include=(0, Nb - 1))
+        res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, rc, rn, rows=rows, cls=cls)
+        worst, rel = compare_rows(out, res, N, wl.dtype)
+        say("  max|d| %.3g rel %.3g over %d query blocks" % (worst, rel, len(rows)))
+        del out, mask
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_workload0_tiny_all_rows(sla):
+    wl = WORKLOADS[0]
+    inp = make_workload(0)
+    out, mask = gpu_forward(sla, inp, 0.05, 0.10)
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, 0.05, 0.10)
+    assert np.array_equal(mask.cpu().numpy(), res["mask"])
+    compare_rows(out, res, wl.N, "f32")
+
+
+@pytest.mark.timeout(600)
+def test_workload1_wan480p(sla):
+    run_workload(sla, 1, per_head=6)
+
+
+@pytest.mark.timeout(600)
+def test_workload1_all_marginal(sla):
+    """The linear branch alone at the metric workload's size."""
+    run_workload(sla, 1, per_head=2, fracs=[(0.0, 0.0)])
+
+
+@pytest.mark.timeout(900)
+def test_workload2_rope_cfg_pair(sla):
+    run_workload(sla, 2, per_head=3)
+
+
+@pytest.mark.timeout(900)
+def test_workload3_720p(sla):
+    run_workload(sla, 3, per_head=2)
+
+
+@pytest.mark.timeout(900)
+def test_workload4_hunyuan(sla):
+    run_workload(sla, 4, per_head=2, fracs=[(0.05, 0.10)])
+
+
+@pytest.mark.timeout(900)
+def test_workload4_dense(sla):
+    run_workload(sla, 4, per_head=1, fracs=[(1.0, 0.0)])

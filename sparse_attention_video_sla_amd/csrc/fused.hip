@@ -175,11 +175,15 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
     __syncthreads();
     float *xb = reinterpret_cast<float *>(lds);
     {
+        // channel tiles are picked with wave-uniform selects, never with a runtime
+        // index into o[] (that would move the accumulators to scratch memory)
         float *dst = xb + ((qh * 2 + (1 - kh)) * HT) * 16 * 64;
 #pragma unroll
-        for (int t = 0; t < HT; ++t)
+        for (int t = 0; t < HT; ++t) {
+            const f32x16 send = kh ? o[t] : o[HT + t];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[(t * 16 + r) * 64 + lane] = o[(1 - kh) * HT + t][r];
+            for (int r = 0; r < 16; ++r) dst[(t * 16 + r) * 64 + lane] = send[r];
+        }
         float *ml = xb + 4 * HT * 16 * 64;
         ml[((qh * 2 + kh) * 2 + 0) * 64 + lane] = m;
         ml[((qh * 2 + kh) * 2 + 1) * 64 + lane] = l;
@@ -197,10 +201,11 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
         const float L = l * fs + lp * fp;
         const float inv = (L > 0.f) ? 1.f / L : 0.f;
 #pragma unroll
-        for (int t = 0; t < HT; ++t)
+        for (int t = 0; t < HT; ++t) {
+            const f32x16 keep = kh ? o[HT + t] : o[t];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                os[t][r] = (o[kh * HT + t][r] * fs + src[(t * 16 + r) * 64 + lane] * fp) * inv;
+            for (int r = 0; r < 16; ++r) os[t][r] = (keep[r] * fs + src[(t * 16 + r) * 64 + lane] * fp) * inv;
+        }
     }
 
     // linear part

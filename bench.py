@@ -116,7 +116,7 @@ def main():
     value = f_comp / (ms * 1e-3) / 1e12
     t_fused = stage_ms["fused"] * 1e-3
     achieved = f_fused / t_fused / 1e12 if t_fused > 0 else 0.0
-    Lp = -(-(d * d + d) // 128) * 128
+    Lp = -(-(d * d + d) // 256) * 256
     nbytes = {
         "pool": 2 * B * H * N * d * 2 + 2 * B * H * Nb * d * 4,
         "state": 2 * B * H * N * d * 2 + B * H * Nb * d * 64 * 2 + B * H * Nb * Lp * 2,

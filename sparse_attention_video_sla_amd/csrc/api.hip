@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/sla.h"
+#include "sla.h"
 #include "sla_launch.h"
 
 namespace {
@@ -73,7 +73,7 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     const long BH = (long)B * H;
     L.Nb = (N + 63) / 64;
     L.Nbc = (int)round_up(L.Nb, 32);
-    L.Lp = (int)round_up((long)d * d + d, 128);
+    L.Lp = (int)round_up((long)d * d + d, 256);
     L.kc = kc;
     L.kn = kn;
     const size_t es = f32 ? 4 : 2;   // state / exclusion element size
@@ -88,7 +88,7 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     const bool states = kc + kn < L.Nb;
     L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
     L.vt = take(kc > 0 ? ts * BH * L.Nb * d * 64 : 0);
-    L.hs = take(states ? es * BH * L.Nb * L.Lp : 0);
+    L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // blocks interleaved by 8, padded to Nbc
     L.hhat = take(states ? es * BH * L.Nb * L.Lp : 0);
     L.total = off;
     return L;

@@ -13,10 +13,15 @@
 // token count: the linear output phi(q) H / (phi(q).Z) does not depend on a
 // common scale of H and Z, and this one keeps |values| <= max|V W^T|.
 //
-// Tile: 128 rows x 128 columns per workgroup, 4 waves of 64 x 64, K-steps of
-// 32 key blocks double-buffered through LDS; Hs arrives row-major (columns
-// contiguous) and is transposed on its way into LDS so that each lane reads
-// 8 consecutive key blocks of one column as its B fragment.
+// The product is computed transposed, D^T = Hs^T E^T (M = state column, N =
+// query-block row, K = key block), so that each lane ends with 4 consecutive
+// columns of one output row.  Tile: 256 columns x 128 rows per workgroup, 4
+// waves of 128 x 64, K-steps of 32 key blocks double-buffered through LDS.
+// Hs arrives interleaved by 8 blocks (see state.hip): an A fragment (8
+// consecutive blocks of one column) is one 16-byte chunk, staged and read back
+// without any transposition; E rows are staged with a padded stride that keeps
+// the B fragment reads free of bank conflicts.  Each thread owns one column of
+// the tile for the totals and adds the 8 blocks of every chunk it stages.
 #include "sla_device.h"
 #include "sla_launch.h"
 
@@ -27,119 +32,124 @@ __global__ __launch_bounds__(256) void assemble_kernel(const S *__restrict__ E, 
                                                        const int32_t *__restrict__ mcount,
                                                        S *__restrict__ hhat, int Nb, int Nbc, int Lp,
                                                        int tiles_m, int tiles_n) {
-    constexpr int EPC = 16 / sizeof(S);     // elements per 16-byte chunk
-    constexpr int CPR = 128 / EPC;          // chunks per 128-column row
-    constexpr int TPC = 256 / CPR;          // threads sharing one column group
-    constexpr int NCH = 32 * CPR / 256;     // chunks per thread per stage
-    constexpr int BSTR = 32 + EPC;          // transposed tile row stride
-    __shared__ S Bs[2][128 * BSTR];
-    __shared__ float red[TPC][128];
-    __shared__ float totc[128];
+    constexpr int TM = 256, TN = 128, TK = 32;
+    constexpr int EPC = 16 / sizeof(S);                  // elements per 16-byte chunk
+    constexpr int AC = 8 * sizeof(S) / 16;               // chunks per (group, column): 1 f16, 2 float
+    constexpr int NA = (TK / 8) * TM * AC / 256;         // A chunks per thread
+    constexpr int BCPR = TK / EPC;                       // chunks per staged E row
+    constexpr int NB = TN * BCPR / 256;                  // B chunks per thread
+    constexpr int BSTR = TK + EPC;                       // padded E row stride
+    __shared__ __attribute__((aligned(16))) S As[2][(TK / 8) * TM * 8];
+    __shared__ __attribute__((aligned(16))) S Bs[2][TN * BSTR];
+    __shared__ float tot_s[TM];
+    __shared__ float scale_s[TN];
 
     const int bid = blockIdx.x;
-    const int tm = bid % tiles_m;
-    const int rest = bid / tiles_m;
-    const int tn = rest % tiles_n;
-    const long bh = rest / tiles_n;
-    const int row0 = 128 * tm, col0 = 128 * tn;
+    const int tn = bid % tiles_n;
+    const int rest = bid / tiles_n;
+    const int tm = rest % tiles_m;
+    const long bh = rest / tiles_m;
+    const int col0 = TM * tm, row0 = TN * tn;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wm = wave & 1, wn = wave >> 1;
     const S *Eh = E + bh * Nb * (long)Nbc;
-    const S *Hh = hs + bh * Nb * (long)Lp;
+    const S *Hh = hs + bh * (long)(Nbc / 8) * Lp * 8;
 
-    const int cg = tid % CPR, jr = tid / CPR;
-    float tot[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) tot[e] = 0.f;
-    Chunk pre[NCH];
+    float tot = 0.f;                     // column col0 + tid (every thread owns one)
+    Chunk pa[NA], pb[NB];
     auto gload = [&](int j0) {
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int j = j0 + jr + TPC * u;
-            pre[u] = (j < Nb) ? ld_chunk(Hh + (long)j * Lp + col0 + cg * EPC) : zero_chunk();
+        for (int u = 0; u < NA; ++u) {
+            const int g = u / AC, part = u % AC;        // group within the step, chunk within the column
+            pa[u] = ld_chunk(Hh + (((long)(j0 / 8 + g) * Lp + col0 + tid) * 8) + part * EPC);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int idx = tid + 256 * u, row = idx / BCPR, q = idx % BCPR;
+            pb[u] = (row0 + row < Nb) ? ld_chunk(Eh + (long)(row0 + row) * Nbc + j0 + q * EPC) : zero_chunk();
         }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int jj = jr + TPC * u;
-            const S *x = reinterpret_cast<const S *>(&pre[u]);
+        for (int u = 0; u < NA; ++u) {
+            const int g = u / AC, part = u % AC;
+            st_chunk(&As[buf][(g * TM + tid) * 8 + part * EPC], pa[u]);
+            const S *x = reinterpret_cast<const S *>(&pa[u]);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                Bs[buf][(cg * EPC + e) * BSTR + jj] = x[e];
-                tot[e] += to_f32<S>(x[e]);
-            }
+            for (int e = 0; e < EPC; ++e) tot += to_f32<S>(x[e]);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int idx = tid + 256 * u, row = idx / BCPR, q = idx % BCPR;
+            st_chunk(&Bs[buf][row * BSTR + q * EPC], pb[u]);
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
-    const int nst = Nbc / 32;
+    const int nst = Nbc / TK;
     gload(0);
     lstore(0);
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
-        if (st + 1 < nst) gload(32 * (st + 1));
+        if (st + 1 < nst) gload(TK * (st + 1));
         const int buf = st & 1;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            v8<S> a[2];
+        for (int s = 0; s < TK / 16; ++s) {
+            v8<S> b[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int i = row0 + 64 * wr + 32 * mt + l32;
-                a[mt] = (i < Nb) ? ld8<S>(Eh + (long)i * Nbc + 32 * st + 16 * ks + 8 * hh) : zero8<S>();
-            }
+            for (int nt = 0; nt < 2; ++nt)
+                b[nt] = ld8<S>(&Bs[buf][(64 * wn + 32 * nt + l32) * BSTR + 16 * s + 8 * hh]);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const v8<S> b = ld8<S>(&Bs[buf][(64 * wc + 32 * nt + l32) * BSTR + 16 * ks + 8 * hh]);
+            for (int mt = 0; mt < 4; ++mt) {
+                const v8<S> a = ld8<S>(&As[buf][((2 * s + hh) * TM + 128 * wm + 32 * mt + l32) * 8]);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) mma16(acc[mt][nt], a[mt], b);
+                for (int nt = 0; nt < 2; ++nt) mma16(acc[mt][nt], a, b[nt]);
             }
         }
         if (st + 1 < nst) lstore(buf ^ 1);
         __syncthreads();
     }
 
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) red[jr][cg * EPC + e] = tot[e];
-    __syncthreads();
-    if (tid < 128) {
-        float t = 0.f;
-#pragma unroll
-        for (int x = 0; x < TPC; ++x) t += red[x][tid];
-        totc[tid] = t;
+    tot_s[tid] = tot;
+    if (tid < TN) {
+        const int i = row0 + tid;
+        const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
+        scale_s[tid] = mc > 0 ? 64.f / (float)mc : 0.f;
     }
     __syncthreads();
 
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int nt = 0; nt < 2; ++nt) {
+        const int il = 64 * wn + 32 * nt + l32;
+        const int i = row0 + il;
+        if (i >= Nb) continue;
+        const float sc = scale_s[il];
+        S *orow = hhat + (bh * Nb + i) * (long)Lp + col0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = row0 + 64 * wr + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (i >= Nb) continue;
-            const int mc = mcount[bh * Nb + i];
-            const float sc = mc > 0 ? 64.f / (float)mc : 0.f;
-            S *orow = hhat + (bh * Nb + i) * (long)Lp + col0;
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int col = 64 * wc + 32 * nt + l32;
-                orow[col] = from_f32<S>((totc[col] - acc[mt][nt][r]) * sc);
+            for (int g = 0; g < 4; ++g) {
+                const int cl = 128 * wm + 32 * mt + 8 * g + 4 * hh;
+                v4<S> y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = from_f32<S>((tot_s[cl + e] - acc[mt][nt][4 * g + e]) * sc);
+                __builtin_memcpy(orow + cl, &y, sizeof(y));
             }
-        }
     }
 }
 
 template <typename S>
 static hipError_t launch_assemble_t(const AssembleArgs &a, hipStream_t st) {
-    const int tiles_m = (a.Nb + 127) / 128;
-    const int tiles_n = a.Lp / 128;
+    const int tiles_m = a.Lp / 256;             // column tiles (Lp is a multiple of 256)
+    const int tiles_n = (a.Nb + 127) / 128;     // row tiles
     const unsigned grid = (unsigned)(a.BH * tiles_m * tiles_n);
     assemble_kernel<S><<<grid, 256, 0, st>>>((const S *)a.E, (const S *)a.hs, a.mcount, (S *)a.hhat,
                                              a.Nb, a.Nbc, a.Lp, tiles_m, tiles_n);

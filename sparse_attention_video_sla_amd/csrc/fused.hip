@@ -45,8 +45,8 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
                                                        TO *__restrict__ out, long G, int per_xcd, int N,
                                                        int Nb, float sl2) {
     constexpr int EPC = 16 / sizeof(T);
-    constexpr int KSTR = D + EPC;            // K tile row stride (elements)
-    constexpr int VSTR = 64 + EPC;           // V^T tile row stride
+    constexpr int KSTR = D + EPC;            // K tile row stride (elements): conflict-free 16-byte reads
+    constexpr int VSTR = 64 + 4;             // V^T tile row stride: conflict-free 8-byte reads
     constexpr int KT = 64 * KSTR, VT = D * VSTR;
     constexpr int CPR_K = D / EPC, CPR_V = 64 / EPC;
     constexpr int NK = 64 * CPR_K / 256, NV = D * CPR_V / 256;
@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
     constexpr int NCT = D / 32;              // 32-channel tiles
     constexpr int HT = D / 64;               // channel tiles per key half after the merge
     constexpr float NEG_INF = -__builtin_inff();
+    constexpr float TAU = 8.f;               // lazy rescale: P may reach 2^TAU before O is rescaled
     __shared__ __attribute__((aligned(16))) T lds[2 * (KT + VT)];
 
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -80,94 +81,126 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
         for (int r = 0; r < 16; ++r) o[ct][r] = 0.f;
 
     const int32_t *cl = crit + (bh * Nb + i) * (long)kc;
-    Chunk pk[NK], pv[NV];
-    auto gload = [&](int j) {
-        const T *kb = k + (bh * N + 64L * j) * D;
-        const T *vb = vt + (bh * Nb + j) * (long)D * 64;
+    // one buffer resource per head: loads past the head's end come back as zeros
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, (uint32_t)((long)N * D * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + bh * Nb * (long)D * 64, (uint32_t)((long)Nb * D * 64 * sizeof(T)));
+    uint32_t vok[NK], vov[NV];
 #pragma unroll
-        for (int u = 0; u < NK; ++u) {
-            const int ch = tid + 256 * u, row = ch / CPR_K, cc = ch % CPR_K;
-            pk[u] = (64 * j + row < N) ? ld_chunk(kb + (long)row * D + cc * EPC) : zero_chunk();
-        }
+    for (int u = 0; u < NK; ++u) {
+        const int ch = tid + 256 * u;
+        vok[u] = (uint32_t)(((ch / CPR_K) * D + (ch % CPR_K) * EPC) * sizeof(T));
+    }
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int ch = tid + 256 * u, c = ch / CPR_V, cc = ch % CPR_V;
-            pv[u] = ld_chunk(vb + c * 64 + cc * EPC);
-        }
+    for (int u = 0; u < NV; ++u) {
+        const int ch = tid + 256 * u;
+        vov[u] = (uint32_t)(((ch / CPR_V) * 64 + (ch % CPR_V) * EPC) * sizeof(T));
+    }
+    // Two register stages (A, B) and two LDS buffers: while tile n is computed
+    // from LDS, tile n+1 sits in one register stage (issued an iteration ago)
+    // and tile n+2 is being fetched into the other, so every load has two
+    // tile times to land.  The stages alternate by an unrolled pair of
+    // iterations, so they are always indexed statically.
+    struct Stage { Chunk k[NK], v[NV]; };
+    Stage ra, rb;
+    auto gload = [&](Stage &st, int j) {
+        const uint32_t sk = (uint32_t)(64L * j * D * sizeof(T));
+        const uint32_t sv = (uint32_t)((long)j * D * 64 * sizeof(T));
+#pragma unroll
+        for (int u = 0; u < NK; ++u) st.k[u] = buf_ld(rk, vok[u], sk);
+#pragma unroll
+        for (int u = 0; u < NV; ++u) st.v[u] = buf_ld(rv, vov[u], sv);
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](const Stage &st, int buf) {
         T *Ks = lds + buf * (KT + VT);
         T *Vs = Ks + KT;
 #pragma unroll
         for (int u = 0; u < NK; ++u) {
             const int ch = tid + 256 * u, row = ch / CPR_K, cc = ch % CPR_K;
-            st_chunk(Ks + row * KSTR + cc * EPC, pk[u]);
+            st_chunk(Ks + row * KSTR + cc * EPC, st.k[u]);
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int ch = tid + 256 * u, c = ch / CPR_V, cc = ch % CPR_V;
-            st_chunk(Vs + c * VSTR + cc * EPC, pv[u]);
+            if constexpr ((VSTR * sizeof(T)) % 16 == 0) st_chunk(Vs + c * VSTR + cc * EPC, st.v[u]);
+            else st_chunk8(Vs + c * VSTR + cc * EPC, st.v[u]);
         }
     };
-
-    if (kc > 0) {
-        // list entries are clamped to [0, Nb) so that no index can leave the tensors
-        auto blk_at = [&](int n) { return min(max(cl[n], 0), Nb - 1); };
-        gload(blk_at(0));
-        lstore(0);
-        __syncthreads();
-        for (int n = 0; n < kc; ++n) {
-            const int j = blk_at(n);
-            if (n + 1 < kc) gload(blk_at(n + 1));
-            const T *Ks = lds + (n & 1) * (KT + VT);
-            const T *Vs = Ks + KT;
-            // S^T (keys 32kh.. of the tile x this wave's 32 queries)
-            f32x16 sacc;
+    // one critical tile from LDS buffer `buf` (key block j)
+    auto compute = [&](int buf, int j) {
+        const T *Ks = lds + buf * (KT + VT);
+        const T *Vs = Ks + KT;
+        // S^T (keys 32kh.. of the tile x this wave's 32 queries)
+        f32x16 sacc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) mma16(sacc, ld8<T>(Ks + (32 * kh + l32) * KSTR + 16 * s + 8 * hh), qf[s]);
-            if (64 * j + 64 > N) {
+        for (int s = 0; s < NS; ++s) mma16(sacc, ld8<T>(Ks + (32 * kh + l32) * KSTR + 16 * s + 8 * hh), qf[s]);
+        if (64 * j + 64 > N) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 64 * j + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= N) sacc[r] = NEG_INF;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int key = 64 * j + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= N) sacc[r] = NEG_INF;
             }
-            float mx = sacc[0];
+        }
+        float mx = sacc[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-            mx = fmaxf(mx, shfl_xor32(mx));
-            const float mnew = fmaxf(m, mx * sl2);
-            const float msub = (mnew == NEG_INF) ? 0.f : mnew;
-            const float alpha = fast_exp2(m - msub);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        mx = fmaxf(mx, shfl_xor32(mx)) * sl2;
+        // lazy rescale: move the running max only when the tile exceeds it by TAU
+        if (__ballot(mx > m + TAU)) {
+            const float mnew = fmaxf(m, mx);
+            const float alpha = (mnew == NEG_INF) ? 1.f : fast_exp2(m - mnew);
             l *= alpha;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
             m = mnew;
-            v8<T> pb[2];
-            float ps = 0.f;
+        }
+        const float msub = (m == NEG_INF) ? 0.f : m;
+        v8<T> pb[2];
+        float ps = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[r], sl2, -msub));
-                ps += p;
-                pb[r >> 3][r & 7] = from_f32<T>(p);
+        for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(__builtin_fmaf(sacc[r], sl2, -msub));
+            ps += p;
+            pb[r >> 3][r & 7] = from_f32<T>(p);
+        }
+        l += ps;
+        // O^T (channels x queries) += V^T P^T over this wave's 32 keys, permuted k
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const T *vp = Vs + (32 * ct + l32) * VSTR + 32 * kh + 16 * ks + 4 * hh;
+                mma16(o[ct], ld4x2<T>(vp, vp + 8), pb[ks]);
             }
-            l += ps;
-            // O^T (channels x queries) += V^T P^T over this wave's 32 keys, permuted k
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const T *vp = Vs + (32 * ct + l32) * VSTR + 32 * kh + 16 * ks + 4 * hh;
-                    mma16(o[ct], ld4x2<T>(vp, vp + 8), pb[ks]);
-                }
-            }
-            if (n + 1 < kc) lstore((n + 1) & 1);
+        }
+    };
+
+    if (kc > 0) {
+        // list entries are clamped to [0, Nb) so that no index can leave the tensors
+        auto blk_at = [&](int n) { return min(max(cl[n], 0), Nb - 1); };
+        gload(ra, blk_at(0));
+        if (kc > 1) gload(rb, blk_at(1));
+        lstore(ra, 0);
+        __syncthreads();
+        // invariant at the top of iteration n: LDS buffer n&1 holds tile n and the
+        // register stage of parity (n+1) holds tile n+1 (in flight)
+        int n = 0;
+        for (; n + 1 < kc; n += 2) {
+            // even n: tile n+1 in rb; fetch tile n+2 into ra
+            if (n + 2 < kc) gload(ra, blk_at(n + 2));
+            compute(0, blk_at(n));
+            lstore(rb, 1);
+            __syncthreads();
+            // odd n+1: tile n+2 in ra; fetch tile n+3 into rb
+            if (n + 3 < kc) gload(rb, blk_at(n + 3));
+            compute(1, blk_at(n + 1));
+            if (n + 2 < kc) lstore(ra, 0);
             __syncthreads();
         }
+        if (n < kc) compute(0, blk_at(n));   // odd kc: the last tile, already in buffer 0
     }
     l += shfl_xor32(l);
 

@@ -98,6 +98,28 @@ template <typename E> __device__ __forceinline__ v8<E> ld4x2(const E *p0, const 
     return r;
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer loads through a 128-bit resource: the hardware checks each
+// access against num_records and returns zeros past the end, so a tile that
+// runs over the end of a head needs no per-lane guard.  The resource covers
+// one head, so a ragged last block reads zeros, never the next head.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ Chunk buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    Chunk c;
+    c.w[0] = v[0]; c.w[1] = v[1]; c.w[2] = v[2]; c.w[3] = v[3];
+    return c;
+}
+// 16 bytes to LDS at an address that is only 8-byte aligned
+__device__ __forceinline__ void st_chunk8(void *p, const Chunk &c) {
+    uint32_t *q = reinterpret_cast<uint32_t *>(p);
+    *reinterpret_cast<uint64_t *>(q) = (uint64_t)c.w[0] | ((uint64_t)c.w[1] << 32);
+    *reinterpret_cast<uint64_t *>(q + 2) = (uint64_t)c.w[2] | ((uint64_t)c.w[3] << 32);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -12,7 +12,13 @@
 //   the same linear map as applying it to the output.
 //   z_j = sum_t phi(k_t).
 // Stored per block, scaled by 1/64 (exact) so that values stay within the
-// range of the fp16 staging type: [h'^T row-major (d*d), z (d), zero pad].
+// range of the fp16 staging type, as one "column" vector of Lp values
+// [h'^T row-major (d*d), z (d), zero pad] per block.  The blocks are
+// interleaved by 8: value (block j, column x) sits at ((j/8)*Lp + x)*8 + j%8,
+// so that the assembly GEMM reads 8 consecutive blocks of one column as one
+// 16-byte MFMA fragment.  Blocks past Nb up to the next multiple of 32 are
+// written as zeros.  Workgroups are mapped so that the 8 blocks of a group run
+// back to back on one XCD, whose L2 then merges their interleaved stores.
 // The same kernel writes V_j transposed ([d][64], pad tokens zero) in the
 // input dtype, the layout the fused kernel streams through LDS.
 #include "sla_device.h"
@@ -22,9 +28,9 @@ namespace sla {
 
 template <typename T, typename S, int D>
 __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, const T *__restrict__ v,
-                                                      const float *__restrict__ w, int N, int Nb,
-                                                      T *__restrict__ vt, S *__restrict__ hs, int Lp,
-                                                      int do_states, int do_vt) {
+                                                      const float *__restrict__ w, int N, int Nb, int Nbc,
+                                                      long G, int per_xcd, T *__restrict__ vt,
+                                                      S *__restrict__ hs, int Lp, int do_states, int do_vt) {
     constexpr int NT = 2 * D;
     constexpr int EPC = 16 / sizeof(T);      // input elements per 16-byte chunk
     constexpr int CPR = D / EPC;             // chunks per token row
@@ -35,14 +41,23 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
     __shared__ S Vs[64 * SSTR];
     __shared__ S Pt[D * PSTR];
 
-    const long blk = blockIdx.x;             // bh * Nb + j
-    const int j = (int)(blk % Nb);
-    const long bh = blk / Nb;
+    const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);   // bh * Nbc + j
+    if (logical >= G) return;
+    const int j = (int)(logical % Nbc);
+    const long bh = logical / Nbc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    // interleaved state column of this block: element x at hsb[x * 8]
+    S *hsb = hs + ((bh * (Nbc / 8) + j / 8) * (long)Lp) * 8 + (j % 8);
+    if (j >= Nb) {                           // padding block: zero states only
+        if (do_states)
+            for (int x = tid; x < Lp; x += NT) hsb[(long)x * 8] = from_f32<S>(0.f);
+        return;
+    }
+    const long blk = bh * Nb + j;
     const int n = min(64, N - 64 * j);
     const T *kb = k + (bh * N + 64L * j) * D;
     const T *vb = v + (bh * N + 64L * j) * D;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
 
     Chunk kc[NCH], vc[NCH];
 #pragma unroll
@@ -124,28 +139,32 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
         }
     }
 
-    S *hsb = hs + blk * (long)Lp;
     const float scale = 1.f / 64.f;
 #pragma unroll
     for (int nt = 0; nt < D / 32; ++nt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c = 32 * wave + 8 * (r >> 2) + 4 * hh + (r & 3);
-            hsb[c * D + 32 * nt + l32] = from_f32<S>(acch[nt][r] * scale);
+            hsb[(long)(c * D + 32 * nt + l32) * 8] = from_f32<S>(acch[nt][r] * scale);
         }
     if (tid < D) {
         float z = 0.f;
         for (int t = 0; t < 64; ++t) z += to_f32<S>(Pt[tid * PSTR + t]);
-        hsb[D * D + tid] = from_f32<S>(z * scale);
+        hsb[(long)(D * D + tid) * 8] = from_f32<S>(z * scale);
     }
-    for (int x = D * D + D + tid; x < Lp; x += NT) hsb[x] = from_f32<S>(0.f);
+    for (int x = D * D + D + tid; x < Lp; x += NT) hsb[(long)x * 8] = from_f32<S>(0.f);
 }
 
 template <typename T, typename S, int D>
 static hipError_t launch_state_t(const StateArgs &a, hipStream_t st) {
-    const unsigned grid = (unsigned)(a.BH * a.Nb);
-    state_kernel<T, S, D><<<grid, 2 * D, 0, st>>>((const T *)a.k, (const T *)a.v, a.w, a.N, a.Nb,
-                                                  (T *)a.vt, (S *)a.hs, a.Lp, a.do_states, a.do_vt);
+    const int Nbc = (a.Nb + 31) / 32 * 32;
+    const long G = a.BH * (a.do_states ? Nbc : a.Nb);
+    const int per = (int)((G + 7) / 8);
+    // without states there is no padding: the grid is then bh * Nb blocks, j < Nb
+    const int nbc = a.do_states ? Nbc : a.Nb;
+    state_kernel<T, S, D><<<(unsigned)(8L * per), 2 * D, 0, st>>>((const T *)a.k, (const T *)a.v, a.w, a.N, a.Nb,
+                                                                  nbc, G, per, (T *)a.vt, (S *)a.hs, a.Lp,
+                                                                  a.do_states, a.do_vt);
     return hipGetLastError();
 }
 

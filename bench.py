@@ -117,10 +117,11 @@ def main():
     t_fused = stage_ms["fused"] * 1e-3
     achieved = f_fused / t_fused / 1e12 if t_fused > 0 else 0.0
     Lp = -(-(d * d + d) // 256) * 256
-    nbytes = {
+    Nbc = -(-Nb // 32) * 32
+    nbytes = {   # algorithmic bytes per launch
         "pool": 2 * B * H * N * d * 2 + 2 * B * H * Nb * d * 4,
-        "state": 2 * B * H * N * d * 2 + B * H * Nb * d * 64 * 2 + B * H * Nb * Lp * 2,
-        "assemble": B * H * Nb * (-(-Nb // 32) * 32) * 2 + 2 * B * H * Nb * Lp * 2,
+        "state": 2 * B * H * N * d * 2 + B * H * Nbc * Lp * 2,
+        "assemble": B * H * Nb * Nbc * 2 + B * H * Nbc * Lp * 2 + B * H * Nb * Lp * 2,
     }
     stages = {}
     for name in _lib.STAGES:
@@ -128,7 +129,7 @@ def main():
         if name in nbytes and stage_ms[name] > 0:
             s["GB/s"] = round(nbytes[name] / (stage_ms[name] * 1e-3) / 1e9, 1)
         stages[name] = s
-    stages["assemble"]["TFLOP/s"] = round(2 * B * H * Nb * (-(-Nb // 32) * 32) * Lp / max(stage_ms["assemble"], 1e-9) / 1e9, 1)
+    stages["assemble"]["TFLOP/s"] = round(2 * B * H * Nb * Nbc * Lp / max(stage_ms["assemble"], 1e-9) / 1e9, 1)
     line = {
         "metric": METRIC,
         "value": round(value, 3),

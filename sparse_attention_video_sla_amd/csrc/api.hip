@@ -64,7 +64,7 @@ sla_status check_shape(int B, int H, int N, int d, int block) {
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, E, mcount, vt, hs, hhat, total;
+    size_t qp, kp, mask, crit, E, mcount, hs, hhat, total;
     int Nb, Nbc, Lp, kc, kn;
 };
 
@@ -77,7 +77,6 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.kc = kc;
     L.kn = kn;
     const size_t es = f32 ? 4 : 2;   // state / exclusion element size
-    const size_t ts = f32 ? 4 : 2;   // input element size
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     L.qp = take(sizeof(float) * BH * L.Nb * d);
@@ -87,7 +86,6 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.mcount = take(sizeof(int32_t) * BH * L.Nb);
     const bool states = kc + kn < L.Nb;
     L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
-    L.vt = take(kc > 0 ? ts * BH * L.Nb * d * 64 : 0);
     L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // blocks interleaved by 8, padded to Nbc
     L.hhat = take(states ? es * BH * L.Nb * L.Lp : 0);
     L.total = off;
@@ -251,10 +249,10 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     if (st != SLA_OK) return st;
     mark_stage(ev, 2, s);
 
-    if (states || kc > 0) {
+    if (states) {
         sla::StateArgs sa{};
         sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp;
-        sa.vt = ws + L.vt; sa.hs = ws + L.hs; sa.do_states = states; sa.do_vt = kc > 0; sa.bf16_in = !f32;
+        sa.hs = ws + L.hs; sa.bf16_in = !f32;
         st = device_status(sla::launch_state(sa, s), "state launch");
         if (st != SLA_OK) return st;
     }
@@ -268,7 +266,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     }
     mark_stage(ev, 4, s);
     sla::FusedArgs fa{};
-    fa.q = q; fa.k = k; fa.vt = ws + L.vt; fa.crit = crit; fa.kc = kc;
+    fa.q = q; fa.k = k; fa.v = v; fa.crit = crit; fa.kc = kc;
     fa.hhat = ws + L.hhat; fa.mcount = states ? mcount : nullptr; fa.Lp = L.Lp;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;

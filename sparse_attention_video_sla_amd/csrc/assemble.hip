@@ -17,53 +17,59 @@
 // query-block row, K = key block), so that each lane ends with 4 consecutive
 // columns of one output row.  Tile: 256 columns x 128 rows per workgroup, 4
 // waves of 128 x 64, K-steps of 32 key blocks double-buffered through LDS.
-// Hs arrives interleaved by 8 blocks (see state.hip): an A fragment (8
-// consecutive blocks of one column) is one 16-byte chunk, staged and read back
-// without any transposition; E rows are staged with a padded stride that keeps
-// the B fragment reads free of bank conflicts.  Each thread owns one column of
-// the tile for the totals and adds the 8 blocks of every chunk it stages.
+// Hs rows (one per key block, columns contiguous) are staged as they are and
+// the A fragments (8 consecutive blocks of one column) come out of LDS with
+// transposing reads; E rows are staged with a padded stride that keeps the B
+// fragment reads free of bank conflicts.  The totals are summed from the very
+// chunks each thread stages, then reduced across the 8 threads of a column
+// group.  Workgroups are ordered so that the row tiles of one column slice run
+// together on one XCD and share its L2.
 #include "sla_device.h"
 #include "sla_launch.h"
 
 namespace sla {
 
 template <typename S>
-__global__ __launch_bounds__(256) void assemble_kernel(const S *__restrict__ E, const S *__restrict__ hs,
-                                                       const int32_t *__restrict__ mcount,
-                                                       S *__restrict__ hhat, int Nb, int Nbc, int Lp,
-                                                       int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ E, const S *__restrict__ hs,
+                                                          const int32_t *__restrict__ mcount,
+                                                          S *__restrict__ hhat, int Nb, int Nbc, int Lp,
+                                                          int tiles_m, int tiles_n, long G, int per_xcd) {
     constexpr int TM = 256, TN = 128, TK = 32;
     constexpr int EPC = 16 / sizeof(S);                  // elements per 16-byte chunk
-    constexpr int AC = 8 * sizeof(S) / 16;               // chunks per (group, column): 1 f16, 2 float
-    constexpr int NA = (TK / 8) * TM * AC / 256;         // A chunks per thread
+    constexpr int ACPR = TM / EPC;                       // chunks per staged Hs row
+    constexpr int NA = TK * ACPR / 256;                  // A chunks per thread
+    constexpr int TPA = 256 / ACPR;                      // threads sharing one A column group
+    constexpr int ASTR = TM + (sizeof(S) == 2 ? 16 : 8); // staged Hs row stride
     constexpr int BCPR = TK / EPC;                       // chunks per staged E row
     constexpr int NB = TN * BCPR / 256;                  // B chunks per thread
     constexpr int BSTR = TK + EPC;                       // padded E row stride
-    __shared__ __attribute__((aligned(16))) S As[2][(TK / 8) * TM * 8];
+    __shared__ __attribute__((aligned(16))) S As[2][TK * ASTR];
     __shared__ __attribute__((aligned(16))) S Bs[2][TN * BSTR];
-    __shared__ float tot_s[TM];
+    __shared__ float red[TPA][TM];
     __shared__ float scale_s[TN];
 
-    const int bid = blockIdx.x;
-    const int tn = bid % tiles_n;
-    const int rest = bid / tiles_n;
-    const int tm = rest % tiles_m;
+    const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (logical >= G) return;
+    const int tn = (int)(logical % tiles_n);
+    const long rest = logical / tiles_n;
+    const int tm = (int)(rest % tiles_m);
     const long bh = rest / tiles_m;
     const int col0 = TM * tm, row0 = TN * tn;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
+    const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
     const S *Eh = E + bh * Nb * (long)Nbc;
-    const S *Hh = hs + bh * (long)(Nbc / 8) * Lp * 8;
+    const S *Hh = hs + bh * (long)Nbc * Lp;
 
-    float tot = 0.f;                     // column col0 + tid (every thread owns one)
+    const int acg = tid % ACPR, ajr = tid / ACPR;        // this thread's A column group and first row
+    float tot[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) tot[e] = 0.f;
     Chunk pa[NA], pb[NB];
     auto gload = [&](int j0) {
 #pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            const int g = u / AC, part = u % AC;        // group within the step, chunk within the column
-            pa[u] = ld_chunk(Hh + (((long)(j0 / 8 + g) * Lp + col0 + tid) * 8) + part * EPC);
-        }
+        for (int u = 0; u < NA; ++u)
+            pa[u] = ld_chunk(Hh + (long)(j0 + ajr + TPA * u) * Lp + col0 + acg * EPC);
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
             const int idx = tid + 256 * u, row = idx / BCPR, q = idx % BCPR;
@@ -73,11 +79,10 @@ __global__ __launch_bounds__(256) void assemble_kernel(const S *__restrict__ E, 
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < NA; ++u) {
-            const int g = u / AC, part = u % AC;
-            st_chunk(&As[buf][(g * TM + tid) * 8 + part * EPC], pa[u]);
+            st_chunk(&As[buf][(ajr + TPA * u) * ASTR + acg * EPC], pa[u]);
             const S *x = reinterpret_cast<const S *>(&pa[u]);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) tot += to_f32<S>(x[e]);
+            for (int e = 0; e < EPC; ++e) tot[e] += to_f32<S>(x[e]);
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -107,9 +112,12 @@ __global__ __launch_bounds__(256) void assemble_kernel(const S *__restrict__ E, 
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
                 b[nt] = ld8<S>(&Bs[buf][(64 * wn + 32 * nt + l32) * BSTR + 16 * s + 8 * hh]);
+            const int k0 = 16 * s + 8 * (grp >> 1);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const v8<S> a = ld8<S>(&As[buf][((2 * s + hh) * TM + 128 * wm + 32 * mt + l32) * 8]);
+                const int n0 = 128 * wm + 32 * mt + 16 * (grp & 1);
+                const v8<S> a = cat8<S>(lds_col4<S>(As[buf], ASTR, k0, n0, lane),
+                                        lds_col4<S>(As[buf], ASTR, k0 + 4, n0, lane));
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) mma16(acc[mt][nt], a, b[nt]);
             }
@@ -118,11 +126,21 @@ __global__ __launch_bounds__(256) void assemble_kernel(const S *__restrict__ E, 
         __syncthreads();
     }
 
-    tot_s[tid] = tot;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) red[ajr][acg * EPC + e] = tot[e];
     if (tid < TN) {
         const int i = row0 + tid;
         const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
         scale_s[tid] = mc > 0 ? 64.f / (float)mc : 0.f;
+    }
+    __syncthreads();
+    // column totals in LDS (reuse the A staging area)
+    float *tot_s = reinterpret_cast<float *>(&As[0][0]);
+    {
+        float t = 0.f;
+#pragma unroll
+        for (int x = 0; x < TPA; ++x) t += red[x][tid];
+        tot_s[tid] = t;
     }
     __syncthreads();
 
@@ -150,9 +168,11 @@ template <typename S>
 static hipError_t launch_assemble_t(const AssembleArgs &a, hipStream_t st) {
     const int tiles_m = a.Lp / 256;             // column tiles (Lp is a multiple of 256)
     const int tiles_n = (a.Nb + 127) / 128;     // row tiles
-    const unsigned grid = (unsigned)(a.BH * tiles_m * tiles_n);
-    assemble_kernel<S><<<grid, 256, 0, st>>>((const S *)a.E, (const S *)a.hs, a.mcount, (S *)a.hhat,
-                                             a.Nb, a.Nbc, a.Lp, tiles_m, tiles_n);
+    const long G = a.BH * tiles_m * tiles_n;
+    const int per = (int)((G + 7) / 8);
+    assemble_kernel<S><<<(unsigned)(8L * per), 256, 0, st>>>((const S *)a.E, (const S *)a.hs, a.mcount,
+                                                            (S *)a.hhat, a.Nb, a.Nbc, a.Lp, tiles_m,
+                                                            tiles_n, G, per);
     return hipGetLastError();
 }
 

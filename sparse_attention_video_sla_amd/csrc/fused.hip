@@ -7,8 +7,8 @@
 // owns query rows 32qh..32qh+31 and, of every critical key tile, keys
 // 32kh..32kh+31.
 //   Sparse part: the k_c critical key blocks of row i (ascending) are
-//   streamed through double-buffered LDS (K row-major, V pre-transposed by the
-//   state kernel).  Per tile, S^T = K Q^T on 32x32x16 MFMA (Q held in
+//   streamed through double-buffered LDS (K and V tiles row-major, as they lie
+//   in memory; the V^T operand comes out of LDS with transposing reads).  Per tile, S^T = K Q^T on 32x32x16 MFMA (Q held in
 //   registers as the B operand), online softmax in the log2 domain with the
 //   1/sqrt(d) scale folded into one multiply-add, P^T converted to the input
 //   type straight from the accumulator, O^T += V^T P^T on MFMA.  Keys past N
@@ -38,7 +38,7 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float
 
 template <typename T, typename S, int D, typename TO>
 __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                       const T *__restrict__ vt,
+                                                       const T *__restrict__ v,
                                                        const int32_t *__restrict__ crit, int kc,
                                                        const S *__restrict__ hhat,
                                                        const int32_t *__restrict__ mcount, int Lp,
@@ -46,10 +46,10 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
                                                        int Nb, float sl2) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int KSTR = D + EPC;            // K tile row stride (elements): conflict-free 16-byte reads
-    constexpr int VSTR = 64 + 4;             // V^T tile row stride: conflict-free 8-byte reads
-    constexpr int KT = 64 * KSTR, VT = D * VSTR;
-    constexpr int CPR_K = D / EPC, CPR_V = 64 / EPC;
-    constexpr int NK = 64 * CPR_K / 256, NV = D * CPR_V / 256;
+    constexpr int VSTR = D + (sizeof(T) == 2 ? 16 : 4);   // V tile row stride: 8 dwords mod 64 for the transposing reads
+    constexpr int KT = 64 * KSTR, VT = 64 * VSTR;
+    constexpr int CPR_K = D / EPC;
+    constexpr int NK = 64 * CPR_K / 256;
     constexpr int NS = D / 16;               // k-steps over channels
     constexpr int NCT = D / 32;              // 32-channel tiles
     constexpr int HT = D / 64;               // channel tiles per key half after the merge
@@ -83,32 +83,26 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
     const int32_t *cl = crit + (bh * Nb + i) * (long)kc;
     // one buffer resource per head: loads past the head's end come back as zeros
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, (uint32_t)((long)N * D * sizeof(T)));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + bh * Nb * (long)D * 64, (uint32_t)((long)Nb * D * 64 * sizeof(T)));
-    uint32_t vok[NK], vov[NV];
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * N * (long)D, (uint32_t)((long)N * D * sizeof(T)));
+    uint32_t vok[NK];
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
         const int ch = tid + 256 * u;
         vok[u] = (uint32_t)(((ch / CPR_K) * D + (ch % CPR_K) * EPC) * sizeof(T));
-    }
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-        const int ch = tid + 256 * u;
-        vov[u] = (uint32_t)(((ch / CPR_V) * 64 + (ch % CPR_V) * EPC) * sizeof(T));
     }
     // Two register stages (A, B) and two LDS buffers: while tile n is computed
     // from LDS, tile n+1 sits in one register stage (issued an iteration ago)
     // and tile n+2 is being fetched into the other, so every load has two
     // tile times to land.  The stages alternate by an unrolled pair of
     // iterations, so they are always indexed statically.
-    struct Stage { Chunk k[NK], v[NV]; };
+    struct Stage { Chunk k[NK], v[NK]; };
     Stage ra, rb;
     auto gload = [&](Stage &st, int j) {
         const uint32_t sk = (uint32_t)(64L * j * D * sizeof(T));
-        const uint32_t sv = (uint32_t)((long)j * D * 64 * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NK; ++u) st.k[u] = buf_ld(rk, vok[u], sk);
 #pragma unroll
-        for (int u = 0; u < NV; ++u) st.v[u] = buf_ld(rv, vov[u], sv);
+        for (int u = 0; u < NK; ++u) st.v[u] = buf_ld(rv, vok[u], sk);
     };
     auto lstore = [&](const Stage &st, int buf) {
         T *Ks = lds + buf * (KT + VT);
@@ -119,10 +113,9 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
             st_chunk(Ks + row * KSTR + cc * EPC, st.k[u]);
         }
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int ch = tid + 256 * u, c = ch / CPR_V, cc = ch % CPR_V;
-            if constexpr ((VSTR * sizeof(T)) % 16 == 0) st_chunk(Vs + c * VSTR + cc * EPC, st.v[u]);
-            else st_chunk8(Vs + c * VSTR + cc * EPC, st.v[u]);
+        for (int u = 0; u < NK; ++u) {
+            const int ch = tid + 256 * u, row = ch / CPR_K, cc = ch % CPR_K;
+            st_chunk(Vs + row * VSTR + cc * EPC, st.v[u]);
         }
     };
     // one critical tile from LDS buffer `buf` (key block j)
@@ -167,13 +160,17 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
             pb[r >> 3][r & 7] = from_f32<T>(p);
         }
         l += ps;
-        // O^T (channels x queries) += V^T P^T over this wave's 32 keys, permuted k
+        // O^T (channels x queries) += V^T P^T over this wave's 32 keys, in the
+        // permuted key order of P^T: slots 0-3 are keys 16ks+4h+0..3, slots 4-7
+        // keys 16ks+8+4h+0..3, each run read as a column of the V tile
+        const int grp = lane >> 4;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
+            const int n0 = 32 * ct + 16 * (grp & 1);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const T *vp = Vs + (32 * ct + l32) * VSTR + 32 * kh + 16 * ks + 4 * hh;
-                mma16(o[ct], ld4x2<T>(vp, vp + 8), pb[ks]);
+                const int k0 = 32 * kh + 16 * ks + 4 * (grp >> 1);
+                mma16(o[ct], cat8<T>(lds_col4<T>(Vs, VSTR, k0, n0, lane), lds_col4<T>(Vs, VSTR, k0 + 8, n0, lane)), pb[ks]);
             }
         }
     };
@@ -308,7 +305,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
     const int per = (int)((G + 7) / 8);
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
     fused_kernel<T, S, D, TO><<<(unsigned)(8L * per), 256, 0, st>>>(
-        (const T *)a.q, (const T *)a.k, (const T *)a.vt, a.crit, a.kc, (const S *)a.hhat, a.mcount, a.Lp,
+        (const T *)a.q, (const T *)a.k, (const T *)a.v, a.crit, a.kc, (const S *)a.hhat, a.mcount, a.Lp,
         (TO *)a.out, G, per, a.N, a.Nb, sl2);
     return hipGetLastError();
 }

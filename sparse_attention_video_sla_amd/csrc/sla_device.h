@@ -120,6 +120,50 @@ __device__ __forceinline__ void st_chunk8(void *p, const Chunk &c) {
     *reinterpret_cast<uint64_t *>(q + 2) = (uint64_t)c.w[2] | ((uint64_t)c.w[3] << 32);
 }
 
+// ---------------------------------------------------------------- LDS transposing reads
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane L supplies
+// the address of 4 consecutive 16-bit elements (row L of a 16 x 4 block) and
+// lane i receives the elements (4e + i/4, i%4), e = 0..3.  Pointing lane L at
+// T[k0 + L/4][n0 + 4*(L%4)] of a row-major LDS tile T therefore hands lane i
+// the column run T[k0 + e][n0 + i], e = 0..3: four consecutive k-values of one
+// MFMA row/column, read from a tile stored with that row/column contiguous.
+// (k0, n0) are the same for the 16 lanes of a group.  32-bit data has no
+// transposing read; it takes the same values with four scalar reads.
+template <typename E> __device__ __forceinline__ v4<E> lds_tr_raw(const E *p);
+template <> __device__ __forceinline__ v4<bf16> lds_tr_raw<bf16>(const bf16 *p) {
+    typedef __bf16 raw4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+    const raw4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) raw4 *)(p));
+    v4<bf16> o;
+    __builtin_memcpy(&o, &r, sizeof(o));
+    return o;
+}
+template <> __device__ __forceinline__ v4<f16> lds_tr_raw<f16>(const f16 *p) {
+    typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+    const raw4 r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) raw4 *)(p));
+    v4<f16> o;
+    __builtin_memcpy(&o, &r, sizeof(o));
+    return o;
+}
+// The column run T[k0 .. k0+3][n0 + lane%16] of a row-major LDS tile (stride in elements).
+template <typename E>
+__device__ __forceinline__ v4<E> lds_col4(const E *tile, int stride, int k0, int n0, int lane) {
+    const int L = lane & 15;
+    if constexpr (sizeof(E) == 2) {
+        return lds_tr_raw<E>(tile + (k0 + (L >> 2)) * stride + n0 + 4 * (L & 3));
+    } else {
+        v4<E> o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = tile[(k0 + e) * stride + n0 + L];
+        return o;
+    }
+}
+template <typename E> __device__ __forceinline__ v8<E> cat8(const v4<E> &a, const v4<E> &b) {
+    v8<E> r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[e + 4] = b[e]; }
+    return r;
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -25,9 +25,8 @@ struct StateArgs {
     const float *w;
     long BH;
     int N, Nb, D, Lp;
-    void *vt;         // [BH][Nb][D][64] transposed V, in the input dtype
-    void *hs;         // [BH][Nb][Lp] per-block states (h'^T then z), scaled by 1/64
-    bool do_states, do_vt, bf16_in;
+    void *hs;         // [BH][Nbc][Lp] per-block states (h'^T then z), scaled by 1/64
+    bool bf16_in;
 };
 
 struct AssembleArgs {
@@ -40,7 +39,7 @@ struct AssembleArgs {
 };
 
 struct FusedArgs {
-    const void *q, *k, *vt;
+    const void *q, *k, *v;
     const int32_t *crit;
     int kc;
     const void *hhat;

@@ -64,7 +64,7 @@ sla_status check_shape(int B, int H, int N, int d, int block) {
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, E, mcount, hs, hhat, total;
+    size_t qp, kp, mask, crit, E, mcount, ulist, ucount, hs, hhat, total;
     int Nb, Nbc, Lp, kc, kn;
 };
 
@@ -84,6 +84,9 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.mask = take((size_t)BH * L.Nb * L.Nb);
     L.crit = take(sizeof(int32_t) * BH * L.Nb * (kc > 0 ? kc : 1));
     L.mcount = take(sizeof(int32_t) * BH * L.Nb);
+    const long Np = (L.Nb + 1) / 2;
+    L.ulist = take(sizeof(uint32_t) * BH * Np * 2 * (kc > 0 ? kc : 1));
+    L.ucount = take(sizeof(int32_t) * BH * Np);
     const bool states = kc + kn < L.Nb;
     L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
     L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // blocks interleaved by 8, padded to Nbc
@@ -193,6 +196,7 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
     a.qp = q_pool; a.kp = k_pool; a.BH = (long)B * H; a.Nb = Nb; a.D = d; a.kc = kc; a.kn = kn;
     a.mask = mask; a.crit = crit_idx; a.excl = excl_idx; a.pc = p_c;
     a.E = nullptr; a.Nbc = 0; a.mcount = nullptr; a.n_last = 64; a.e_is_f32 = false;
+    a.ulist = nullptr; a.ucount = nullptr;
     a.inv_sqrt_d = 1.0 / sqrt((double)d);
     return device_status(sla::launch_classify(a, (hipStream_t)stream), "classify launch");
 }
@@ -244,6 +248,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     ca.mask = mask; ca.crit = crit; ca.excl = nullptr; ca.pc = nullptr;
     ca.E = states ? (void *)(ws + L.E) : nullptr; ca.Nbc = L.Nbc;
     ca.mcount = mcount; ca.n_last = N - 64 * (Nb - 1); ca.e_is_f32 = f32;
+    ca.ulist = (uint32_t *)(ws + L.ulist); ca.ucount = (int32_t *)(ws + L.ucount);
     ca.inv_sqrt_d = 1.0 / sqrt((double)d);
     st = device_status(sla::launch_classify(ca, s), "classify launch");
     if (st != SLA_OK) return st;
@@ -266,7 +271,8 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     }
     mark_stage(ev, 4, s);
     sla::FusedArgs fa{};
-    fa.q = q; fa.k = k; fa.v = v; fa.crit = crit; fa.kc = kc;
+    fa.q = q; fa.k = k; fa.v = v; fa.ulist = (const uint32_t *)(ws + L.ulist);
+    fa.ucount = (const int32_t *)(ws + L.ucount); fa.kc = kc;
     fa.hhat = ws + L.hhat; fa.mcount = states ? mcount : nullptr; fa.Lp = L.Lp;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;

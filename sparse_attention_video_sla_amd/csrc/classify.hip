@@ -19,6 +19,10 @@
 //      ascending excluded list, optional P_c, and for the forward pass the
 //      0/1 exclusion row E (critical or negligible) used by the marginal-state
 //      GEMM and the number of marginal tokens of the row.
+//   4. For the forward pass, per pair of rows (2p, 2p+1): the ascending union
+//      of their critical lists, each entry j | in_row_2p << 16 | in_row_2p+1 << 17
+//      (32-bit, so that the fused kernel reads it with scalar loads), and its
+//      length.  The fused kernel streams a pair's union once.
 #include "sla_device.h"
 #include "sla_launch.h"
 
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, int Nb, int kc, int kn,
     int8_t *__restrict__ mask, int32_t *__restrict__ crit, int32_t *__restrict__ excl,
     float *__restrict__ pc, ES *__restrict__ E, int Nbc, int32_t *__restrict__ mcount, int n_last,
-    double inv_sqrt_d) {
+    uint32_t *__restrict__ ulist, int32_t *__restrict__ ucount, double inv_sqrt_d) {
     extern __shared__ double smem[];
     double *qd = smem;                                        // [R][D]
     double *sc = smem + R * D;                                // [R][Nb]
@@ -168,6 +172,27 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
             for (int j = lane; j < Nb; j += 64) pc[row * Nb + j] = (float)(exp((s[j] - m) * inv_sqrt_d) / z);
         }
     }
+    if (ulist == nullptr) return;
+    __syncthreads();
+    // union of the critical lists of each row pair (R is even, i0 is even)
+    const int Np = (Nb + 1) / 2;
+    for (int pr = wave; 2 * pr < nr; pr += CL_THREADS / 64) {
+        const long pair = bh * Np + (i0 / 2 + pr);
+        const int8_t *la = labs + (2 * pr) * Nb;
+        const int8_t *lb = (2 * pr + 1 < nr) ? labs + (2 * pr + 1) * Nb : nullptr;
+        int run = 0;
+        for (int e = 0; e < ne; ++e) {
+            const int j = lane + 64 * e;
+            const bool a = j < Nb && la[j] == 1;
+            const bool b = j < Nb && lb != nullptr && lb[j] == 1;
+            const uint64_t bu = __ballot(a || b);
+            const int pos = run + __popcll(bu & lt);
+            if ((a || b) && pos < 2 * kc)
+                ulist[pair * (2 * kc) + pos] = (uint32_t)j | (a ? 1u << 16 : 0u) | (b ? 1u << 17 : 0u);
+            run += __popcll(bu);
+        }
+        if (lane == 0) ucount[pair] = run;
+    }
 }
 
 template <typename ES, int D, int R>
@@ -179,7 +204,7 @@ static hipError_t launch_cls_r(const ClassifyArgs &a, hipStream_t st) {
     const long tiles = (a.Nb + R - 1) / R;
     const unsigned grid = (unsigned)(a.BH * tiles);
     kern<<<grid, CL_THREADS, lds, st>>>(a.qp, a.kp, a.Nb, a.kc, a.kn, a.mask, a.crit, a.excl, a.pc,
-                                        (ES *)a.E, a.Nbc, a.mcount, a.n_last, a.inv_sqrt_d);
+                                        (ES *)a.E, a.Nbc, a.mcount, a.n_last, a.ulist, a.ucount, a.inv_sqrt_d);
     return hipGetLastError();
 }
 
@@ -190,7 +215,7 @@ static hipError_t launch_cls_d(const ClassifyArgs &a, hipStream_t st) {
     case 8: return launch_cls_r<ES, D, 8>(a, st);
     case 4: return launch_cls_r<ES, D, 4>(a, st);
     case 2: return launch_cls_r<ES, D, 2>(a, st);
-    default: return launch_cls_r<ES, D, 1>(a, st);
+    default: return launch_cls_r<ES, D, 2>(a, st);
     }
 }
 
@@ -200,9 +225,9 @@ size_t classify_lds_bytes(int R, int D, int Nb) {
 
 int classify_rows_per_group(int Nb, int D) {
     const size_t limit = 160 * 1024;
-    for (int R = 8; R > 1; R >>= 1)
+    for (int R = 8; R > 2; R >>= 1)
         if (classify_lds_bytes(R, D, Nb) <= limit) return R;
-    return 1;
+    return 2;   // rows come in pairs; two rows fit for every supported Nb
 }
 
 hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st) {

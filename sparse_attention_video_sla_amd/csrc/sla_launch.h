@@ -16,6 +16,8 @@ struct ClassifyArgs {
     int Nbc;
     int32_t *mcount;  // nullable [BH][Nb] marginal token count per row
     int n_last;       // valid tokens of the last block
+    uint32_t *ulist;  // nullable [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
+    int32_t *ucount;  // [BH][ceil(Nb/2)] union lengths
     bool e_is_f32;
     double inv_sqrt_d;
 };
@@ -40,7 +42,8 @@ struct AssembleArgs {
 
 struct FusedArgs {
     const void *q, *k, *v;
-    const int32_t *crit;
+    const uint32_t *ulist;   // [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
+    const int32_t *ucount;   // [BH][ceil(Nb/2)]
     int kc;
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere

@@ -64,7 +64,7 @@ sla_status check_shape(int B, int H, int N, int d, int block) {
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, E, mcount, ulist, ucount, hs, hhat, total;
+    size_t qp, kp, mask, crit, E, mcount, ulist, ucount, wst, hs, hhat, total;
     int Nb, Nbc, Lp, kc, kn;
 };
 
@@ -89,6 +89,7 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.ucount = take(sizeof(int32_t) * BH * Np);
     const bool states = kc + kn < L.Nb;
     L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
+    L.wst = take(states ? es * d * d : 0);
     L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // blocks interleaved by 8, padded to Nbc
     L.hhat = take(states ? es * BH * L.Nb * L.Lp : 0);
     L.total = off;
@@ -257,7 +258,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     if (states) {
         sla::StateArgs sa{};
         sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp;
-        sa.hs = ws + L.hs; sa.bf16_in = !f32;
+        sa.hs = ws + L.hs; sa.wstate = ws + L.wst; sa.bf16_in = !f32;
         st = device_status(sla::launch_state(sa, s), "state launch");
         if (st != SLA_OK) return st;
     }

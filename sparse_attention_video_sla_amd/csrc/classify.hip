@@ -36,24 +36,28 @@ __device__ __forceinline__ uint64_t order_key(double s) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Key of block j for the search: the order key (inv = false) or its
-// complement (inv = true); 0 for lanes past the row end, which no candidate
-// (always >= 1) can reach.
-__device__ __forceinline__ uint64_t key_at(const double *s, int j, int Nb, bool inv) {
-    if (j >= Nb) return 0ull;
-    const uint64_t k = order_key(s[j]);
-    return inv ? ~k : k;
+// The keys of one row live in registers: lane l holds blocks j = l + 64e,
+// e < KM, as order-preserving 64-bit keys (0 past the row end, which no
+// candidate, always >= 1, can reach).  The inverted keys of the bottom search
+// are the complements of the valid ones.
+template <int KM> struct RowKeys { uint64_t k[KM]; };
+
+template <int KM>
+__device__ __forceinline__ uint64_t key_of(const RowKeys<KM> &rk, int e, int j, int Nb, bool inv) {
+    return (j >= Nb) ? 0ull : (inv ? ~rk.k[e] : rk.k[e]);
 }
 
 // Largest v with #{keys >= v} >= k (k >= 1); `exact` when that count is exactly k,
 // which lets the search stop as soon as the prefix separates k keys.
-__device__ uint64_t kth_largest(const double *s, int Nb, int ne, int lane, bool inv, int k, bool &exact) {
+template <int KM>
+__device__ uint64_t kth_largest(const RowKeys<KM> &rk, int Nb, int lane, bool inv, int k, bool &exact) {
     uint64_t lo = 0;
     exact = false;
     for (int bit = 63; bit >= 0; --bit) {
         const uint64_t cand = lo | (1ull << bit);
         int cnt = 0;
-        for (int e = 0; e < ne; ++e) cnt += __popcll(__ballot(key_at(s, lane + 64 * e, Nb, inv) >= cand));
+#pragma unroll
+        for (int e = 0; e < KM; ++e) cnt += __popcll(__ballot(key_of(rk, e, lane + 64 * e, Nb, inv) >= cand));
         if (cnt >= k) {
             lo = cand;
             if (cnt == k) { exact = true; break; }
@@ -64,22 +68,25 @@ __device__ uint64_t kth_largest(const double *s, int Nb, int ne, int lane, bool 
 
 // Label +1 (inv = false, sign = 1) or -1 (inv = true, sign = -1) for the k
 // blocks ranked first by (key desc, index asc) / (inverted key desc, index desc).
-__device__ void mark(const double *s, int8_t *lab, int Nb, int ne, int lane, bool inv, int k, int8_t sign) {
+template <int KM>
+__device__ void mark(const RowKeys<KM> &rk, int8_t *lab, int Nb, int lane, bool inv, int k, int8_t sign) {
     bool exact;
-    const uint64_t t = kth_largest(s, Nb, ne, lane, inv, k, exact);
+    const uint64_t t = kth_largest(rk, Nb, lane, inv, k, exact);
     int need = 0;
     if (!exact) {
         int g = 0;
-        for (int e = 0; e < ne; ++e) g += __popcll(__ballot(key_at(s, lane + 64 * e, Nb, inv) > t));
+#pragma unroll
+        for (int e = 0; e < KM; ++e) g += __popcll(__ballot(key_of(rk, e, lane + 64 * e, Nb, inv) > t));
         need = k - g;
     }
     const uint64_t lt = (1ull << lane) - 1ull;
     const uint64_t gt = (lane == 63) ? 0ull : (~0ull << (lane + 1));
     int run = 0;
-    for (int x = 0; x < ne; ++x) {
-        const int e = inv ? ne - 1 - x : x;      // ties: ascending index for +1, descending for -1
+#pragma unroll
+    for (int x = 0; x < KM; ++x) {
+        const int e = inv ? KM - 1 - x : x;      // ties: ascending index for +1, descending for -1
         const int j = lane + 64 * e;
-        const uint64_t key = key_at(s, j, Nb, inv);
+        const uint64_t key = key_of(rk, e, j, Nb, inv);
         bool on = exact ? key >= t : key > t;
         const uint64_t tie = __ballot(!exact && key == t);
         if (!exact && key == t) on = run + __popcll(tie & (inv ? gt : lt)) < need;
@@ -88,7 +95,7 @@ __device__ void mark(const double *s, int8_t *lab, int Nb, int ne, int lane, boo
     }
 }
 
-template <typename ES, int D, int R>
+template <typename ES, int D, int R, int KM>
 __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, int Nb, int kc, int kn,
     int8_t *__restrict__ mask, int32_t *__restrict__ crit, int32_t *__restrict__ excl,
@@ -137,8 +144,14 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
         const long row = bh * Nb + i0 + r;
         const double *s = sc + r * Nb;
         int8_t *lab = labs + r * Nb;
-        if (kc > 0) mark(s, lab, Nb, ne, lane, false, kc, 1);
-        if (kn > 0) mark(s, lab, Nb, ne, lane, true, kn, -1);
+        RowKeys<KM> rk;
+#pragma unroll
+        for (int e = 0; e < KM; ++e) {
+            const int j = lane + 64 * e;
+            rk.k[e] = (j < Nb) ? order_key(s[j]) : 0ull;
+        }
+        if (kc > 0) mark(rk, lab, Nb, lane, false, kc, 1);
+        if (kn > 0) mark(rk, lab, Nb, lane, true, kn, -1);
         int run_c = 0, run_x = 0, n_marg = 0;
         bool last_marg = false;
         for (int e = 0; e < ne; ++e) {
@@ -195,10 +208,10 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
     }
 }
 
-template <typename ES, int D, int R>
-static hipError_t launch_cls_r(const ClassifyArgs &a, hipStream_t st) {
+template <typename ES, int D, int R, int KM>
+static hipError_t launch_cls_k(const ClassifyArgs &a, hipStream_t st) {
     const size_t lds = classify_lds_bytes(R, D, a.Nb);
-    auto kern = classify_kernel<ES, D, R>;
+    auto kern = classify_kernel<ES, D, R, KM>;
     hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     const long tiles = (a.Nb + R - 1) / R;
@@ -206,6 +219,17 @@ static hipError_t launch_cls_r(const ClassifyArgs &a, hipStream_t st) {
     kern<<<grid, CL_THREADS, lds, st>>>(a.qp, a.kp, a.Nb, a.kc, a.kn, a.mask, a.crit, a.excl, a.pc,
                                         (ES *)a.E, a.Nbc, a.mcount, a.n_last, a.ulist, a.ucount, a.inv_sqrt_d);
     return hipGetLastError();
+}
+
+// keys per lane: ceil(Nb / 64) rounded up to 8, 16, 24, 32 or 38 registers pairs
+template <typename ES, int D, int R>
+static hipError_t launch_cls_r(const ClassifyArgs &a, hipStream_t st) {
+    const int ne = (a.Nb + 63) / 64;
+    if (ne <= 8) return launch_cls_k<ES, D, R, 8>(a, st);
+    if (ne <= 16) return launch_cls_k<ES, D, R, 16>(a, st);
+    if (ne <= 24) return launch_cls_k<ES, D, R, 24>(a, st);
+    if (ne <= 32) return launch_cls_k<ES, D, R, 32>(a, st);
+    return launch_cls_k<ES, D, R, 38>(a, st);
 }
 
 template <typename ES, int D>

@@ -28,6 +28,7 @@ struct StateArgs {
     long BH;
     int N, Nb, D, Lp;
     void *hs;         // [BH][Nbc][Lp] per-block states (h'^T then z), scaled by 1/64
+    void *wstate;     // [d][d] W converted to the state type (scratch)
     bool bf16_in;
 };
 

@@ -20,9 +20,16 @@
 
 namespace sla {
 
+// W in the state type, once per call (d x d)
+template <typename S>
+__global__ __launch_bounds__(256) void w_to_state_kernel(const float *__restrict__ w, S *__restrict__ ws, int n) {
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    if (x < n) ws[x] = from_f32<S>(w[x]);
+}
+
 template <typename T, typename S, int D>
 __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, const T *__restrict__ v,
-                                                      const float *__restrict__ w, int N, int Nb, int Nbc,
+                                                      const S *__restrict__ w, int N, int Nb, int Nbc,
                                                       S *__restrict__ hs, int Lp) {
     constexpr int NT = 2 * D;
     constexpr int EPC = 16 / sizeof(T);      // input elements per 16-byte chunk
@@ -30,9 +37,9 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
     constexpr int NCH = 64 * CPR / NT;       // chunks per thread
     constexpr int SE = 16 / sizeof(S);
     constexpr int SSTR = D + SE;             // V row stride in LDS (state type)
-    constexpr int PSTR = 64 + SE;            // phi^T row stride in LDS
-    __shared__ S Vs[64 * SSTR];
-    __shared__ S Pt[D * PSTR];
+    constexpr int PSTR = D + (sizeof(S) == 2 ? 16 : 4);   // phi row stride: 8 dwords mod 64 for transposing reads
+    __shared__ __attribute__((aligned(16))) S Vs[64 * SSTR];
+    __shared__ __attribute__((aligned(16))) S Ph[64 * PSTR];
 
     const long blk = blockIdx.x;             // bh * Nbc + j
     const int j = (int)(blk % Nbc);
@@ -57,7 +64,9 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
         vc[u] = ok ? ld_chunk(vb + (long)row * D + cc * EPC) : zero_chunk();
     }
 
-    // phi(K) per token row: the CPR threads of a row are CPR consecutive lanes
+    // phi(K) per token row: the CPR threads of a row are CPR consecutive lanes.
+    // phi and V go to LDS row-major in the state type.
+    constexpr float LOG2E = 1.4426950408889634f;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
         const int ch = tid + NT * u, row = ch / CPR, cc = ch % CPR;
@@ -70,16 +79,19 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
         for (int off = 1; off < CPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) { xf[e] = expf(xf[e] - mx); sum += xf[e]; }
+        for (int e = 0; e < EPC; ++e) { xf[e] = fast_exp2((xf[e] - mx) * LOG2E); sum += xf[e]; }
 #pragma unroll
         for (int off = 1; off < CPR; off <<= 1) sum += __shfl_xor(sum, off, 64);
         const float inv = (row < n) ? 1.f / sum : 0.f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) Pt[(cc * EPC + e) * PSTR + row] = from_f32<S>(xf[e] * inv);
-        // V in the state type, row-major
+        S ph[EPC], vv[EPC];
         const T *y = reinterpret_cast<const T *>(&vc[u]);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) Vs[row * SSTR + cc * EPC + e] = from_f32<S>(to_f32<T>(y[e]));
+        for (int e = 0; e < EPC; ++e) {
+            ph[e] = from_f32<S>(xf[e] * inv);
+            vv[e] = from_f32<S>(to_f32<T>(y[e]));
+        }
+        __builtin_memcpy(&Ph[row * PSTR + cc * EPC], ph, sizeof(ph));
+        __builtin_memcpy(&Vs[row * SSTR + cc * EPC], vv, sizeof(vv));
     }
     __syncthreads();
 
@@ -91,7 +103,7 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
         for (int r = 0; r < 16; ++r) accv[mt][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        const v8<S> bw = cvt8<S>(ld8<float>(w + (long)(32 * wave + l32) * D + 16 * s + 8 * hh));
+        const v8<S> bw = ld8<S>(w + (long)(32 * wave + l32) * D + 16 * s + 8 * hh);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const v8<S> a = ld8<S>(&Vs[(32 * mt + l32) * SSTR + 16 * s + 8 * hh]);
@@ -100,7 +112,9 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
     }
     // h'[a][c] = sum_t phi[t][a] V'[t][c]: M = a, N = c (this wave's tile), K = t.
     // V' is the B operand straight from its accumulator, so t runs in the
-    // accumulator's permuted order and phi^T is read with the same order.
+    // accumulator's permuted order; the phi^T operand takes the same t runs as
+    // columns of the row-major phi tile (transposing reads).
+    const int grp = lane >> 4;
     f32x16 acch[D / 32];
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
@@ -111,10 +125,11 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
         v8<S> b;
 #pragma unroll
         for (int e = 0; e < 8; ++e) b[e] = from_f32<S>(accv[s >> 1][8 * (s & 1) + e]);
+        const int k0 = 16 * s + 4 * (grp >> 1);
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-            const S *p = &Pt[(32 * mt + l32) * PSTR + 16 * s + 4 * hh];
-            mma16(acch[mt], ld4x2<S>(p, p + 8), b);
+            const int n0 = 32 * mt + 16 * (grp & 1);
+            mma16(acch[mt], cat8<S>(lds_col4<S>(Ph, PSTR, k0, n0, lane), lds_col4<S>(Ph, PSTR, k0 + 8, n0, lane)), b);
         }
     }
 
@@ -133,7 +148,7 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
         }
     if (tid < D) {
         float z = 0.f;
-        for (int t = 0; t < 64; ++t) z += to_f32<S>(Pt[tid * PSTR + t]);
+        for (int t = 0; t < 64; ++t) z += to_f32<S>(Ph[t * PSTR + tid]);
         hsb[D * D + tid] = from_f32<S>(z * scale);
     }
     for (int x = D * D + D + tid; x < Lp; x += NT) hsb[x] = from_f32<S>(0.f);
@@ -142,9 +157,12 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
 template <typename T, typename S, int D>
 static hipError_t launch_state_t(const StateArgs &a, hipStream_t st) {
     const int Nbc = (a.Nb + 31) / 32 * 32;
+    w_to_state_kernel<S><<<(D * D + 255) / 256, 256, 0, st>>>(a.w, (S *)a.wstate, D * D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(a.BH * Nbc);
-    state_kernel<T, S, D><<<grid, 2 * D, 0, st>>>((const T *)a.k, (const T *)a.v, a.w, a.N, a.Nb, Nbc,
-                                                  (S *)a.hs, a.Lp);
+    state_kernel<T, S, D><<<grid, 2 * D, 0, st>>>((const T *)a.k, (const T *)a.v, (const S *)a.wstate, a.N,
+                                                  a.Nb, Nbc, (S *)a.hs, a.Lp);
     return hipGetLastError();
 }
 

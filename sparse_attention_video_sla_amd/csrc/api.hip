@@ -64,7 +64,7 @@ sla_status check_shape(int B, int H, int N, int d, int block) {
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, E, mcount, ulist, ucount, wst, hs, hhat, total;
+    size_t qp, kp, mask, crit, E, mcount, ulist, ucount, slots, wst, hs, hhat, total;
     int Nb, Nbc, Lp, kc, kn;
 };
 
@@ -85,12 +85,14 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.crit = take(sizeof(int32_t) * BH * L.Nb * (kc > 0 ? kc : 1));
     L.mcount = take(sizeof(int32_t) * BH * L.Nb);
     const long Np = (L.Nb + 1) / 2;
-    L.ulist = take(sizeof(uint32_t) * BH * Np * 2 * (kc > 0 ? kc : 1));
-    L.ucount = take(sizeof(int32_t) * BH * Np);
+    // float inputs: union of each row pair's critical lists; 16-bit inputs: slot schedule
+    L.ulist = take(f32 ? sizeof(uint32_t) * BH * Np * 2 * (kc > 0 ? kc : 1) : 0);
+    L.ucount = take(f32 ? sizeof(int32_t) * BH * Np : 0);
+    L.slots = take(f32 ? 0 : sizeof(uint32_t) * BH * Np * (kc > 0 ? kc : 1));
     const bool states = kc + kn < L.Nb;
     L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
     L.wst = take(states ? es * d * d : 0);
-    L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // blocks interleaved by 8, padded to Nbc
+    L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // one row per key block, padded to Nbc rows
     L.hhat = take(states ? es * BH * L.Nb * L.Lp : 0);
     L.total = off;
     return L;
@@ -197,7 +199,7 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
     a.qp = q_pool; a.kp = k_pool; a.BH = (long)B * H; a.Nb = Nb; a.D = d; a.kc = kc; a.kn = kn;
     a.mask = mask; a.crit = crit_idx; a.excl = excl_idx; a.pc = p_c;
     a.E = nullptr; a.Nbc = 0; a.mcount = nullptr; a.n_last = 64; a.e_is_f32 = false;
-    a.ulist = nullptr; a.ucount = nullptr;
+    a.ulist = nullptr; a.ucount = nullptr; a.slots = nullptr;
     a.inv_sqrt_d = 1.0 / sqrt((double)d);
     return device_status(sla::launch_classify(a, (hipStream_t)stream), "classify launch");
 }
@@ -249,7 +251,9 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     ca.mask = mask; ca.crit = crit; ca.excl = nullptr; ca.pc = nullptr;
     ca.E = states ? (void *)(ws + L.E) : nullptr; ca.Nbc = L.Nbc;
     ca.mcount = mcount; ca.n_last = N - 64 * (Nb - 1); ca.e_is_f32 = f32;
-    ca.ulist = (uint32_t *)(ws + L.ulist); ca.ucount = (int32_t *)(ws + L.ucount);
+    ca.ulist = f32 ? (uint32_t *)(ws + L.ulist) : nullptr;
+    ca.ucount = f32 ? (int32_t *)(ws + L.ucount) : nullptr;
+    ca.slots = f32 ? nullptr : (uint32_t *)(ws + L.slots);
     ca.inv_sqrt_d = 1.0 / sqrt((double)d);
     st = device_status(sla::launch_classify(ca, s), "classify launch");
     if (st != SLA_OK) return st;
@@ -273,11 +277,11 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     mark_stage(ev, 4, s);
     sla::FusedArgs fa{};
     fa.q = q; fa.k = k; fa.v = v; fa.ulist = (const uint32_t *)(ws + L.ulist);
-    fa.ucount = (const int32_t *)(ws + L.ucount); fa.kc = kc;
+    fa.ucount = (const int32_t *)(ws + L.ucount); fa.slots = (const uint32_t *)(ws + L.slots); fa.kc = kc;
     fa.hhat = ws + L.hhat; fa.mcount = states ? mcount : nullptr; fa.Lp = L.Lp;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;
-    st = device_status(sla::launch_fused(fa, s), "fused launch");
+    st = device_status(f32 ? sla::launch_fused(fa, s) : sla::launch_fused16(fa, s), "fused launch");
     mark_stage(ev, 5, s);
     return st;
 }

@@ -1,4 +1,4 @@
-// fused.hip -- one kernel for the three branches of SLA (SLA article,
+// fused.hip -- float inputs: one kernel for the three branches of SLA (SLA article,
 // section 3: exact sparse FlashAttention over the critical blocks, linear
 // attention over the marginal ones, negligible ones skipped, all in one GPU
 // kernel, with the learnable projection on the linear output).
@@ -293,11 +293,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
-    if (a.bf16_in) {
-        if (a.bf16_out)
-            return a.D == 64 ? launch_fused_t<bf16, f16, 64, bf16>(a, st) : launch_fused_t<bf16, f16, 128, bf16>(a, st);
-        return a.D == 64 ? launch_fused_t<bf16, f16, 64, float>(a, st) : launch_fused_t<bf16, f16, 128, float>(a, st);
-    }
+    if (a.bf16_in) return hipErrorInvalidValue;           // 16-bit inputs run fused16_kernel
     return a.D == 64 ? launch_fused_t<float, float, 64, float>(a, st) : launch_fused_t<float, float, 128, float>(a, st);
 }
 

@@ -18,6 +18,7 @@ struct ClassifyArgs {
     int n_last;       // valid tokens of the last block
     uint32_t *ulist;  // nullable [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
     int32_t *ucount;  // [BH][ceil(Nb/2)] union lengths
+    uint32_t *slots;  // nullable [BH][ceil(Nb/2)][kc] slot schedule of each row pair (16-bit path)
     bool e_is_f32;
     double inv_sqrt_d;
 };
@@ -45,6 +46,7 @@ struct FusedArgs {
     const void *q, *k, *v;
     const uint32_t *ulist;   // [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
     const int32_t *ucount;   // [BH][ceil(Nb/2)]
+    const uint32_t *slots;   // [BH][ceil(Nb/2)][kc] slot schedule (16-bit inputs)
     int kc;
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere
@@ -62,6 +64,7 @@ size_t classify_lds_bytes(int R, int D, int Nb);
 hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st);
 hipError_t launch_state(const StateArgs &a, hipStream_t st);
 hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st);
-hipError_t launch_fused(const FusedArgs &a, hipStream_t st);
+hipError_t launch_fused(const FusedArgs &a, hipStream_t st);     // float inputs
+hipError_t launch_fused16(const FusedArgs &a, hipStream_t st);   // bf16 inputs
 
 }  // namespace sla

@@ -134,6 +134,12 @@ SMALL = [
     (1, 1, 4096, 128, "f32", 0.05, 0.10),
     (1, 3, 70, 128, "bf16", 0.5, 0.0),
     (1, 1, 5000, 128, "bf16", 0.0, 0.5),
+    # odd Nb: the last pair of query blocks has no second block
+    (1, 2, 3000, 128, "bf16", 0.1, 0.1),
+    # last block of exactly 32 tokens: keys 32..63 of that tile are all past N
+    (1, 1, 2080, 128, "bf16", 0.05, 0.1),
+    (2, 2, 1100, 64, "bf16", 0.3, 0.2),
+    (1, 1, 1050, 128, "bf16", 1.0, 0.0),
 ]
 
 

@@ -12,7 +12,9 @@ counting the method's work F = 4*64*64*d per critical block pair +
 kernel, timed live with HIP events recorded on its stream; its algorithmic
 flops are the critical pairs plus 2*64*d*d per query block (phi(Q) times the
 marginal state; the projection is folded into the state kernel).
-`cpu_baseline` times the CPU oracle on a bounded sample (whole heads).
+`roofline.traffic` is the kernel's HBM bytes per launch from the committed
+rocprofv3 counter summary, reported only while the kernel source matches.
+`cpu_baseline` times the CPU oracle on whole heads (by default all of them).
 """
 import argparse
 import ctypes
@@ -26,6 +28,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFMA peak"
+FUSED_SRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc", "fused16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -37,6 +41,24 @@ def work(B, H, N, d, kc, kn):
     f_comp = 4 * 64 * 64 * d * pairs + 4 * 64 * d * d * marg_rows
     f_fused = 4 * 64 * 64 * d * pairs + 2 * 64 * d * d * marg_rows
     return f_comp, f_fused, pairs, marg_rows
+
+
+def fused_traffic():
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when the kernel source has changed since the
+    counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = open(FUSED_SRC, "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"fused16_kernel HBM bytes per launch: (\d+) \(source sha256 ([0-9a-f]{16})\)", text)
+    if not m or hashlib.sha256(src).hexdigest()[:16] != m.group(2):
+        return None
+    return int(m.group(1))
 
 
 def cpu_baseline(inp, wl, rc, rn, heads):
@@ -62,7 +84,7 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="named workload id (1 = Wan2.1 480p)")
     ap.add_argument("--crit", type=float, default=None)
     ap.add_argument("--negl", type=float, default=None)
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -147,13 +169,13 @@ def main():
                    "crit_frac": rc, "negl_frac": rn, "k_c": kc, "k_n": kn, "parallelism": "none (1 GPU)"},
         "mfma_frac_fused": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fused_kernel<bf16,f16,128,float>",
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(),
+                     "kernel": "fused16_kernel<bf16,f16,128,float>",
                      "flops_per_launch": f_fused, "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": stages,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(inp, wl, rc, rn, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(inp, wl, rc, rn, args.cpu_heads or wl.H)
     print(json.dumps(line), flush=True)
 
 

@@ -72,10 +72,15 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float
     __builtin_memcpy(p, &v, sizeof(v));
 }
 
-// Workgroup barrier that waits for this wave's LDS traffic only: global
-// loads issued before it stay in flight.  The memory clobber keeps the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barrier that waits for this wave's LDS (and scalar) traffic
+// only: global loads issued before it stay in flight.  The wait goes through
+// the builtin so that the compiler's own wait placement knows about it; the
+// memory clobber keeps the compiler from moving memory accesses across the
+// barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
 
 // maximum that propagates NaN instead of quieting it (v_maximum3_f32 on
 // gfx950): it takes MFMA results without canonicalising them first
@@ -199,14 +204,21 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
     const int vbase = ((8 * kh + (grp >> 1)) * 8 * D + ((2 * (grp & 1) + ((L & 3) >> 1)) * 4 + (L >> 2)) * 16 +
                        (L & 1) * 8) / 2;
     // loads into LDS by the kh = 0 waves: 1 KB block w4 * NB1 + u of a tile, lane at 16 * lane
-    uint32_t dvk[NB1], dvv[NB1];
+    // This wave loads K (kh = 1) or V (kh = 0): its buffer resource and, per
+    // block, the source offset of its lane, chosen once here so that the
+    // loop's loads carry no per-tensor selects.
+    const __amdgpu_buffer_rsrc_t rmy = kh == 1 ? rk : rv;
+    uint32_t dvm[NB1];
 #pragma unroll
     for (int u = 0; u < NB1; ++u) {
         const int byte = (w4 * NB1 + u) * 1024 + 16 * lane;
-        const int rk_ = byte / (2 * D), pk = (byte % (2 * D)) / 16;
-        dvk[u] = (uint32_t)(rk_ * 2 * D + (pk ^ kswz<D>(rk_)) * 16);
-        const int g = byte / (8 * D), qv = (byte % (8 * D)) / 16;
-        dvv[u] = (uint32_t)((4 * g + (qv & 3)) * 2 * D + (qv >> 2) * 16);
+        if (kh == 1) {
+            const int rk_ = byte / (2 * D), pk = (byte % (2 * D)) / 16;
+            dvm[u] = (uint32_t)(rk_ * 2 * D + (pk ^ kswz<D>(rk_)) * 16);
+        } else {
+            const int g = byte / (8 * D), qv = (byte % (8 * D)) / 16;
+            dvm[u] = (uint32_t)((4 * g + (qv & 3)) * 2 * D + (qv >> 2) * 16);
+        }
     }
 
     f32x16 sacc;
@@ -259,15 +271,10 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
         const uint32_t sb = (uint32_t)(64L * tile_b(e) * D * sizeof(T));
         const bool two = !single(e);
 #pragma unroll
-        for (int u = 0; u < NB1; ++u) {
-            const int blk = w4 * NB1 + u;
-            if (kh == 1) {
-                dma16(rk, dst + blk * 512, dvk[u], sa);
-                if (two) dma16(rk, dst + TILE + blk * 512, dvk[u], sb);
-            } else {
-                dma16(rv, dst + blk * 512, dvv[u], sa);
-                if (two) dma16(rv, dst + TILE + blk * 512, dvv[u], sb);
-            }
+        for (int u = 0; u < NB1; ++u) dma16(rmy, dst + (w4 * NB1 + u) * 512, dvm[u], sa);
+        if (two) {
+#pragma unroll
+            for (int u = 0; u < NB1; ++u) dma16(rmy, dst + TILE + (w4 * NB1 + u) * 512, dvm[u], sb);
         }
     };
     auto softmax = [&](uint32_t e1) {

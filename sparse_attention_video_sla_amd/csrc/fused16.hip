@@ -133,7 +133,13 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
     constexpr int NCT = D / 32;                          // 32-channel tiles of O
     constexpr int NCH = NCT / 2;                         // channel tiles each wave finishes
     constexpr float NEG_INF = -__builtin_inff();
-    constexpr float TAU = 8.f;                           // lazy rescale: P may reach 2^TAU before O is rescaled
+    // Lazy rescale: the running max moves only when a tile exceeds it by TAU
+    // (log2 units), so P may reach 2^TAU.  P is bf16 (the float exponent
+    // range) and O and the row sums accumulate in fp32 over at most 64 * Nb
+    // < 2^18 keys, so with TAU = 64 every value stays below 2^90: the rescale
+    // (80 multiplies per wave) runs about once per row instead of on every
+    // tile that raises the max.
+    constexpr float TAU = 64.f;
     // rings: [tile A][tile B] per slot
     __shared__ __attribute__((aligned(1024))) T Kb0[2 * TILE];
     __shared__ __attribute__((aligned(1024))) T Kb1[2 * TILE];

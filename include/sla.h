@@ -35,9 +35,13 @@
  *     gives a thread-local message for the last non-OK status of the thread.
  *   - Inputs must be finite.  BF16 inputs: the linear branch stages values in
  *     fp16, so |V| and |V W^T| must stay below 65504.
- *   - Reentrant; the only mutable state is per thread (the error message and
- *     the optional stage-timing events).  Results are deterministic run to run
- *     (no atomics).
+ *   - Reentrant.  Mutable state: per thread, the error message and the
+ *     optional stage-timing events; per device, one side stream (default
+ *     priority) and two events, created on first use and kept until the
+ *     process ends.  sla_forward runs its block-state kernel on that side
+ *     stream, forked from and joined back to the caller's stream, so all of
+ *     its work is still ordered on the caller's stream.  Results are
+ *     deterministic run to run (no atomics).
  */
 #ifndef SLA_H
 #define SLA_H
@@ -113,9 +117,11 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Stage timing, for profiling.  While enabled on a thread, every sla_forward
- * call of that thread records HIP events on its stream around each of its
- * kernels: 0 pool, 1 classify, 2 state, 3 assemble, 4 fused (a stage that
- * does not run records zero time).  sla_stage_times waits for the recorded
+ * call of that thread records HIP events around each of its kernels, on the
+ * stream the kernel runs on: 0 pool, 1 classify, 2 state, 3 assemble, 4 fused
+ * (a stage that does not run records zero time).  The state stage runs
+ * concurrently with pool and classify, so stage times do not add up to the
+ * time of a call.  sla_stage_times waits for the recorded
  * events, writes the summed milliseconds per stage to ms[0..4] and the number
  * of calls summed to *calls, and forgets them.  Events are created on first
  * use and kept per thread.  Disabled by default. */

@@ -1,14 +1,17 @@
 // api.hip -- the extern "C" entry points of libsla (declared in include/sla.h).
 //
 // Host-side only: argument checks, per-row counts, workspace carving and the
-// launch sequence pool -> classify -> state -> assemble -> fused, all on the
-// caller's stream with no synchronisation.
+// launch sequence.  pool -> classify run on the caller's stream while the
+// block-state kernel, which needs only K, V and W, runs on a side stream of
+// the device; the caller's stream then waits for it and runs assemble ->
+// fused.  No host synchronisation.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <array>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -64,19 +67,20 @@ sla_status check_shape(int B, int H, int N, int d, int block) {
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, E, mcount, ulist, ucount, slots, wst, hs, hhat, total;
-    int Nb, Nbc, Lp, kc, kn;
+    size_t qp, kp, mask, crit, marg, mbits, mcount, ulist, ucount, slots, wst, hs, hhat, total;
+    int Nb, Nbc, Nbp, Lp, kc, kn;
 };
 
 Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     Layout L;
     const long BH = (long)B * H;
     L.Nb = (N + 63) / 64;
-    L.Nbc = (int)round_up(L.Nb, 32);
+    L.Nbc = (int)round_up(L.Nb, 64);
+    L.Nbp = (int)round_up(L.Nb, 512);
     L.Lp = (int)round_up((long)d * d + d, 256);
     L.kc = kc;
     L.kn = kn;
-    const size_t es = f32 ? 4 : 2;   // state / exclusion element size
+    const size_t es = f32 ? 4 : 2;   // state element size
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     L.qp = take(sizeof(float) * BH * L.Nb * d);
@@ -90,7 +94,9 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.ucount = take(f32 ? sizeof(int32_t) * BH * Np : 0);
     L.slots = take(f32 ? 0 : sizeof(uint32_t) * BH * Np * (kc > 0 ? kc : 1));
     const bool states = kc + kn < L.Nb;
-    L.E = take(states ? es * BH * L.Nb * L.Nbc : 0);
+    // marginal indicator: float rows for float inputs, bits for 16-bit inputs
+    L.marg = take(states && f32 ? sizeof(float) * BH * L.Nb * L.Nbc : 0);
+    L.mbits = take(states && !f32 ? sizeof(uint32_t) * BH * (L.Nbc / 32) * L.Nbp : 0);
     L.wst = take(states ? es * d * d : 0);
     L.hs = take(states ? es * BH * L.Nbc * L.Lp : 0);     // one row per key block, padded to Nbc rows
     L.hhat = take(states ? es * BH * L.Nb * L.Lp : 0);
@@ -98,12 +104,14 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     return L;
 }
 
-// Per-thread stage timing (sla_set_stage_timing / sla_stage_times).
+// Per-thread stage timing (sla_set_stage_timing / sla_stage_times): a start
+// and an end event per stage, recorded on the stream the stage runs on.
+typedef std::array<hipEvent_t, 2 * SLA_NUM_STAGES> StageEvents;
 struct StageTimer {
     bool on = false;
     std::vector<hipEvent_t> pool;      // created events, reused
     size_t used = 0;
-    std::vector<std::array<hipEvent_t, SLA_NUM_STAGES + 1>> calls;
+    std::vector<StageEvents> calls;
 
     hipEvent_t next() {
         if (used == pool.size()) {
@@ -116,9 +124,41 @@ struct StageTimer {
 };
 thread_local StageTimer g_timer;
 
-// Records the boundary `b` (0..SLA_NUM_STAGES) of the current call.
-void mark_stage(std::array<hipEvent_t, SLA_NUM_STAGES + 1> *ev, int b, hipStream_t s) {
-    if (ev && (*ev)[b]) hipEventRecord((*ev)[b], s);
+// Records the start (end = 0) or the end (end = 1) of stage `i` of the current call.
+void mark_stage(StageEvents *ev, int i, int end, hipStream_t s) {
+    if (ev && (*ev)[2 * i + end]) hipEventRecord((*ev)[2 * i + end], s);
+}
+
+// The side stream of a device (default priority, non-blocking) and the two
+// events that fork it from and join it to the caller's stream.  Created on
+// first use and kept until the process ends.  The fork is recorded and waited
+// under the lock, so that a caller's side work never waits on another
+// caller's stream; the join may be re-recorded by a later caller, which only
+// makes a wait cover more of the side stream.
+struct SideStream {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int MAX_DEVICES = 64;
+SideStream g_side[MAX_DEVICES];
+
+hipError_t side_stream(SideStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    std::lock_guard<std::mutex> lock(ss.mu);
+    if (!ss.ready) {
+        if ((e = hipStreamCreateWithFlags(&ss.side, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+        ss.ready = true;
+    }
+    *out = &ss;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -135,11 +175,11 @@ sla_status sla_stage_times(float *ms, int *calls) {
     for (int i = 0; i < SLA_NUM_STAGES; ++i) ms[i] = 0.f;
     *calls = (int)g_timer.calls.size();
     for (auto &ev : g_timer.calls) {
-        hipError_t e = hipEventSynchronize(ev[SLA_NUM_STAGES]);
-        if (e != hipSuccess) return device_status(e, "stage timing");
         for (int i = 0; i < SLA_NUM_STAGES; ++i) {
+            hipError_t e = hipEventSynchronize(ev[2 * i + 1]);
+            if (e != hipSuccess) return device_status(e, "stage timing");
             float t = 0.f;
-            e = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+            e = hipEventElapsedTime(&t, ev[2 * i], ev[2 * i + 1]);
             if (e != hipSuccess) return device_status(e, "stage timing");
             ms[i] += t;
         }
@@ -198,7 +238,7 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
     sla::ClassifyArgs a{};
     a.qp = q_pool; a.kp = k_pool; a.BH = (long)B * H; a.Nb = Nb; a.D = d; a.kc = kc; a.kn = kn;
     a.mask = mask; a.crit = crit_idx; a.excl = excl_idx; a.pc = p_c;
-    a.E = nullptr; a.Nbc = 0; a.mcount = nullptr; a.n_last = 64; a.e_is_f32 = false;
+    a.marg = nullptr; a.mbits = nullptr; a.Nbc = 0; a.Nbp = 0; a.mcount = nullptr; a.n_last = 64;
     a.ulist = nullptr; a.ucount = nullptr; a.slots = nullptr;
     a.inv_sqrt_d = 1.0 / sqrt((double)d);
     return device_status(sla::launch_classify(a, (hipStream_t)stream), "classify launch");
@@ -234,47 +274,77 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     int32_t *crit = (int32_t *)(ws + L.crit);
     int32_t *mcount = (int32_t *)(ws + L.mcount);
 
-    std::array<hipEvent_t, SLA_NUM_STAGES + 1> *ev = nullptr;
+    StageEvents *ev = nullptr;
     if (g_timer.on) {
-        std::array<hipEvent_t, SLA_NUM_STAGES + 1> set;
+        StageEvents set;
         for (auto &e : set) e = g_timer.next();
         g_timer.calls.push_back(set);
         ev = &g_timer.calls.back();
     }
-    mark_stage(ev, 0, s);
+    // block states on the side stream, concurrent with pool and classify; a
+    // return after the fork still makes the caller's stream wait for the join
+    SideStream *ss = nullptr;
+    struct JoinOnExit {
+        hipStream_t s;
+        SideStream *ss = nullptr;
+        ~JoinOnExit() { if (ss) hipStreamWaitEvent(s, ss->join, 0); }
+    } guard{s};
+    if (states) {
+        st = device_status(side_stream(&ss), "side stream");
+        if (st != SLA_OK) return st;
+        std::lock_guard<std::mutex> lock(ss->mu);
+        st = device_status(hipEventRecord(ss->fork, s), "fork");
+        if (st == SLA_OK) st = device_status(hipStreamWaitEvent(ss->side, ss->fork, 0), "fork");
+        if (st != SLA_OK) return st;
+        sla::StateArgs sa{};
+        sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp; sa.Nbc = L.Nbc;
+        sa.hs = ws + L.hs; sa.wstate = ws + L.wst; sa.bf16_in = !f32;
+        mark_stage(ev, 2, 0, ss->side);
+        st = device_status(sla::launch_state(sa, ss->side), "state launch");
+        mark_stage(ev, 2, 1, ss->side);
+        if (st == SLA_OK) st = device_status(hipEventRecord(ss->join, ss->side), "join");
+        if (st != SLA_OK) return st;
+        guard.ss = ss;
+    } else {
+        mark_stage(ev, 2, 0, s);
+        mark_stage(ev, 2, 1, s);
+    }
+    mark_stage(ev, 0, 0, s);
     st = device_status(sla::launch_pool(!f32, d, q, k, qp, kp, BH, N, Nb, 64, s), "pool launch");
     if (st != SLA_OK) return st;
-    mark_stage(ev, 1, s);
+    mark_stage(ev, 0, 1, s);
 
     sla::ClassifyArgs ca{};
     ca.qp = qp; ca.kp = kp; ca.BH = BH; ca.Nb = Nb; ca.D = d; ca.kc = kc; ca.kn = kn;
     ca.mask = mask; ca.crit = crit; ca.excl = nullptr; ca.pc = nullptr;
-    ca.E = states ? (void *)(ws + L.E) : nullptr; ca.Nbc = L.Nbc;
-    ca.mcount = mcount; ca.n_last = N - 64 * (Nb - 1); ca.e_is_f32 = f32;
+    ca.marg = states && f32 ? (float *)(ws + L.marg) : nullptr;
+    ca.mbits = states && !f32 ? (uint32_t *)(ws + L.mbits) : nullptr;
+    ca.Nbc = L.Nbc; ca.Nbp = L.Nbp;
+    ca.mcount = mcount; ca.n_last = N - 64 * (Nb - 1);
     ca.ulist = f32 ? (uint32_t *)(ws + L.ulist) : nullptr;
     ca.ucount = f32 ? (int32_t *)(ws + L.ucount) : nullptr;
     ca.slots = f32 ? nullptr : (uint32_t *)(ws + L.slots);
     ca.inv_sqrt_d = 1.0 / sqrt((double)d);
+    mark_stage(ev, 1, 0, s);
     st = device_status(sla::launch_classify(ca, s), "classify launch");
     if (st != SLA_OK) return st;
-    mark_stage(ev, 2, s);
+    mark_stage(ev, 1, 1, s);
 
     if (states) {
-        sla::StateArgs sa{};
-        sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp;
-        sa.hs = ws + L.hs; sa.wstate = ws + L.wst; sa.bf16_in = !f32;
-        st = device_status(sla::launch_state(sa, s), "state launch");
+        guard.ss = nullptr;
+        st = device_status(hipStreamWaitEvent(s, ss->join, 0), "join");
         if (st != SLA_OK) return st;
     }
-    mark_stage(ev, 3, s);
+    mark_stage(ev, 3, 0, s);
     if (states) {
         sla::AssembleArgs aa{};
-        aa.E = ws + L.E; aa.hs = ws + L.hs; aa.mcount = mcount; aa.hhat = ws + L.hhat;
-        aa.BH = BH; aa.Nb = Nb; aa.Nbc = L.Nbc; aa.Lp = L.Lp; aa.f32 = f32;
+        aa.marg = ws + L.marg; aa.mbits = (const uint32_t *)(ws + L.mbits); aa.hs = ws + L.hs; aa.mcount = mcount; aa.hhat = ws + L.hhat;
+        aa.BH = BH; aa.Nb = Nb; aa.Nbc = L.Nbc; aa.Nbp = L.Nbp; aa.Lp = L.Lp; aa.f32 = f32;
         st = device_status(sla::launch_assemble(aa, s), "assemble launch");
         if (st != SLA_OK) return st;
     }
-    mark_stage(ev, 4, s);
+    mark_stage(ev, 3, 1, s);
+    mark_stage(ev, 4, 0, s);
     sla::FusedArgs fa{};
     fa.q = q; fa.k = k; fa.v = v; fa.ulist = (const uint32_t *)(ws + L.ulist);
     fa.ucount = (const int32_t *)(ws + L.ucount); fa.slots = (const uint32_t *)(ws + L.slots); fa.kc = kc;
@@ -282,7 +352,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;
     st = device_status(f32 ? sla::launch_fused(fa, s) : sla::launch_fused16(fa, s), "fused launch");
-    mark_stage(ev, 5, s);
+    mark_stage(ev, 4, 1, s);
     return st;
 }
 

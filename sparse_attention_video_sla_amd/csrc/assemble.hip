@@ -1,52 +1,247 @@
 // assemble.hip -- marginal linear-attention states per query-block row.
 //
-// For each row i the linear branch needs H_i = sum over the marginal key
-// blocks of h_j (and Z_i likewise).  They are formed as the total over all
-// key blocks minus the excluded (critical and negligible) ones:
-//     H_i = H_tot - sum_j E_ij h_j,   E_ij = 1 if block j is critical or negligible.
-// The excluded sums for all rows of a head are one dense GEMM E * Hs
-// ([Nb x Nb] 0/1 times [Nb x (d*d+d)]) on fp16 MFMA with fp32 accumulation
-// (float MFMA for float inputs); the 0/1 matrix is exact in fp16.  The
-// totals are summed by the same workgroup from the very Hs values it streams,
-// so H_tot and the excluded sums subtract consistently.
-// Output row i is (H_tot - E_i Hs) * 64 / m_i with m_i the row's marginal
-// token count: the linear output phi(q) H / (phi(q).Z) does not depend on a
-// common scale of H and Z, and this one keeps |values| <= max|V W^T|.
+// For each row i the linear branch needs H_i = sum of h_j over the marginal
+// key blocks j of that row (and Z_i likewise; SLA article, section 3).  For all
+// rows of a head at once this is one dense GEMM M * Hs with M the [Nb x Nbc]
+// 0/1 marginal indicator (M_ij = 1 iff block j is marginal for row i; padding
+// columns 0) and Hs the [Nbc x Lp] block states, on fp16 MFMA with fp32
+// accumulation (float MFMA for float inputs); the 0/1 matrix is exact in
+// fp16.
+// Output row i is (M_i Hs) * 64 / m_i with m_i the row's marginal token
+// count: the linear output phi(q) H / (phi(q).Z) does not depend on a common
+// scale of H and Z, and this one keeps |values| <= max|V W^T|.
 //
-// The product is computed transposed, D^T = Hs^T E^T (M = state column, N =
+// The product is computed transposed, D^T = Hs^T M^T (M = state column, N =
 // query-block row, K = key block), so that each lane ends with 4 consecutive
-// columns of one output row.  Tile: 256 columns x 128 rows per workgroup, 4
-// waves of 128 x 64, K-steps of 32 key blocks double-buffered through LDS.
-// Hs rows (one per key block, columns contiguous) are staged as they are and
-// the A fragments (8 consecutive blocks of one column) come out of LDS with
-// transposing reads; E rows are staged with a padded stride that keeps the B
-// fragment reads free of bank conflicts.  The totals are summed from the very
-// chunks each thread stages, then reduced across the 8 threads of a column
-// group.  Workgroups are ordered so that the row tiles of one column slice run
-// together on one XCD and share its L2.
+// columns of one output row.  Workgroups are ordered so that the row tiles
+// of one column slice run together on one XCD and share its L2.
+//
+// float path: the indicator as float rows; tile 256 columns x 128 rows per
+// workgroup, 4 waves of 128 x 64, K-steps of 32 key blocks double-buffered
+// through registers and LDS.
+//
+// fp16 path: one workgroup of 8 waves owns 128 state columns and up to 512
+// query-block rows (64 per wave), so a head's states stream from memory into
+// LDS once per 512 rows.  The K-steps (64 key blocks, 16 KB of Hs) go through
+// a ring of four LDS stages filled by loads that go straight from memory into
+// LDS: three steps are in flight while the fourth is multiplied, with one
+// barrier per step.  A stage also holds the step's indicator words of the
+// tile's rows.  The step loop is unrolled by four so that every stage is
+// a fixed LDS array.  Hs rows are stored as they are with 16-byte chunks
+// XOR-swizzled by row, so that the A fragments (8 consecutive blocks of one
+// column) come out with conflict-free transposing reads.  The indicator comes
+// as bits (32 key blocks per word); each lane reads the words of its own
+// rows from the stage and expands them into the fp16 B operand in registers.  The output tile of a wave is
+// scaled, staged through LDS (8-byte units swizzled by row) and written as
+// whole contiguous row segments.
 #include "sla_device.h"
 #include "sla_launch.h"
 
 namespace sla {
 
+namespace {
+
+// workgroup barrier that leaves global loads (and loads into LDS) in flight
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+// 16 (4) bytes per lane from a buffer into LDS at lds + 16 (4) * lane (lds is wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
+}
+
+constexpr int AT_TM = 128;                               // state columns per workgroup
+constexpr int AT_TN = 512;                               // query-block rows per workgroup (8 waves x 64)
+constexpr int AT_TK = 64;                                // key blocks per step
+constexpr int AT_HS = AT_TK * AT_TM;                     // Hs elements of one step (16 KB)
+constexpr int AT_STAGE = AT_HS + 2 * AT_TN * 2;          // one LDS stage in f16 units: Hs, then 2 x 512 words
+constexpr int AT_NA = AT_HS * 2 / 1024 / 8;              // 1 KB Hs loads per wave per step (2)
+constexpr int AT_NW = 2 * AT_TN * 4 / 256 / 8;           // 256-byte indicator loads per wave per step (2)
+constexpr int AT_VM = AT_NA + AT_NW;                     // memory operations per wave per step
+
+// one K-step into a stage: this wave's two 1 KB pieces of the Hs rows (four
+// 256-byte rows each) and its two 256-byte pieces of the indicator words
+// (word h of rows 64 i .. 64 i + 63 of the tile at 64 (8 h + i))
+__device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rb, f16 *S,
+                                         const uint32_t (&va)[AT_NA], const uint32_t (&vw)[AT_NW], int w,
+                                         uint32_t aoff, uint32_t woff) {
+#pragma unroll
+    for (int u = 0; u < AT_NA; ++u) dma16(rh, S + (AT_NA * w + u) * 512, va[u] + aoff);
+    uint32_t *W = reinterpret_cast<uint32_t *>(S + AT_HS);
+#pragma unroll
+    for (int u = 0; u < AT_NW; ++u) dma4(rb, W + 64 * (AT_NW * w + u), vw[u] + woff);
+}
+
+// 8 indicator bits -> 8 fp16 values (1.0 = 0x3C00): each dword takes two bits
+// y, spread to bit 0 and bit 16 by (y * 0x8001) & 0x10001, times 0x3C00
+__device__ __forceinline__ v8<f16> expand_bits(uint32_t x) {
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t y = (x >> (2 * e)) & 3u;
+        d[e] = __umul24(__umul24(y, 0x8001u) & 0x10001u, 0x3C00u);
+    }
+    v8<f16> r;
+    __builtin_memcpy(&r, d, sizeof(r));
+    return r;
+}
+
+// the 32 MFMAs of one K-step for a wave's 128 x 64 tile (rows 64 w .. 64 w + 63)
+__device__ __forceinline__ void at_compute(const f16 *S, f32x16 (&acc)[4][2], int w, int lane) {
+    const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4, L = lane & 15;
+    const f16 *A = S;
+    const uint32_t *W = reinterpret_cast<const uint32_t *>(S + AT_HS);
+    uint32_t bw[2][2];                                   // word h of row nt: key blocks 32 h .. 32 h + 31
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bw[nt][h] = W[AT_TN * h + 64 * w + 32 * nt + l32];
+#pragma unroll
+    for (int s = 0; s < AT_TK / 16; ++s) {
+        v8<f16> b[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)                  // key blocks 16 s + 8 hh .. + 7 of the lane's row
+            b[nt] = expand_bits(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int n = 32 * mt + 16 * (grp & 1) + 4 * (L & 3);              // state column of this lane's run
+            v4<f16> h[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int k = 16 * s + 8 * (grp >> 1) + 4 * x + (L >> 2);      // key block within the step
+                h[x] = lds_tr_raw<f16>(&A[k * AT_TM + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7)]);
+            }
+            const v8<f16> a = cat8<f16>(h[0], h[1]);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) mma16(acc[mt][nt], a, b[nt]);
+        }
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restrict__ mbits,
+                                                         const f16 *__restrict__ hs,
+                                                         const int32_t *__restrict__ mcount,
+                                                         f16 *__restrict__ hhat, int Nb, int Nbc, int Nbp, int Lp,
+                                                         int tiles_m, int tiles_n, long G, int per_xcd) {
+    // four stages; separate arrays so that reads of one stage never wait for
+    // loads still landing in another
+    __shared__ __attribute__((aligned(1024))) f16 S0[AT_STAGE], S1[AT_STAGE], S2[AT_STAGE], S3[AT_STAGE];
+
+    const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (logical >= G) return;
+    const int tn = (int)(logical % tiles_n);
+    const long rest = logical / tiles_n;
+    const int tm = (int)(rest % tiles_m);
+    const long bh = rest / tiles_m;
+    const int col0 = AT_TM * tm, row0 = AT_TN * tn;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wrow = row0 + 64 * wave;                   // first row of this wave
+
+    // buffer resources over one head: Hs rows and indicator words past the
+    // end read as zeros
+    const int nw = Nbc / 32;
+    const auto rh = make_rsrc(hs + bh * (long)Nbc * Lp, (uint32_t)((long)Nbc * Lp * 2));
+    const auto rb = make_rsrc(mbits + bh * (long)nw * Nbp, (uint32_t)((long)nw * Nbp * 4));
+    uint32_t va[AT_NA], vw[AT_NW];
+#pragma unroll
+    for (int u = 0; u < AT_NA; ++u) {
+        const int r = 4 * (AT_NA * wave + u) + (lane >> 4), p = lane & 15;   // LDS row and chunk of this lane
+        va[u] = (uint32_t)(((long)r * Lp + col0 + 8 * (p ^ (4 * (r & 3)))) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < AT_NW; ++u) {
+        const int i = AT_NW * wave + u;                  // word i / 8 of rows 64 (i % 8) + lane
+        vw[u] = (uint32_t)(((long)(i >> 3) * Nbp + row0 + 64 * (i & 7) + lane) * 4);
+    }
+    const uint32_t astep = (uint32_t)AT_TK * Lp * 2, wstep = (uint32_t)Nbp * 8;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+    const int nst = Nbc / AT_TK;
+    const bool active = wrow < Nb;                       // the wave has rows to compute
+    at_issue(rh, rb, S0, va, vw, wave, 0, 0);
+    at_issue(rh, rb, S1, va, vw, wave, astep, wstep);
+    at_issue(rh, rb, S2, va, vw, wave, 2 * astep, 2 * wstep);
+    // step st: wait for its loads (the next two steps' stay in flight),
+    // barrier, refill the stage freed by step st - 1 with step st + 3,
+    // multiply.  The loads are issued on every path, also for the steps past
+    // the end (they read zeros): every step then issues the same number of
+    // memory operations, which the wait counts, and the compiler tells the
+    // stages apart and adds no waits of its own before the reads of a stage.
+    auto stage = [&](int st, const f16 *S, f16 *Sn) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * AT_VM));   // vmcnt(8)
+        lds_barrier();
+        at_issue(rh, rb, Sn, va, vw, wave, (uint32_t)(st + 3) * astep, (uint32_t)(st + 3) * wstep);
+        if (active && st < nst) at_compute(S, acc, wave, lane);
+    };
+    for (int st = 0; st < nst; st += 4) {
+        stage(st, S0, S3);
+        stage(st + 1, S1, S0);
+        stage(st + 2, S2, S1);
+        stage(st + 3, S3, S2);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    lds_barrier();                                       // every wave is done with the stages
+    if (!active) return;
+
+    // epilogue: the wave's 32-row halves go through a private 8 KB LDS slice,
+    // 8-byte unit u of row r at unit u ^ r (conflict-free both ways)
+    f16 *stg = (wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) + (wave & 1) * 4096;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int i = wrow + 32 * nt + l32;
+        const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
+        const float sc = mc > 0 ? 64.f / (float)mc : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int u = 8 * mt + 2 * g + hh;       // 8-byte unit: columns 4u .. 4u + 3 of the tile
+                v4<f16> y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = (f16)(acc[mt][nt][4 * g + e] * sc);
+                __builtin_memcpy(&stg[l32 * AT_TM + 4 * (u ^ l32)], &y, sizeof(y));
+            }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int r = 2 * x + hh, u = l32;           // row r, unit u of the staged half
+            const int ir = wrow + 32 * nt + r;
+            const v4<f16> y = ld4<f16>(&stg[r * AT_TM + 4 * (u ^ r)]);
+            if (ir < Nb) __builtin_memcpy(hhat + (bh * Nb + ir) * (long)Lp + col0 + 4 * u, &y, sizeof(y));
+        }
+    }
+}
+
 template <typename S>
-__global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ E, const S *__restrict__ hs,
+__global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ marg, const S *__restrict__ hs,
                                                           const int32_t *__restrict__ mcount,
                                                           S *__restrict__ hhat, int Nb, int Nbc, int Lp,
                                                           int tiles_m, int tiles_n, long G, int per_xcd) {
+    // register-staged double buffering (float states)
     constexpr int TM = 256, TN = 128, TK = 32;
     constexpr int EPC = 16 / sizeof(S);                  // elements per 16-byte chunk
     constexpr int ACPR = TM / EPC;                       // chunks per staged Hs row
     constexpr int NA = TK * ACPR / 256;                  // A chunks per thread
     constexpr int TPA = 256 / ACPR;                      // threads sharing one A column group
     constexpr int ASTR = TM + (sizeof(S) == 2 ? 16 : 8); // staged Hs row stride
-    constexpr int BCPR = TK / EPC;                       // chunks per staged E row
+    constexpr int BCPR = TK / EPC;                       // chunks per staged M row
     constexpr int NB = TN * BCPR / 256;                  // B chunks per thread
-    constexpr int BSTR = TK + EPC;                       // padded E row stride
+    constexpr int BSTR = TK + EPC;                       // padded M row stride
     __shared__ __attribute__((aligned(16))) S As[2][TK * ASTR];
     __shared__ __attribute__((aligned(16))) S Bs[2][TN * BSTR];
-    __shared__ float red[TPA][TM];
-    __shared__ float scale_s[TN];
 
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
@@ -58,13 +253,10 @@ __global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
-    const S *Eh = E + bh * Nb * (long)Nbc;
+    const S *Mh = marg + bh * Nb * (long)Nbc;
     const S *Hh = hs + bh * (long)Nbc * Lp;
 
     const int acg = tid % ACPR, ajr = tid / ACPR;        // this thread's A column group and first row
-    float tot[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) tot[e] = 0.f;
     Chunk pa[NA], pb[NB];
     auto gload = [&](int j0) {
 #pragma unroll
@@ -73,17 +265,12 @@ __global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ 
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
             const int idx = tid + 256 * u, row = idx / BCPR, q = idx % BCPR;
-            pb[u] = (row0 + row < Nb) ? ld_chunk(Eh + (long)(row0 + row) * Nbc + j0 + q * EPC) : zero_chunk();
+            pb[u] = (row0 + row < Nb) ? ld_chunk(Mh + (long)(row0 + row) * Nbc + j0 + q * EPC) : zero_chunk();
         }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            st_chunk(&As[buf][(ajr + TPA * u) * ASTR + acg * EPC], pa[u]);
-            const S *x = reinterpret_cast<const S *>(&pa[u]);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) tot[e] += to_f32<S>(x[e]);
-        }
+        for (int u = 0; u < NA; ++u) st_chunk(&As[buf][(ajr + TPA * u) * ASTR + acg * EPC], pa[u]);
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
             const int idx = tid + 256 * u, row = idx / BCPR, q = idx % BCPR;
@@ -127,29 +314,11 @@ __global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ 
     }
 
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) red[ajr][acg * EPC + e] = tot[e];
-    if (tid < TN) {
-        const int i = row0 + tid;
-        const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
-        scale_s[tid] = mc > 0 ? 64.f / (float)mc : 0.f;
-    }
-    __syncthreads();
-    // column totals in LDS (reuse the A staging area)
-    float *tot_s = reinterpret_cast<float *>(&As[0][0]);
-    {
-        float t = 0.f;
-#pragma unroll
-        for (int x = 0; x < TPA; ++x) t += red[x][tid];
-        tot_s[tid] = t;
-    }
-    __syncthreads();
-
-#pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const int il = 64 * wn + 32 * nt + l32;
-        const int i = row0 + il;
+        const int i = row0 + 64 * wn + 32 * nt + l32;
         if (i >= Nb) continue;
-        const float sc = scale_s[il];
+        const int mc = mcount[bh * Nb + i];
+        const float sc = mc > 0 ? 64.f / (float)mc : 0.f;
         S *orow = hhat + (bh * Nb + i) * (long)Lp + col0;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -158,26 +327,32 @@ __global__ __launch_bounds__(256, 2) void assemble_kernel(const S *__restrict__ 
                 const int cl = 128 * wm + 32 * mt + 8 * g + 4 * hh;
                 v4<S> y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = from_f32<S>((tot_s[cl + e] - acc[mt][nt][4 * g + e]) * sc);
+                for (int e = 0; e < 4; ++e) y[e] = from_f32<S>(acc[mt][nt][4 * g + e] * sc);
                 __builtin_memcpy(orow + cl, &y, sizeof(y));
             }
     }
 }
 
-template <typename S>
-static hipError_t launch_assemble_t(const AssembleArgs &a, hipStream_t st) {
-    const int tiles_m = a.Lp / 256;             // column tiles (Lp is a multiple of 256)
-    const int tiles_n = (a.Nb + 127) / 128;     // row tiles
-    const long G = a.BH * tiles_m * tiles_n;
-    const int per = (int)((G + 7) / 8);
-    assemble_kernel<S><<<(unsigned)(8L * per), 256, 0, st>>>((const S *)a.E, (const S *)a.hs, a.mcount,
-                                                            (S *)a.hhat, a.Nb, a.Nbc, a.Lp, tiles_m,
-                                                            tiles_n, G, per);
-    return hipGetLastError();
-}
-
 hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st) {
-    return a.f32 ? launch_assemble_t<float>(a, st) : launch_assemble_t<f16>(a, st);
+    if (a.Nbc % 64 != 0 || a.Nbc < a.Nb || (long)(a.Nbc + 256) * a.Lp * 4 >= (1L << 32)) return hipErrorInvalidValue;
+    if (a.f32) {
+        const int tiles_m = a.Lp / 256;             // column tiles (Lp is a multiple of 256)
+        const int tiles_n = (a.Nb + 127) / 128;     // row tiles
+        const long G = a.BH * tiles_m * tiles_n;
+        const int per = (int)((G + 7) / 8);
+        assemble_kernel<float><<<(unsigned)(8L * per), 256, 0, st>>>((const float *)a.marg, (const float *)a.hs,
+                                                                    a.mcount, (float *)a.hhat, a.Nb, a.Nbc, a.Lp,
+                                                                    tiles_m, tiles_n, G, per);
+    } else {
+        if (a.Nbp % AT_TN != 0 || a.Nbp < a.Nb) return hipErrorInvalidValue;
+        const int tiles_m = a.Lp / AT_TM;
+        const int tiles_n = (a.Nb + AT_TN - 1) / AT_TN;
+        const long G = a.BH * tiles_m * tiles_n;
+        const int per = (int)((G + 7) / 8);
+        assemble16_kernel<<<(unsigned)(8L * per), 512, 0, st>>>(a.mbits, (const f16 *)a.hs, a.mcount, (f16 *)a.hhat,
+                                                                a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G, per);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace sla

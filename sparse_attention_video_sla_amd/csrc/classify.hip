@@ -17,8 +17,9 @@
 //      runs on inverted keys with ties taken from the highest index down.
 //   3. The row's outputs: int8 labels, ascending critical list, optional
 //      ascending excluded list, optional P_c, and for the forward pass the
-//      0/1 exclusion row E (critical or negligible) used by the marginal-state
-//      GEMM and the number of marginal tokens of the row.
+//      0/1 marginal indicator row used by the marginal-state GEMM (float
+//      values for float inputs, bits otherwise) and the number of marginal
+//      tokens of the row.
 //   4. For the forward pass, per pair of rows (2p, 2p+1): the ascending union
 //      of their critical lists, each entry j | in_row_2p << 16 | in_row_2p+1 << 17
 //      (32-bit, so that the fused kernel reads it with scalar loads), and its
@@ -101,11 +102,12 @@ __device__ void mark(const RowKeys<KM> &rk, int8_t *lab, int Nb, int lane, bool 
     }
 }
 
-template <typename ES, int D, int R, int KM>
+template <int D, int R, int KM>
 __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, int Nb, int kc, int kn,
     int8_t *__restrict__ mask, int32_t *__restrict__ crit, int32_t *__restrict__ excl,
-    float *__restrict__ pc, ES *__restrict__ E, int Nbc, int32_t *__restrict__ mcount, int n_last,
+    float *__restrict__ pc, float *__restrict__ marg, uint32_t *__restrict__ mbits, int Nbc, int Nbp,
+    int32_t *__restrict__ mcount, int n_last,
     uint32_t *__restrict__ ulist, int32_t *__restrict__ ucount, uint32_t *__restrict__ slots,
     double inv_sqrt_d) {
     extern __shared__ double smem[];
@@ -174,9 +176,15 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
             const int px_pos = run_x + __popcll(bx & lt);
             if (excl && ok && lb != 0 && px_pos < kc + kn) excl[row * (kc + kn) + px_pos] = j;
             run_x += __popcll(bx);
-            n_marg += __popcll(__ballot(ok && lb == 0));
+            const uint64_t bm = __ballot(ok && lb == 0);
+            n_marg += __popcll(bm);
+            if (mbits && lane == 0) {                  // Nbc is a multiple of 64: both words exist
+                uint32_t *wp = mbits + (bh * (Nbc / 32) + 2 * e) * (long)Nbp + i0 + r;
+                wp[0] = (uint32_t)bm;
+                wp[Nbp] = (uint32_t)(bm >> 32);
+            }
             if (ok && lb == 0 && j == Nb - 1) last_marg = true;
-            if (E && j < Nbc) E[row * Nbc + j] = from_f32<ES>((ok && lb != 0) ? 1.f : 0.f);
+            if (marg && j < Nbc) marg[row * Nbc + j] = (ok && lb == 0) ? 1.f : 0.f;
         }
         if (mcount) {
             const bool lm = __ballot(last_marg) != 0ull;
@@ -247,39 +255,39 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
     }
 }
 
-template <typename ES, int D, int R, int KM>
+template <int D, int R, int KM>
 static hipError_t launch_cls_k(const ClassifyArgs &a, hipStream_t st) {
     const size_t lds = classify_lds_bytes(R, D, a.Nb);
-    auto kern = classify_kernel<ES, D, R, KM>;
+    auto kern = classify_kernel<D, R, KM>;
     hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     const long tiles = (a.Nb + R - 1) / R;
     const unsigned grid = (unsigned)(a.BH * tiles);
     kern<<<grid, CL_THREADS, lds, st>>>(a.qp, a.kp, a.Nb, a.kc, a.kn, a.mask, a.crit, a.excl, a.pc,
-                                        (ES *)a.E, a.Nbc, a.mcount, a.n_last, a.ulist, a.ucount, a.slots,
+                                        a.marg, a.mbits, a.Nbc, a.Nbp, a.mcount, a.n_last, a.ulist, a.ucount, a.slots,
                                         a.inv_sqrt_d);
     return hipGetLastError();
 }
 
 // keys per lane: ceil(Nb / 64) rounded up to 8, 16, 24, 32 or 38 registers pairs
-template <typename ES, int D, int R>
+template <int D, int R>
 static hipError_t launch_cls_r(const ClassifyArgs &a, hipStream_t st) {
     const int ne = (a.Nb + 63) / 64;
-    if (ne <= 8) return launch_cls_k<ES, D, R, 8>(a, st);
-    if (ne <= 16) return launch_cls_k<ES, D, R, 16>(a, st);
-    if (ne <= 24) return launch_cls_k<ES, D, R, 24>(a, st);
-    if (ne <= 32) return launch_cls_k<ES, D, R, 32>(a, st);
-    return launch_cls_k<ES, D, R, 38>(a, st);
+    if (ne <= 8) return launch_cls_k<D, R, 8>(a, st);
+    if (ne <= 16) return launch_cls_k<D, R, 16>(a, st);
+    if (ne <= 24) return launch_cls_k<D, R, 24>(a, st);
+    if (ne <= 32) return launch_cls_k<D, R, 32>(a, st);
+    return launch_cls_k<D, R, 38>(a, st);
 }
 
-template <typename ES, int D>
+template <int D>
 static hipError_t launch_cls_d(const ClassifyArgs &a, hipStream_t st) {
     const int R = classify_rows_per_group(a.Nb, D);
     switch (R) {
-    case 8: return launch_cls_r<ES, D, 8>(a, st);
-    case 4: return launch_cls_r<ES, D, 4>(a, st);
-    case 2: return launch_cls_r<ES, D, 2>(a, st);
-    default: return launch_cls_r<ES, D, 2>(a, st);
+    case 8: return launch_cls_r<D, 8>(a, st);
+    case 4: return launch_cls_r<D, 4>(a, st);
+    case 2: return launch_cls_r<D, 2>(a, st);
+    default: return launch_cls_r<D, 2>(a, st);
     }
 }
 
@@ -295,8 +303,7 @@ int classify_rows_per_group(int Nb, int D) {
 }
 
 hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st) {
-    if (a.e_is_f32) return a.D == 64 ? launch_cls_d<float, 64>(a, st) : launch_cls_d<float, 128>(a, st);
-    return a.D == 64 ? launch_cls_d<f16, 64>(a, st) : launch_cls_d<f16, 128>(a, st);
+    return a.D == 64 ? launch_cls_d<64>(a, st) : launch_cls_d<128>(a, st);
 }
 
 }  // namespace sla

@@ -12,14 +12,14 @@ struct ClassifyArgs {
     int8_t *mask;
     int32_t *crit, *excl;
     float *pc;
-    void *E;          // nullable [BH][Nb][Nbc] 0/1 exclusion rows (f16, or float for f32 inputs)
-    int Nbc;
+    float *marg;      // nullable [BH][Nb][Nbc] 0/1 marginal indicator rows (float inputs)
+    uint32_t *mbits;  // nullable [BH][Nbc/32][Nbp] the same as bits: word w of row i holds blocks 32w..32w+31
+    int Nbc, Nbp;     // key blocks rounded up to 64, rows of the bit array
     int32_t *mcount;  // nullable [BH][Nb] marginal token count per row
     int n_last;       // valid tokens of the last block
     uint32_t *ulist;  // nullable [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
     int32_t *ucount;  // [BH][ceil(Nb/2)] union lengths
     uint32_t *slots;  // nullable [BH][ceil(Nb/2)][kc] slot schedule of each row pair (16-bit path)
-    bool e_is_f32;
     double inv_sqrt_d;
 };
 
@@ -28,17 +28,20 @@ struct StateArgs {
     const float *w;
     long BH;
     int N, Nb, D, Lp;
+    int Nbc;          // rows of hs per head (Nb rounded up to 64; the extra rows are zero)
     void *hs;         // [BH][Nbc][Lp] per-block states (h'^T then z), scaled by 1/64
     void *wstate;     // [d][d] W converted to the state type (scratch)
     bool bf16_in;
 };
 
 struct AssembleArgs {
-    const void *E, *hs;
+    const void *marg;        // [BH][Nb][Nbc] float marginal indicator (float inputs)
+    const uint32_t *mbits;   // [BH][Nbc/32][Nbp] marginal indicator bits (16-bit inputs)
+    const void *hs;          // [BH][Nbc][Lp] block states
     const int32_t *mcount;
     void *hhat;       // [BH][Nb][Lp] marginal states per query-block row
     long BH;
-    int Nb, Nbc, Lp;
+    int Nb, Nbc, Nbp, Lp;
     bool f32;
 };
 

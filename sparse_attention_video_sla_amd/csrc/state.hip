@@ -14,7 +14,9 @@
 // Stored per block as one row of Lp values, scaled by 1/64 (exact) so that
 // values stay within the range of the fp16 staging type:
 //   [h'^T row-major (column c*d + a holds h'[a][c]), z (d), zero pad].
-// Blocks past Nb up to the next multiple of 32 are written as zero rows.
+// Blocks past Nb up to Nbc (the next multiple of 64) are written as zero rows.
+#include <algorithm>
+
 #include "sla_device.h"
 #include "sla_launch.h"
 
@@ -154,9 +156,188 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
     for (int x = D * D + D + tid; x < Lp; x += NT) hsb[x] = from_f32<S>(0.f);
 }
 
+// workgroup barrier that leaves global loads in flight (the prefetched block)
+__device__ __forceinline__ void st_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// bf16 inputs, fp16 states: a persistent grid of two workgroups per CU, each
+// walking the key blocks b = blockIdx.x, + gridDim.x, ...  W stays in LDS for
+// the workgroup's lifetime.  The next block's K and V are loaded into the
+// registers that held the current block's as soon as phi and V are in LDS, so
+// the loads run under the products and stores of the current block.  The
+// state h'^T goes out through LDS (8-byte units swizzled by row) as whole
+// contiguous rows.
+template <int D>
+__global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+                                                          const f16 *__restrict__ w, int N, int Nb, int Nbc,
+                                                          long total, f16 *__restrict__ hs, int Lp) {
+    constexpr int NT = 2 * D;
+    constexpr int CPR = D / 8;               // 16-byte chunks per token row
+    constexpr int NCH = 64 * CPR / NT;       // chunks per thread and tensor
+    constexpr int SSTR = D + 8;              // V row stride in LDS
+    constexpr int PSTR = D + 16;             // phi row stride: 8 dwords mod 64 for transposing reads
+    constexpr int WSTR = D + 8;              // W row stride: conflict-free 16-byte B-fragment reads
+    constexpr int UPR = D / 4;               // 8-byte units per staged state row
+    constexpr int RPI = 64 / UPR;            // staged rows per wave-wide read
+    __shared__ __attribute__((aligned(16))) f16 Vs[64 * SSTR];
+    __shared__ __attribute__((aligned(16))) f16 Ph[64 * PSTR];
+    __shared__ __attribute__((aligned(16))) f16 Ws[D * WSTR];
+    static_assert(32 * D * 2 <= 64 * SSTR * 2 && 32 * D * 2 <= 64 * PSTR * 2, "staging fits");
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int x = tid; x < D * CPR; x += NT) {
+        const int r = x / CPR, c = x % CPR;
+        st_chunk(&Ws[r * WSTR + 8 * c], ld_chunk(w + (long)r * D + 8 * c));
+    }
+
+    Chunk kc[NCH], vc[NCH];
+    auto load = [&](long bb) {
+        const int j = (int)(bb % Nbc);
+        const long bh = bb / Nbc;
+        const int n = j < Nb ? min(64, N - 64 * j) : 0;
+        const bf16 *kb = k + (bh * N + 64L * j) * D;
+        const bf16 *vb = v + (bh * N + 64L * j) * D;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int ch = tid + NT * u, row = ch / CPR, cc = ch % CPR;
+            const bool ok = row < n;
+            kc[u] = ok ? ld_chunk(kb + (long)row * D + cc * 8) : zero_chunk();
+            vc[u] = ok ? ld_chunk(vb + (long)row * D + cc * 8) : zero_chunk();
+        }
+    };
+    long b = blockIdx.x;
+    const long G = gridDim.x;
+    if (b < total) load(b);
+    st_barrier();                            // W in LDS
+
+    constexpr float LOG2E = 1.4426950408889634f;
+    const float scale = 1.f / 64.f;
+    for (; b < total; b += G) {
+        const int j = (int)(b % Nbc);
+        f16 *hsb = hs + b * (long)Lp;
+        if (j >= Nb) {                       // padding block: a zero row (uniform branch, no LDS)
+            for (int x = tid; x < Lp; x += NT) hsb[x] = (f16)0.f;
+            if (b + G < total) load(b + G);
+            continue;
+        }
+        const int n = min(64, N - 64 * j);
+        // phi(K) per token row (the CPR threads of a row are consecutive lanes);
+        // phi and V to LDS in fp16
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int ch = tid + NT * u, row = ch / CPR, cc = ch % CPR;
+            const bf16 *x = reinterpret_cast<const bf16 *>(&kc[u]);
+            float xf[8];
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { xf[e] = (float)x[e]; mx = fmaxf(mx, xf[e]); }
+#pragma unroll
+            for (int off = 1; off < CPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { xf[e] = fast_exp2((xf[e] - mx) * LOG2E); sum += xf[e]; }
+#pragma unroll
+            for (int off = 1; off < CPR; off <<= 1) sum += __shfl_xor(sum, off, 64);
+            const float inv = (row < n) ? 1.f / sum : 0.f;
+            f16 ph[8], vv[8];
+            const bf16 *y = reinterpret_cast<const bf16 *>(&vc[u]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[e] = (f16)(xf[e] * inv);
+                vv[e] = (f16)(float)y[e];
+            }
+            __builtin_memcpy(&Ph[row * PSTR + cc * 8], ph, sizeof(ph));
+            __builtin_memcpy(&Vs[row * SSTR + cc * 8], vv, sizeof(vv));
+        }
+        st_barrier();
+        if (b + G < total) load(b + G);      // next block, under this block's products and stores
+
+        // V'[t][c] = sum_b V[t][b] W[c][b]: M = t (2 tiles), N = c (this wave's tile), K = b
+        f32x16 accv[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accv[mt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const v8<f16> bw = ld8<f16>(&Ws[(32 * wave + l32) * WSTR + 16 * s + 8 * hh]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) mma16(accv[mt], ld8<f16>(&Vs[(32 * mt + l32) * SSTR + 16 * s + 8 * hh]), bw);
+        }
+        // h'[a][c] = sum_t phi[t][a] V'[t][c]: M = a, N = c, K = t in the
+        // accumulator's permuted order (the phi^T operand takes the same t runs
+        // with transposing reads of the row-major phi tile)
+        f32x16 acch[D / 32];
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acch[mt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v8<f16> bv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = (f16)accv[s >> 1][8 * (s & 1) + e];
+            const int k0 = 16 * s + 4 * (grp >> 1);
+#pragma unroll
+            for (int mt = 0; mt < D / 32; ++mt) {
+                const int n0 = 32 * mt + 16 * (grp & 1);
+                mma16(acch[mt], cat8<f16>(lds_col4<f16>(Ph, PSTR, k0, n0, lane), lds_col4<f16>(Ph, PSTR, k0 + 8, n0, lane)), bv);
+            }
+        }
+        if (tid < D) {                       // z = sum over the block's tokens of phi
+            float z = 0.f;
+            for (int t = 0; t < 64; ++t) z += (float)Ph[t * PSTR + tid];
+            hsb[D * D + tid] = (f16)(z * scale);
+        }
+        for (int x = D * D + D + tid; x < Lp; x += NT) hsb[x] = (f16)0.f;
+        st_barrier();                        // Vs and Ph free: stage the state
+
+        // lane (c, h) holds h'[a][c] for a = 32 mt + 8 g + 4 h + 0..3, i.e. the
+        // 8-byte unit u = 8 mt + 2 g + h of row c; the wave's 32 rows c go
+        // through a private LDS slice with unit u of row r at u ^ (r % UPR)
+        f16 *stg = (wave < 2 ? Vs : Ph) + (wave & 1) * (32 * D);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int u = 8 * mt + 2 * g + hh;
+                v4<f16> y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = (f16)(acch[mt][4 * g + e] * scale);
+                __builtin_memcpy(&stg[l32 * D + 4 * (u ^ (l32 % UPR))], &y, sizeof(y));
+            }
+        f16 *orow = hsb + (long)(32 * wave) * D;
+#pragma unroll
+        for (int x = 0; x < 32 / RPI; ++x) {
+            const int r = RPI * x + lane / UPR, u = lane % UPR;
+            const v4<f16> y = ld4<f16>(&stg[r * D + 4 * (u ^ (r % UPR))]);
+            __builtin_memcpy(orow + r * D + 4 * u, &y, sizeof(y));
+        }
+        st_barrier();                        // staging read before the next block's phi and V
+    }
+}
+
+template <int D>
+static hipError_t launch_state16_t(const StateArgs &a, hipStream_t st) {
+    w_to_state_kernel<f16><<<(D * D + 255) / 256, 256, 0, st>>>(a.w, (f16 *)a.wstate, D * D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const long total = a.BH * a.Nbc;
+    const long grid = std::min<long>(total, 2L * cus);
+    state16_kernel<D><<<(unsigned)grid, 2 * D, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, (const f16 *)a.wstate,
+                                                        a.N, a.Nb, a.Nbc, total, (f16 *)a.hs, a.Lp);
+    return hipGetLastError();
+}
+
 template <typename T, typename S, int D>
 static hipError_t launch_state_t(const StateArgs &a, hipStream_t st) {
-    const int Nbc = (a.Nb + 31) / 32 * 32;
+    const int Nbc = a.Nbc;
     w_to_state_kernel<S><<<(D * D + 255) / 256, 256, 0, st>>>(a.w, (S *)a.wstate, D * D);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -167,8 +348,7 @@ static hipError_t launch_state_t(const StateArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_state(const StateArgs &a, hipStream_t st) {
-    if (a.bf16_in)
-        return a.D == 64 ? launch_state_t<bf16, f16, 64>(a, st) : launch_state_t<bf16, f16, 128>(a, st);
+    if (a.bf16_in) return a.D == 64 ? launch_state16_t<64>(a, st) : launch_state16_t<128>(a, st);
     return a.D == 64 ? launch_state_t<float, float, 64>(a, st) : launch_state_t<float, float, 128>(a, st);
 }
 

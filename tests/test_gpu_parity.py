@@ -209,6 +209,62 @@ def test_deterministic(sla):
     assert torch.equal(a, b) and torch.equal(ma, mb)
 
 
+def test_stream_ordering(sla):
+    """The block-state kernel runs on a side stream forked from the caller's
+    stream.  It must see K and V written on the caller's stream just before
+    the call (behind other queued work), and a second call that reuses the
+    workspace must not overwrite the first call's states before they are
+    used.  Nothing is synchronised between the steps below."""
+    say("stream ordering")
+    N, d, rc, rn = 3000, 128, 0.05, 0.10
+    a = make_inputs(1, 2, (1, 1, N), d, "bf16", seed=31)
+    b = make_inputs(1, 2, (1, 1, N), d, "bf16", seed=32)
+    qa, ka, va = dev(a.q, "bf16"), dev(a.k, "bf16"), dev(a.v, "bf16")
+    qb, kb, vb = dev(b.q, "bf16"), dev(b.k, "bf16"), dev(b.v, "bf16")
+    wa, wb = torch.from_numpy(a.w).to("cuda"), torch.from_numpy(b.w).to("cuda")
+    ws = torch.empty(sla.workspace_size(1, 2, N, d, "bf16", rc, rn), dtype=torch.uint8, device="cuda")
+    busy = torch.randn(2048, 2048, device="cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q, k, v = qa.clone(), ka.clone(), va.clone()
+        out_a = sla.forward(q, k, v, wa, rc, rn, workspace=ws)
+        for _ in range(8):                               # queue work ahead of the writes
+            busy = torch.mm(busy, busy) * 1e-3
+        q.copy_(qb)
+        k.copy_(kb)
+        v.copy_(vb)
+        out_b = sla.forward(q, k, v, wb, rc, rn, workspace=ws)
+    torch.cuda.synchronize()
+    for inp, out in ((a, out_a), (b, out_b)):
+        res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, rc, rn)
+        worst, rel = compare_rows(out, res, N, "bf16")
+        say("  max|d| %.3g rel %.3g" % (worst, rel))
+
+
+def test_stage_timing(sla):
+    """Stage timing records every stage of each call; the state stage runs
+    concurrently with pool and classify."""
+    import ctypes
+    say("stage timing")
+    inp = make_inputs(1, 2, (1, 1, 3000), 128, "bf16", seed=5)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    w = torch.from_numpy(inp.w).to("cuda")
+    L = sla._lib.load()
+    ms = (ctypes.c_float * 5)()
+    calls = ctypes.c_int()
+    L.sla_set_stage_timing(1)
+    try:
+        L.sla_stage_times(ms, ctypes.byref(calls))
+        for _ in range(3):
+            sla.forward(q, k, v, w, 0.05, 0.10)
+        sla._lib.check(L.sla_stage_times(ms, ctypes.byref(calls)))
+    finally:
+        L.sla_set_stage_timing(0)
+    assert calls.value == 3
+    assert all(ms[i] > 0 for i in range(5)), list(ms)
+
+
 # ------------------------------------------------------------------ named workloads, full size
 
 

@@ -110,9 +110,9 @@ __global__ __launch_bounds__(256, 2) void fused_kernel(const T *__restrict__ q, 
     auto gload = [&](Stage &st, int j) {
         const uint32_t so = (uint32_t)(64L * j * D * sizeof(T));
 #pragma unroll
-        for (int u = 0; u < NK; ++u) st.k[u] = buf_ld(rk, voff[u], so);
+        for (int u = 0; u < NK; ++u) st.k[u] = buf_ld(rk, voff[u] + so, 0);
 #pragma unroll
-        for (int u = 0; u < NK; ++u) st.v[u] = buf_ld(rv, voff[u], so);
+        for (int u = 0; u < NK; ++u) st.v[u] = buf_ld(rv, voff[u] + so, 0);
     };
     auto lstore = [&](const Stage &st, int buf) {
         T *Ks = lds + buf * (KT + VT);

@@ -271,16 +271,19 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
         }
     };
     // loads into LDS of the tiles of slot entry e: K (kh = 1 waves) or V
-    // (kh = 0 waves) into the ring slot dst; NB1 1 KB blocks per tile and wave
+    // (kh = 0 waves) into the ring slot dst; NB1 1 KB blocks per tile and
+    // wave.  The tile's offset goes into the per-lane offset, which the
+    // buffer's bounds check covers, so a ragged last tile reads zeros past
+    // the head's end.
     auto load_tiles = [&](uint32_t e, const T *dst) {
         const uint32_t sa = (uint32_t)(64L * tile_a(e) * D * sizeof(T));
         const uint32_t sb = (uint32_t)(64L * tile_b(e) * D * sizeof(T));
         const bool two = !single(e);
 #pragma unroll
-        for (int u = 0; u < NB1; ++u) dma16(rmy, dst + (w4 * NB1 + u) * 512, dvm[u], sa);
+        for (int u = 0; u < NB1; ++u) dma16(rmy, dst + (w4 * NB1 + u) * 512, dvm[u] + sa, 0);
         if (two) {
 #pragma unroll
-            for (int u = 0; u < NB1; ++u) dma16(rmy, dst + TILE + (w4 * NB1 + u) * 512, dvm[u], sb);
+            for (int u = 0; u < NB1; ++u) dma16(rmy, dst + TILE + (w4 * NB1 + u) * 512, dvm[u] + sb, 0);
         }
     };
     auto softmax = [&](uint32_t e1) {

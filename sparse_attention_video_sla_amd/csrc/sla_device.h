@@ -102,7 +102,9 @@ template <typename E> __device__ __forceinline__ v8<E> ld4x2(const E *p0, const 
 // Raw buffer loads through a 128-bit resource: the hardware checks each
 // access against num_records and returns zeros past the end, so a tile that
 // runs over the end of a head needs no per-lane guard.  The resource covers
-// one head, so a ragged last block reads zeros, never the next head.
+// one head, so a ragged last block reads zeros, never the next head.  Every
+// offset that must be checked goes into the per-lane offset (voff): callers
+// pass 0 as the scalar offset.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);

@@ -209,6 +209,30 @@ def test_deterministic(sla):
     assert torch.equal(a, b) and torch.equal(ma, mb)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_tail_reads_nothing_past_the_tensors(sla, dtype):
+    """K and V end right before a region of NaNs.  The last head's ragged
+    last block must read zeros (or nothing) past N: a NaN value of V would
+    reach the output through 0 * NaN."""
+    say("ragged tail", dtype)
+    B, H, N, d, rc, rn = 1, 2, 1000, 128, 0.3, 0.1
+    inp = make_inputs(B, H, (1, 1, N), d, dtype, seed=41)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    n = B * H * N * d
+    guarded = []
+    for x in (inp.k, inp.v):
+        buf = torch.full((n + 64 * d * 4,), float("nan"), dtype=tdt, device="cuda")
+        buf[:n].copy_(torch.from_numpy(np.ascontiguousarray(x)).reshape(-1).to(tdt))
+        guarded.append(buf[:n].view(B, H, N, d))
+    q = dev(inp.q, dtype)
+    w = torch.from_numpy(inp.w).to("cuda")
+    out = sla.forward(q, guarded[0], guarded[1], w, rc, rn)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, rc, rn)
+    compare_rows(out, res, N, dtype)
+
+
 def test_stream_ordering(sla):
     """The block-state kernel runs on a side stream forked from the caller's
     stream.  It must see K and V written on the caller's stream just before

@@ -160,14 +160,17 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
     const int i = 2 * pr + b;                            // this wave's query block
     const bool bvalid = i < Nb;
 
-    // Q rows of this wave as B fragments: lane (q, h) holds channels 16s + 8h .. +7
+    // Q rows of this wave as B fragments: lane (q, h) holds channels 16s + 8h .. +7.
+    // Their loads, the row's marginal count and the first slot entries are
+    // all issued before anything waits, so that their latencies overlap.
     const int qrow = 64 * i + 32 * qh + l32;
     const bool qvalid = bvalid && qrow < N;
+    const long rid = bh * Nb + i;
+    const bool lin = bvalid && mcount != nullptr && mcount[rid] > 0;
     v8<T> qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         qf[s] = qvalid ? ld8<T>(q + (bh * N + qrow) * (long)D + 16 * s + 8 * hh) : zero8<T>();
-    wait_vm0();                                          // Q complete: later waits count loads only
 
     float m = NEG_INF, l = 0.f;
     // row sums of P on the matrix core: lsum = 1^T P^T, every row of the
@@ -397,8 +400,6 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
     }
 
     // linear part: issue its loads before the exchange completes
-    const long rid = bh * Nb + i;
-    const bool lin = bvalid && mcount != nullptr && mcount[rid] > 0;
     const S *hr = hhat + rid * (long)Lp;
     v8<S> hz[NS], hv[NCH][NS];
     if (lin) {

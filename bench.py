@@ -15,6 +15,15 @@ marginal state; the projection is folded into the state kernel).
 `roofline.traffic` is the kernel's HBM bytes per launch from the committed
 rocprofv3 counter summary, reported only while the kernel source matches.
 `cpu_baseline` times the CPU oracle on whole heads (by default all of them).
+
+With --quality it prints instead one JSON line for the mask-quality
+diagnostics (sla_block_mass + sla_mask_stats) on the same workload: the
+exact block attention mass kept by the critical, marginal and negligible
+blocks, the 95 % block density, the relative error against dense attention
+(the same fused kernel at 100 % critical) of sparse-only attention as the
+skipped share grows and of sparse + linear attention (projection = identity:
+W is learned in the article), and the block-mass kernel's rate against the
+bf16 MFMA roofline, with the fp64 oracle timed on a sample of rows.
 """
 import argparse
 import ctypes
@@ -76,6 +85,80 @@ def cpu_baseline(inp, wl, rc, rn, heads):
             "ms_per_call_extrapolated": round(t * 1e3 * wl.H / heads, 1)}
 
 
+def run_quality(args, wl):
+    import torch
+    import sparse_attention_video_sla_amd as sla
+    from sparse_attention_video_sla_amd.inputs import make_workload
+
+    rc = args.crit if args.crit is not None else wl.fracs[0][0]
+    rn = args.negl if args.negl is not None else wl.fracs[0][1]
+    inp = make_workload(args.workload)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    B, H, N, d = q.shape
+    Nb = -(-N // 64)
+    eye = torch.eye(d, dtype=torch.float32, device=dev)
+
+    for _ in range(args.warmup):
+        sla.block_mass(q, k)
+    st = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        mass = sla.block_mass(q, k)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2 * 2.0 * B * H * N * N * d          # two passes of Q K^T
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    _, mask = sla.forward(q, k, v, eye, rc, rn, return_mask=True)
+    stats = sla.mask_stats(mass, mask)
+    mean = stats.reshape(-1, 4).double().mean(dim=0).tolist()
+
+    def rel(a, b):
+        return float(torch.linalg.vector_norm((a - b).double()) / torch.linalg.vector_norm(b.double()))
+
+    dense = sla.forward(q, k, v, eye, 1.0, 0.0)
+    sweep = []
+    for skip in (0.45, 0.70, 0.85, 0.92, 0.95):
+        so = sla.forward(q, k, v, eye, 1.0 - skip, skip)         # critical = the rest, nothing linear
+        sweep.append({"skipped_share": skip, "rel_err_sparse_only": round(rel(so, dense), 5)})
+    sl = sla.forward(q, k, v, eye, rc, rn)
+    so = sla.forward(q, k, v, eye, rc, 1.0 - rc)
+    torch.cuda.synchronize()
+
+    line = {
+        "metric": "exact block attention mass (mask-quality diagnostics): TFLOP/s of the block-mass kernel",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded)",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64, "crit_frac": rc, "negl_frac": rn},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "kernel": "block_mass16_kernel<128>",
+                     "flops_per_launch": flops},
+        "quality": {"critical_mass": round(mean[0], 5), "marginal_mass": round(mean[1], 5),
+                    "negligible_mass": round(mean[2], 5), "density95": round(mean[3], 5),
+                    "rel_err_sparse_linear_identity_w": round(rel(sl, dense), 5),
+                    "rel_err_sparse_only_same_critical": round(rel(so, dense), 5),
+                    "skip_sweep": sweep},
+    }
+    if not args.no_cpu:
+        from oracle import quality as oq
+        from sparse_attention_video_sla_amd.inputs import sample_query_blocks
+        rows = sample_query_blocks(B, H, Nb, max(1, args.cpu_heads or 4), 11)
+        t0 = time.perf_counter()
+        ref = oq.block_mass(inp.q, inp.k, 64, blocks=rows)
+        t = time.perf_counter() - t0
+        got = mass.reshape(B * H, Nb, Nb).cpu().numpy()
+        err = max(float(abs(got[bh, i] - ref[x]).max()) for x, (bh, i) in enumerate(rows))
+        f_rows = len(rows) * 64 * 2.0 * N * d
+        line["cpu_baseline"] = {"value": round(f_rows / t / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
+                                "kind": "oracle", "seconds": round(t, 3),
+                                "sample": "%d query blocks (fp64, one pass of Q K^T each)" % len(rows),
+                                "max_abs_diff_vs_gpu": err}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +169,7 @@ def main():
     ap.add_argument("--negl", type=float, default=None)
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quality", action="store_true", help="mask-quality diagnostics line instead of the forward line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
@@ -99,6 +183,9 @@ def main():
     from sparse_attention_video_sla_amd.inputs import WORKLOADS, make_workload
 
     wl = WORKLOADS[args.workload]
+    if args.quality:
+        run_quality(args, wl)
+        return
     rc = args.crit if args.crit is not None else wl.fracs[0][0]
     rn = args.negl if args.negl is not None else wl.fracs[0][1]
     inp = make_workload(args.workload)

@@ -116,6 +116,29 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
                        void *out, int8_t *mask_out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Mask-quality diagnostics (SLA article, section 2: a few attention weights
+ * carry most of the mass; SVOO page: attention density as the share of
+ * entries that covers 95 % of the cumulative attention mass).  Not part of
+ * the forward pass; dense work, O(N^2 d) per head.
+ *
+ * sla_block_mass: the exact block attention mass.
+ *   q, k: [B,H,N,d] bf16 (float32 inputs: SLA_ERR_UNSUPPORTED); block 64;
+ *   d in {64, 128}; Nb = ceil(N/64) <= 2432.
+ *   mass: [B,H,Nb,Nb] float32 output: mass[i][j] = the mean over the valid
+ *   rows r of query block i of the sum over the valid keys u of key block j
+ *   of softmax_u(q_r . k_u / sqrt(d)), the softmax over all N keys; each row
+ *   sums to 1 (fp32 accumulation).  Deterministic.
+ *
+ * sla_mask_stats: per row of blocks, from a mass matrix and the labels of
+ *   sla_classify / sla_forward (mask [rows][Nb] int8, rows = B*H*Nb):
+ *   stats [rows][4] float32 = mass on the critical, marginal and negligible
+ *   blocks, and the 95 % block density: the smallest number of key blocks,
+ *   taken by decreasing mass, whose mass reaches 0.95 of the row's total,
+ *   divided by Nb.  Nb <= 2432. */
+sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
+                          float *mass, void *stream);
+sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, void *stream);
+
 /* Stage timing, for profiling.  While enabled on a thread, every sla_forward
  * call of that thread records HIP events around each of its kernels, on the
  * stream the kernel runs on: 0 pool, 1 classify, 2 state, 3 assemble, 4 fused

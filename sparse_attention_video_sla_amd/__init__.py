@@ -16,7 +16,8 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "version", "SlaError"]
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "block_mass", "mask_stats", "version",
+           "SlaError"]
 
 SlaError = _lib.SlaError
 
@@ -142,3 +143,35 @@ def forward(q, k, v, w, crit_frac: float = 0.05, negl_frac: float = 0.10, block:
                                        out.data_ptr(), mask.data_ptr() if mask is not None else None,
                                        workspace.data_ptr(), workspace.numel(), _stream_ptr(dev)))
     return (out, mask) if return_mask else out
+
+
+def block_mass(q, k, block: int = 64):
+    """Exact block attention mass [B, H, Nb, Nb] float32 (diagnostic): row i,
+    column j is the mean over the valid rows of query block i of the full
+    softmax mass on key block j.  q, k: [B, H, N, d] bf16 on the GPU."""
+    torch = _torch()
+    _check_gpu(q, k)
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must have one shape and dtype")
+    B, H, N, d = q.shape
+    Nb = -(-N // block)
+    mass = torch.empty((B, H, Nb, Nb), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.load().sla_block_mass(q.data_ptr(), k.data_ptr(), _dtype_code(q), B, H, N, d, block,
+                                          mass.data_ptr(), _stream_ptr(q.device)))
+    return mass
+
+
+def mask_stats(mass, mask):
+    """Per row of blocks: [..., 4] float32 = mass on the critical, marginal and
+    negligible blocks and the 95 % block density.  mass: [B, H, Nb, Nb]
+    float32, mask: [B, H, Nb, Nb] int8 (from classify or forward)."""
+    torch = _torch()
+    _check_gpu(mass, mask)
+    if mass.shape != mask.shape or mass.dtype != torch.float32 or mask.dtype != torch.int8:
+        raise ValueError("mass (float32) and mask (int8) must have one shape")
+    Nb = mass.shape[-1]
+    rows = mass.numel() // Nb
+    stats = torch.empty(tuple(mass.shape[:-1]) + (4,), dtype=torch.float32, device=mass.device)
+    _lib.check(_lib.load().sla_mask_stats(mass.data_ptr(), mask.data_ptr(), rows, Nb, stats.data_ptr(),
+                                          _stream_ptr(mass.device)))
+    return stats

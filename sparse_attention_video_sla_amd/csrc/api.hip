@@ -191,6 +191,24 @@ sla_status sla_stage_times(float *ms, int *calls) {
 
 int sla_version(void) { return 100; }
 
+sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
+                          float *mass, void *stream) {
+    if (!q || !k || !mass) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    sla_status st = check_shape(B, H, N, d, block);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "block mass takes bf16 inputs");
+    sla::MassArgs a{};
+    a.q = q; a.k = k; a.BH = (long)B * H; a.N = N; a.Nb = (N + 63) / 64; a.D = d; a.mass = mass;
+    return device_status(sla::launch_block_mass(a, (hipStream_t)stream), "block mass launch");
+}
+
+sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, void *stream) {
+    if (!mass || !mask || !stats) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    if (rows < 1 || Nb < 1) return fail(SLA_ERR_INVALID_ARG, "rows and Nb must be >= 1");
+    if (Nb > MAX_NB) return fail(SLA_ERR_UNSUPPORTED, "Nb = %d exceeds the supported %d", Nb, MAX_NB);
+    return device_status(sla::launch_mask_stats(mass, mask, rows, Nb, stats, (hipStream_t)stream), "mask stats launch");
+}
+
 const char *sla_last_error(void) { return g_err.c_str(); }
 
 sla_status sla_counts(int Nb, double crit_frac, double negl_frac, int *k_c, int *k_n) {

@@ -60,6 +60,13 @@ struct FusedArgs {
     bool bf16_in, bf16_out;
 };
 
+struct MassArgs {
+    const void *q, *k;       // [BH][N][D] bf16
+    long BH;
+    int N, Nb, D;
+    float *mass;             // [BH][Nb][Nb]
+};
+
 hipError_t launch_pool(bool bf16_in, int D, const void *q, const void *k, float *qp, float *kp,
                        long BH, int N, int Nb, int blk, hipStream_t st);
 int classify_rows_per_group(int Nb, int D);
@@ -69,5 +76,7 @@ hipError_t launch_state(const StateArgs &a, hipStream_t st);
 hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st);     // float inputs
 hipError_t launch_fused16(const FusedArgs &a, hipStream_t st);   // bf16 inputs
+hipError_t launch_block_mass(const MassArgs &a, hipStream_t st);
+hipError_t launch_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, hipStream_t st);
 
 }  // namespace sla

@@ -116,6 +116,24 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
                        void *out, int8_t *mask_out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Sparse attention over block lists given by the caller, with the linear
+ * branch off (a mask source other than the scores, e.g. the LVSA page's
+ * frame-level sets A(t) = G_s U W(t) turned into key blocks; block-sparse
+ * softmax over the union of the listed blocks as in the LVSA page's method
+ * steps).
+ * lists: [B,H,Nb,kmax] int32 device array: for every query-block row, its key
+ *   blocks in ascending order in the first counts[row] entries (the rest is
+ *   ignored; entries outside [0, Nb) are ignored, a repeated index counts
+ *   once).  counts: [B,H,Nb] int32, each in [0, kmax].  A row with no block
+ *   gives zeros.  kmax in [1, Nb].
+ * q, k, v: [B,H,N,d] bf16 (float32: SLA_ERR_UNSUPPORTED); out: [B,H,N,d] of
+ *   out_dtype (F32 or BF16).  workspace: sla_lists_workspace_size() bytes,
+ *   256-byte aligned.  The cost follows kmax for every row pair. */
+sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes);
+sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
+                             int B, int H, int N, int d, int block, const int32_t *lists, const int32_t *counts,
+                             int kmax, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Mask-quality diagnostics (SLA article, section 2: a few attention weights
  * carry most of the mass; SVOO page: attention density as the share of
  * entries that covers 95 % of the cumulative attention mass).  Not part of

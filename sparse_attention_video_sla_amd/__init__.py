@@ -16,7 +16,7 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "block_mass", "mask_stats", "version",
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "block_mass", "mask_stats", "version",
            "SlaError"]
 
 SlaError = _lib.SlaError
@@ -175,3 +175,32 @@ def mask_stats(mass, mask):
     _lib.check(_lib.load().sla_mask_stats(mass.data_ptr(), mask.data_ptr(), rows, Nb, stats.data_ptr(),
                                           _stream_ptr(mass.device)))
     return stats
+
+
+def forward_lists(q, k, v, lists, counts, out_dtype=None, out=None, block: int = 64):
+    """Sparse attention over the key-block lists given per query-block row
+    (linear branch off).  lists: [B, H, Nb, kmax] int32 (ascending in the
+    first counts entries), counts: [B, H, Nb] int32, on q's device."""
+    torch = _torch()
+    _check_gpu(q, k, v, lists, counts)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one shape and dtype")
+    B, H, N, d = q.shape
+    Nb = -(-N // block)
+    if lists.dtype != torch.int32 or counts.dtype != torch.int32:
+        raise ValueError("lists and counts must be int32")
+    if lists.dim() != 4 or tuple(lists.shape[:3]) != (B, H, Nb) or tuple(counts.shape) != (B, H, Nb):
+        raise ValueError("lists must be [B, H, Nb, kmax] and counts [B, H, Nb]")
+    kmax = lists.shape[3]
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_code = _lib.SLA_F32 if out_dtype == torch.float32 else _dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    n = ctypes.c_size_t()
+    L = _lib.load()
+    _lib.check(L.sla_lists_workspace_size(B, H, N, kmax, ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(L.sla_forward_lists(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), out_code, B, H, N, d,
+                                   block, lists.data_ptr(), counts.data_ptr(), kmax, out.data_ptr(), ws.data_ptr(),
+                                   ws.numel(), _stream_ptr(q.device)))
+    return out

@@ -17,7 +17,7 @@ SLA_PHI_SOFTMAX = 0
 
 # every symbol include/sla.h declares
 EXPORTS = ("sla_version", "sla_counts", "sla_workspace_size", "sla_pool", "sla_classify",
-           "sla_forward", "sla_block_mass", "sla_mask_stats", "sla_set_stage_timing", "sla_stage_times",
+           "sla_forward", "sla_lists_workspace_size", "sla_forward_lists", "sla_block_mass", "sla_mask_stats", "sla_set_stage_timing", "sla_stage_times",
            "sla_last_error")
 STAGES = ("pool", "classify", "state", "assemble", "fused")
 
@@ -53,6 +53,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.sla_classify.argtypes = [P, P, I, I, I, I, D, D, P, P, P, P, P]
     L.sla_forward.restype = I
     L.sla_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, D, I, P, P, P, SZ, P]
+    L.sla_lists_workspace_size.restype = I
+    L.sla_lists_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
+    L.sla_forward_lists.restype = I
+    L.sla_forward_lists.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, I, P, P, SZ, P]
     L.sla_block_mass.restype = I
     L.sla_block_mass.argtypes = [P, P, I, I, I, I, I, I, P, P]
     L.sla_mask_stats.restype = I

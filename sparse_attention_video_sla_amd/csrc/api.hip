@@ -191,6 +191,45 @@ sla_status sla_stage_times(float *ms, int *calls) {
 
 int sla_version(void) { return 100; }
 
+sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes) {
+    if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
+    sla_status st = check_shape(B, H, N, 128, 64);
+    if (st != SLA_OK) return st;
+    const int Nb = (N + 63) / 64;
+    if (kmax < 1 || kmax > Nb) return fail(SLA_ERR_INVALID_ARG, "kmax must lie in [1, Nb] (got %d, Nb = %d)", kmax, Nb);
+    *bytes = align256(sizeof(uint32_t) * (size_t)B * H * ((Nb + 1) / 2) * kmax);
+    return SLA_OK;
+}
+
+sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
+                             int B, int H, int N, int d, int block, const int32_t *lists, const int32_t *counts,
+                             int kmax, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !lists || !counts || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    sla_status st = check_shape(B, H, N, d, block);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "attention over given lists takes bf16 inputs");
+    if (out_dtype != SLA_F32 && out_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "output dtype must be F32 or BF16");
+    size_t need = 0;
+    st = sla_lists_workspace_size(B, H, N, kmax, &need);
+    if (st != SLA_OK) return st;
+    if (!workspace) return fail(SLA_ERR_INVALID_ARG, "null workspace");
+    if (workspace_bytes < need)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const long BH = (long)B * H;
+    const int Nb = (N + 63) / 64;
+    uint32_t *slots = (uint32_t *)workspace;
+    st = device_status(sla::launch_lists_to_slots(lists, counts, kmax, BH, Nb, slots, s), "slot schedule launch");
+    if (st != SLA_OK) return st;
+    sla::FusedArgs fa{};
+    fa.q = q; fa.k = k; fa.v = v; fa.ulist = nullptr; fa.ucount = nullptr; fa.slots = slots; fa.kc = kmax;
+    fa.hhat = nullptr; fa.mcount = nullptr; fa.Lp = 0;
+    fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
+    fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
+    return device_status(sla::launch_fused16(fa, s), "fused launch");
+}
+
 sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
                           float *mass, void *stream) {
     if (!q || !k || !mass) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");

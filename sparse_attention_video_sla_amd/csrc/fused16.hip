@@ -106,12 +106,15 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 
 // slot entry: key block of row 2p in the low 16 bits, of row 2p+1 in the high
-// 16 bits (0xFFFF: the pair has no second row); indices are clamped to Nb - 1
+// 16 bits (0xFFFF: the pair has no second row; 0xFFFE: this row has no block
+// in the slot, its keys are masked); indices are clamped to Nb - 1
+constexpr uint32_t NO_TILE = 0xFFFEu;
 __device__ __forceinline__ int slot_tile(uint32_t e, int which, int Nb) {
     return min((int)(which ? (e >> 16) : (e & 0xFFFFu)), Nb - 1);
 }
-// one tile serves the slot: both rows selected the block, or there is no second row
-__device__ __forceinline__ bool slot_single(uint32_t e) { return (e >> 16) == (e & 0xFFFFu) || (e >> 16) == 0xFFFFu; }
+// one tile serves the slot: both rows selected the block, or the second row
+// has none (no row, or no block in this slot)
+__device__ __forceinline__ bool slot_single(uint32_t e) { return (e >> 16) == (e & 0xFFFFu) || (e >> 16) >= NO_TILE; }
 
 // swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
 template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -290,6 +293,10 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
         }
     };
     auto softmax = [&](uint32_t e1) {
+        if ((b ? (e1 >> 16) : (e1 & 0xFFFFu)) == NO_TILE) {   // no block for this row in the slot
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = NEG_INF;
+        }
         const int j = my_blk(e1);
         if (64 * j + 64 > N) {                           // ragged last block: keys past N score -inf
 #pragma unroll

@@ -77,6 +77,8 @@ hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st);     // float inputs
 hipError_t launch_fused16(const FusedArgs &a, hipStream_t st);   // bf16 inputs
 hipError_t launch_block_mass(const MassArgs &a, hipStream_t st);
+hipError_t launch_lists_to_slots(const int32_t *lists, const int32_t *counts, int kmax, long BH, int Nb,
+                                 uint32_t *slots, hipStream_t st);
 hipError_t launch_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, hipStream_t st);
 
 }  // namespace sla

@@ -125,14 +125,46 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
  *   blocks in ascending order in the first counts[row] entries (the rest is
  *   ignored; entries outside [0, Nb) are ignored, a repeated index counts
  *   once).  counts: [B,H,Nb] int32, each in [0, kmax].  A row with no block
- *   gives zeros.  kmax in [1, Nb].
+ *   gives zeros.  kmax in [1, Nb]; Nb = ceil(N/64) <= 4095.
  * q, k, v: [B,H,N,d] bf16 (float32: SLA_ERR_UNSUPPORTED); out: [B,H,N,d] of
  *   out_dtype (F32 or BF16).  workspace: sla_lists_workspace_size() bytes,
- *   256-byte aligned.  The cost follows kmax for every row pair. */
+ *   256-byte aligned.  The cost of a pair of rows follows the number of
+ *   distinct blocks the two rows list (a block both list counts once). */
 sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes);
 sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
                              int B, int H, int N, int d, int block, const int32_t *lists, const int32_t *counts,
                              int kmax, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* LVSA frame-level sparse attention (the LVSA page, training-free sparse
+ * attention for long-video diffusion: "Core method", "Method steps in
+ * detail"; linear branch off).  The sequence is T frames of P = N / T tokens
+ * each (token n in frame n / P), P >= 64.  At denoising step `step` every
+ * query token of frame t attends, in one softmax with scale 1/sqrt(d), every
+ * token of the frames in A(t) = G_s U W(t):
+ *   T_per = ceil(T / (C - (2W + 1)))  (C > 2W + 1, else SLA_ERR_INVALID_ARG);
+ *   G_s = {(step mod T_per + i T_per) mod T : 0 <= i < ceil(T / T_per)};
+ *   W(t): the window [w_lo, w_lo + 2W] clipped to frame T - 1, with
+ *   w_lo = max(0, min(t - W, T - 1 - 2W)), grown one frame at a time on the
+ *   side with more frames left outside it (the earlier side on a tie) until
+ *   it holds min(2W + 1, T - |G_s|) frames not in G_s.
+ * Every set then has |G_s| + min(2W + 1, T - |G_s|) frames.
+ *
+ * sla_lvsa_plan: host arithmetic only: T_per, |G_s| and the set size.
+ * sla_lvsa_sets: the sets on the device: sets [T][max_frames] int32, frame
+ *   t's set ascending in its first counts[t] entries; max_frames >= the set
+ *   size.
+ * sla_forward_lvsa: q, k, v: [B,H,N,d] bf16; out: [B,H,N,d] of out_dtype (F32
+ *   or BF16); N = T * P, Nb = ceil(N/64) <= 4095; workspace of
+ *   sla_lvsa_workspace_size() bytes, 256-byte aligned, clobbered.  The sets
+ *   and the block schedule are built in the stream by the library's own
+ *   kernels before the attention kernel (no host round trip). */
+sla_status sla_lvsa_plan(int T, int C, int W, int *t_per, int *n_global, int *frames_per_set);
+sla_status sla_lvsa_sets(int T, int C, int W, int step, int32_t *sets, int32_t *counts, int max_frames,
+                         void *stream);
+sla_status sla_lvsa_workspace_size(int B, int H, int N, int T, int C, int W, size_t *bytes);
+sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
+                            int B, int H, int N, int d, int block, int T, int C, int W, int step, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Mask-quality diagnostics (SLA article, section 2: a few attention weights
  * carry most of the mass; SVOO page: attention density as the share of

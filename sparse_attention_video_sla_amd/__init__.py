@@ -16,7 +16,8 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "block_mass", "mask_stats", "version",
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa",
+           "block_mass", "mask_stats", "version",
            "SlaError"]
 
 SlaError = _lib.SlaError
@@ -143,6 +144,56 @@ def forward(q, k, v, w, crit_frac: float = 0.05, negl_frac: float = 0.10, block:
                                        out.data_ptr(), mask.data_ptr() if mask is not None else None,
                                        workspace.data_ptr(), workspace.numel(), _stream_ptr(dev)))
     return (out, mask) if return_mask else out
+
+
+def lvsa_plan(T: int, C: int, W: int):
+    """(T_per, |G_s|, frames per set) of the LVSA frame sets (host arithmetic)."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _lib.check(_lib.load().sla_lvsa_plan(T, C, W, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def lvsa_sets(T: int, C: int, W: int, step: int, device="cuda"):
+    """LVSA frame sets A(t) built on the device: (sets [T, F] int32, counts
+    [T] int32), frame t's set ascending in its first counts[t] entries."""
+    torch = _torch()
+    F = lvsa_plan(T, C, W)[2]
+    sets = torch.full((T, F), -1, dtype=torch.int32, device=device)
+    cnt = torch.empty(T, dtype=torch.int32, device=device)
+    _lib.check(_lib.load().sla_lvsa_sets(T, C, W, step, sets.data_ptr(), cnt.data_ptr(), F,
+                                         _stream_ptr(torch.device(device))))
+    return sets, cnt
+
+
+def forward_lvsa(q, k, v, T: int, C: int, W: int, step: int, out_dtype=None, out=None, workspace=None,
+                 block: int = 64):
+    """LVSA frame-level sparse attention (linear branch off): the sequence is
+    T frames of N / T tokens; every query token of frame t attends the tokens
+    of the frames in A(t) = G_step U W(t)."""
+    torch = _torch()
+    _check_gpu(q, k, v)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one shape and dtype")
+    B, H, N, d = q.shape
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_code = _lib.SLA_F32 if out_dtype == torch.float32 else _dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    L = _lib.load()
+    n = ctypes.c_size_t()
+    _lib.check(L.sla_lvsa_workspace_size(B, H, N, T, C, W, ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(L.sla_forward_lvsa(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), out_code, B, H, N, d,
+                                  block, T, C, W, step, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                  _stream_ptr(q.device)))
+    return out
+
+
+def lvsa_workspace_size(B: int, H: int, N: int, T: int, C: int, W: int) -> int:
+    n = ctypes.c_size_t()
+    _lib.check(_lib.load().sla_lvsa_workspace_size(B, H, N, T, C, W, ctypes.byref(n)))
+    return n.value
 
 
 def block_mass(q, k, block: int = 64):

@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <array>
 #include <mutex>
 #include <string>
@@ -38,7 +39,8 @@ sla_status device_status(hipError_t e, const char *what) {
     return fail(SLA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int MAX_NB = 2432;
+constexpr int MAX_NB = 2432;        // score-based masks (the selection holds a row of scores per wave)
+constexpr int MAX_NB_LISTS = 4095;  // masks from lists or frame sets: 12-bit block indices in the slots
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 long round_up(long x, long m) { return (x + m - 1) / m * m; }
@@ -57,12 +59,12 @@ sla_status counts_impl(long Nb, double rc, double rn, int *kc, int *kn) {
     return SLA_OK;
 }
 
-sla_status check_shape(int B, int H, int N, int d, int block) {
+sla_status check_shape(int B, int H, int N, int d, int block, int max_nb = MAX_NB) {
     if (B < 1 || H < 1 || N < 1) return fail(SLA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
     if (d != 64 && d != 128) return fail(SLA_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", d);
     if (block != 64) return fail(SLA_ERR_UNSUPPORTED, "block size %d not supported (64)", block);
     const long Nb = (N + 63) / 64;
-    if (Nb > MAX_NB) return fail(SLA_ERR_UNSUPPORTED, "N = %d gives %ld blocks; at most %d are supported", N, Nb, MAX_NB);
+    if (Nb > max_nb) return fail(SLA_ERR_UNSUPPORTED, "N = %d gives %ld blocks; at most %d are supported", N, Nb, max_nb);
     return SLA_OK;
 }
 
@@ -193,11 +195,12 @@ int sla_version(void) { return 100; }
 
 sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes) {
     if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
-    sla_status st = check_shape(B, H, N, 128, 64);
+    sla_status st = check_shape(B, H, N, 128, 64, MAX_NB_LISTS);
     if (st != SLA_OK) return st;
     const int Nb = (N + 63) / 64;
     if (kmax < 1 || kmax > Nb) return fail(SLA_ERR_INVALID_ARG, "kmax must lie in [1, Nb] (got %d, Nb = %d)", kmax, Nb);
-    *bytes = align256(sizeof(uint32_t) * (size_t)B * H * ((Nb + 1) / 2) * kmax);
+    const size_t pairs = (size_t)B * H * ((Nb + 1) / 2);
+    *bytes = align256(sizeof(uint32_t) * pairs * kmax) + align256(sizeof(int32_t) * pairs);
     return SLA_OK;
 }
 
@@ -205,7 +208,7 @@ sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dt
                              int B, int H, int N, int d, int block, const int32_t *lists, const int32_t *counts,
                              int kmax, void *out, void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !lists || !counts || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
-    sla_status st = check_shape(B, H, N, d, block);
+    sla_status st = check_shape(B, H, N, d, block, MAX_NB_LISTS);
     if (st != SLA_OK) return st;
     if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "attention over given lists takes bf16 inputs");
     if (out_dtype != SLA_F32 && out_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "output dtype must be F32 or BF16");
@@ -220,12 +223,114 @@ sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dt
     const long BH = (long)B * H;
     const int Nb = (N + 63) / 64;
     uint32_t *slots = (uint32_t *)workspace;
-    st = device_status(sla::launch_lists_to_slots(lists, counts, kmax, BH, Nb, slots, s), "slot schedule launch");
+    int32_t *pcount = (int32_t *)((char *)workspace + align256(sizeof(uint32_t) * (size_t)BH * ((Nb + 1) / 2) * kmax));
+    st = device_status(sla::launch_lists_to_slots(lists, counts, kmax, BH, Nb, slots, pcount, s), "slot schedule launch");
     if (st != SLA_OK) return st;
     sla::FusedArgs fa{};
-    fa.q = q; fa.k = k; fa.v = v; fa.ulist = nullptr; fa.ucount = nullptr; fa.slots = slots; fa.kc = kmax;
-    fa.hhat = nullptr; fa.mcount = nullptr; fa.Lp = 0;
+    fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
+    fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
+    return device_status(sla::launch_fused16(fa, s), "fused launch");
+}
+
+// ---- LVSA frame-level sets --------------------------------------------------
+
+static sla_status lvsa_params(int T, int C, int W, int step, sla::LvsaParams *p, int *frames_per_set) {
+    if (T < 1) return fail(SLA_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
+    if (W < 0 || step < 0) return fail(SLA_ERR_INVALID_ARG, "W and step must be >= 0 (got %d, %d)", W, step);
+    if (C - (2 * W + 1) < 1) return fail(SLA_ERR_INVALID_ARG, "the budget C = %d must exceed the window 2W + 1 = %d", C, 2 * W + 1);
+    const int K = C - (2 * W + 1);
+    p->T = T; p->W = W; p->s = step;
+    p->Tper = (T + K - 1) / K;
+    p->m = (T + p->Tper - 1) / p->Tper;
+    *frames_per_set = p->m + std::min(2 * W + 1, T - p->m);
+    return SLA_OK;
+}
+
+sla_status sla_lvsa_plan(int T, int C, int W, int *t_per, int *n_global, int *frames_per_set) {
+    if (!t_per || !n_global || !frames_per_set) return fail(SLA_ERR_INVALID_ARG, "null output pointer");
+    sla::LvsaParams p;
+    int f;
+    sla_status st = lvsa_params(T, C, W, 0, &p, &f);
+    if (st != SLA_OK) return st;
+    *t_per = p.Tper; *n_global = p.m; *frames_per_set = f;
+    return SLA_OK;
+}
+
+sla_status sla_lvsa_sets(int T, int C, int W, int step, int32_t *sets, int32_t *counts, int max_frames,
+                         void *stream) {
+    if (!sets || !counts) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    sla::LvsaParams p;
+    int f;
+    sla_status st = lvsa_params(T, C, W, step, &p, &f);
+    if (st != SLA_OK) return st;
+    if (max_frames < f) return fail(SLA_ERR_INVALID_ARG, "max_frames = %d is below the set size %d", max_frames, f);
+    return device_status(sla::launch_lvsa_frames(p, nullptr, sets, counts, max_frames, (hipStream_t)stream),
+                         "frame set launch");
+}
+
+// slots per pair: a row takes the key blocks touched by at most two frames' sets
+static int lvsa_kmax(int Nb, int P, int frames_per_set) {
+    const long bound = 2L * frames_per_set * ((P + 63) / 64 + 1);
+    return (int)std::min<long>(Nb, bound);
+}
+
+static sla_status lvsa_shape(int B, int H, int N, int d, int block, int T, int *P) {
+    sla_status st = check_shape(B, H, N, d, block, MAX_NB_LISTS);
+    if (st != SLA_OK) return st;
+    if (T < 1 || N % T != 0) return fail(SLA_ERR_INVALID_ARG, "N = %d is not T = %d frames of equal size", N, T);
+    *P = N / T;
+    if (*P < 64) return fail(SLA_ERR_UNSUPPORTED, "frames of %d tokens: at least 64 are needed", *P);
+    return SLA_OK;
+}
+
+sla_status sla_lvsa_workspace_size(int B, int H, int N, int T, int C, int W, size_t *bytes) {
+    if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
+    int P, f;
+    sla_status st = lvsa_shape(B, H, N, 128, 64, T, &P);
+    if (st != SLA_OK) return st;
+    sla::LvsaParams p;
+    st = lvsa_params(T, C, W, 0, &p, &f);
+    if (st != SLA_OK) return st;
+    const int Nb = (N + 63) / 64, Np = (Nb + 1) / 2;
+    *bytes = align256(sizeof(int32_t) * 2 * (size_t)T) + align256(sizeof(uint32_t) * (size_t)Np * lvsa_kmax(Nb, P, f)) +
+             align256(sizeof(int32_t) * (size_t)Np);
+    return SLA_OK;
+}
+
+sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
+                            int B, int H, int N, int d, int block, int T, int C, int W, int step, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    int P, f;
+    sla_status st = lvsa_shape(B, H, N, d, block, T, &P);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "LVSA attention takes bf16 inputs");
+    if (out_dtype != SLA_F32 && out_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "output dtype must be F32 or BF16");
+    sla::LvsaParams p;
+    st = lvsa_params(T, C, W, step, &p, &f);
+    if (st != SLA_OK) return st;
+    size_t need = 0;
+    st = sla_lvsa_workspace_size(B, H, N, T, C, W, &need);
+    if (st != SLA_OK) return st;
+    if (!workspace) return fail(SLA_ERR_INVALID_ARG, "null workspace");
+    if (workspace_bytes < need)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int Nb = (N + 63) / 64, Np = (Nb + 1) / 2;
+    const int kmax = lvsa_kmax(Nb, P, f);
+    char *w = (char *)workspace;
+    int32_t *lohi = (int32_t *)w;
+    uint32_t *slots = (uint32_t *)(w + align256(sizeof(int32_t) * 2 * (size_t)T));
+    int32_t *pcount = (int32_t *)((char *)slots + align256(sizeof(uint32_t) * (size_t)Np * kmax));
+    st = device_status(sla::launch_lvsa_frames(p, lohi, nullptr, nullptr, 0, s), "frame window launch");
+    if (st != SLA_OK) return st;
+    st = device_status(sla::launch_lvsa_slots(p, P, N, Nb, lohi, kmax, slots, pcount, s), "slot schedule launch");
+    if (st != SLA_OK) return st;
+    sla::FusedArgs fa{};
+    fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount; fa.bcast = true; fa.fp = P;
+    fa.out = out; fa.BH = (long)B * H; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
     return device_status(sla::launch_fused16(fa, s), "fused launch");
 }

@@ -105,26 +105,44 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds,
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 
-// slot entry: key block of row 2p in the low 16 bits, of row 2p+1 in the high
-// 16 bits (0xFFFF: the pair has no second row; 0xFFFE: this row has no block
-// in the slot, its keys are masked); indices are clamped to Nb - 1
-constexpr uint32_t NO_TILE = 0xFFFEu;
+// slot entry: the half of row 2p in the low 16 bits, of row 2p+1 in the
+// high 16 bits.  A half holds a key block index in its low 12 bits (clamped
+// to Nb - 1 when used) and, in its top 4 bits, the pairs of frame parts it
+// must not score: bit 2a + c set means that the query rows of part a of the
+// query block do not see the keys of part c of the key block, where part 1
+// of a block is what follows the frame boundary inside it (blocks of tokens
+// from one frame have only part 0).  0 (the usual case): every key is seen;
+// 0xF: none, the slot is padding for this row; 0xFFFF: the pair has no
+// second row.
+constexpr uint32_t IDX_BITS = 0xFFFu;
 __device__ __forceinline__ int slot_tile(uint32_t e, int which, int Nb) {
-    return min((int)(which ? (e >> 16) : (e & 0xFFFFu)), Nb - 1);
+    return min((int)((which ? (e >> 16) : e) & IDX_BITS), Nb - 1);
 }
-// one tile serves the slot: both rows selected the block, or the second row
-// has none (no row, or no block in this slot)
-__device__ __forceinline__ bool slot_single(uint32_t e) { return (e >> 16) == (e & 0xFFFFu) || (e >> 16) >= NO_TILE; }
+// one tile serves the slot: both rows name the same block, or the second row
+// has none (no row, or padding in this slot)
+__device__ __forceinline__ bool slot_single(uint32_t e) {
+    return ((e >> 16) & IDX_BITS) == (e & IDX_BITS) || (e >> 28) == 0xFu;
+}
+// offset of the first token of the block's part 1 (a frame boundary inside
+// the block), 64 when the block lies in one frame; frames of fp >= 64 tokens
+__device__ __forceinline__ int frame_split(int blk, int fp) {
+    const int start = 64 * blk;
+    const int bnd = (start / fp + 1) * fp - start;
+    return bnd < 64 ? bnd : 64;
+}
 
 // swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
 template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
 }  // namespace
 
-template <typename T, typename S, int D, typename TO>
+// MARKS: the slots may carry frame marks (schedules from frame sets); without
+// it a half's top bits are 0 or 0xF only.
+template <typename T, typename S, int D, typename TO, bool MARKS>
 __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                          const T *__restrict__ v,
-                                                         const uint32_t *__restrict__ slots, int kc,
+                                                         const uint32_t *__restrict__ slots, int kc_max,
+                                                         const int32_t *__restrict__ pcount, int bcast, int fp,
                                                          const S *__restrict__ hhat,
                                                          const int32_t *__restrict__ mcount, int Lp,
                                                          TO *__restrict__ out, long G, int per_xcd, int N,
@@ -190,8 +208,12 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[ct][r] = 0.f;
 
-    const long pair = bh * Np + pr;
-    const uint32_t *sl = slots + pair * (long)kc;
+    // this pair's slots: a schedule per head, or one shared by all heads (bcast)
+    const long pair = bcast ? pr : bh * Np + pr;
+    const uint32_t *sl = slots + pair * (long)kc_max;
+    const int kc = pcount ? __builtin_amdgcn_readfirstlane(min(max(pcount[pair], 0), kc_max)) : kc_max;
+    // part (0 or 1) of this lane's query row within its block, for the frame marks
+    const int qpart = (MARKS && fp > 0 && 32 * qh + l32 >= frame_split(i, fp)) ? 1 : 0;
     // slot entry: tile of block A in the low half, of block B in the high half (0xFFFF: no block B)
     auto tile_a = [Nb](uint32_t e) { return slot_tile(e, 0, Nb); };
     auto tile_b = [Nb](uint32_t e) { return slot_tile(e, 1, Nb); };
@@ -293,11 +315,20 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
         }
     };
     auto softmax = [&](uint32_t e1) {
-        if ((b ? (e1 >> 16) : (e1 & 0xFFFFu)) == NO_TILE) {   // no block for this row in the slot
+        const uint32_t marks = ((b ? (e1 >> 16) : e1) >> 12) & 0xFu;
+        const int j = my_blk(e1);
+        if (marks == 0xFu) {                             // padding: no key of the slot for this row
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = NEG_INF;
+        } else if (MARKS && marks != 0u) {               // a frame boundary hides some keys
+            const int ks = fp > 0 ? frame_split(j, fp) : 64;
+            const uint32_t hide = marks >> (2 * qpart);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if ((hide >> (key >= ks ? 1 : 0)) & 1u) sacc[r] = NEG_INF;
+            }
         }
-        const int j = my_blk(e1);
         if (64 * j + 64 > N) {                           // ragged last block: keys past N score -inf
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -493,21 +524,28 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
     }
 }
 
-template <typename T, typename S, int D, typename TO>
+template <typename T, typename S, int D, typename TO, bool MARKS>
 static hipError_t launch_fused16_t(const FusedArgs &a, hipStream_t st) {
     const long G = a.BH * ((a.Nb + 1) / 2);
     const int per = (int)((G + 7) / 8);
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-    fused16_kernel<T, S, D, TO><<<(unsigned)(8L * per), 512, 0, st>>>(
-        (const T *)a.q, (const T *)a.k, (const T *)a.v, a.slots, a.kc, (const S *)a.hhat, a.mcount, a.Lp, (TO *)a.out,
-        G, per, a.N, a.Nb, sl2);
+    fused16_kernel<T, S, D, TO, MARKS><<<(unsigned)(8L * per), 512, 0, st>>>(
+        (const T *)a.q, (const T *)a.k, (const T *)a.v, a.slots, a.kc, a.pcount, a.bcast ? 1 : 0, a.fp,
+        (const S *)a.hhat, a.mcount, a.Lp, (TO *)a.out, G, per, a.N, a.Nb, sl2);
     return hipGetLastError();
 }
 
-hipError_t launch_fused16(const FusedArgs &a, hipStream_t st) {
+template <bool MARKS>
+static hipError_t launch_fused16_m(const FusedArgs &a, hipStream_t st) {
     if (a.bf16_out)
-        return a.D == 64 ? launch_fused16_t<bf16, f16, 64, bf16>(a, st) : launch_fused16_t<bf16, f16, 128, bf16>(a, st);
-    return a.D == 64 ? launch_fused16_t<bf16, f16, 64, float>(a, st) : launch_fused16_t<bf16, f16, 128, float>(a, st);
+        return a.D == 64 ? launch_fused16_t<bf16, f16, 64, bf16, MARKS>(a, st)
+                         : launch_fused16_t<bf16, f16, 128, bf16, MARKS>(a, st);
+    return a.D == 64 ? launch_fused16_t<bf16, f16, 64, float, MARKS>(a, st)
+                     : launch_fused16_t<bf16, f16, 128, float, MARKS>(a, st);
+}
+
+hipError_t launch_fused16(const FusedArgs &a, hipStream_t st) {
+    return a.fp > 0 ? launch_fused16_m<true>(a, st) : launch_fused16_m<false>(a, st);
 }
 
 }  // namespace sla

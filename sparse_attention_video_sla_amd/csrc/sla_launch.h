@@ -49,8 +49,11 @@ struct FusedArgs {
     const void *q, *k, *v;
     const uint32_t *ulist;   // [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
     const int32_t *ucount;   // [BH][ceil(Nb/2)]
-    const uint32_t *slots;   // [BH][ceil(Nb/2)][kc] slot schedule (16-bit inputs)
+    const uint32_t *slots;   // [BH][ceil(Nb/2)][kc] slot schedule (16-bit inputs), [ceil(Nb/2)][kc] with bcast
     int kc;
+    const int32_t *pcount;   // nullable: slots used per pair ([BH][ceil(Nb/2)], or [ceil(Nb/2)] with bcast)
+    bool bcast;              // one schedule shared by every head
+    int fp;                  // tokens per frame for the frame marks in the slots (0: no marks)
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere
     int Lp;
@@ -78,7 +81,16 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t st);     // float inputs
 hipError_t launch_fused16(const FusedArgs &a, hipStream_t st);   // bf16 inputs
 hipError_t launch_block_mass(const MassArgs &a, hipStream_t st);
 hipError_t launch_lists_to_slots(const int32_t *lists, const int32_t *counts, int kmax, long BH, int Nb,
-                                 uint32_t *slots, hipStream_t st);
+                                 uint32_t *slots, int32_t *pcount, hipStream_t st);
+
+// LVSA frame sets: T frames, half window W, step s, T_per, m = |G_s| = ceil(T / T_per)
+struct LvsaParams {
+    int T, W, s, Tper, m;
+};
+hipError_t launch_lvsa_frames(const LvsaParams &p, int32_t *lohi, int32_t *sets, int32_t *counts, int max_frames,
+                              hipStream_t st);
+hipError_t launch_lvsa_slots(const LvsaParams &p, int P, int N, int Nb, const int32_t *lohi, int kmax,
+                             uint32_t *slots, int32_t *pcount, hipStream_t st);
 hipError_t launch_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, hipStream_t st);
 
 }  // namespace sla

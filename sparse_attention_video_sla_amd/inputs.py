@@ -79,6 +79,46 @@ WORKLOADS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class LvsaWorkload:
+    """A long-video workload for the LVSA frame-level sets: grid (T latent
+    frames, h, w), budget C frames, half window W, denoising step."""
+    name: str
+    B: int
+    H: int
+    grid: Tuple[int, int, int]
+    d: int
+    C: int
+    W: int
+    step: int
+    seed: int
+
+    @property
+    def T(self) -> int:
+        return self.grid[0]
+
+    @property
+    def P(self) -> int:
+        return self.grid[1] * self.grid[2]
+
+    @property
+    def N(self) -> int:
+        return self.T * self.P
+
+
+# Wan2.1 1.3B at 6x its training length: 481 video frames are 121 latent
+# frames of 30 x 52 tokens (480 x 832); budget C = 21 latent frames (the
+# training length), W = 3 so that every set holds exactly C frames.
+LVSA_WORKLOADS = {
+    "wan6x": LvsaWorkload("wan2.1-1.3b-480p-6x-121x30x52-lvsa", 1, 12, (121, 30, 52), 128, 21, 3, 0, 2001),
+}
+
+
+def make_lvsa_workload(key: str, heads: Optional[int] = None) -> Inputs:
+    wl = LVSA_WORKLOADS[key]
+    return make_inputs(wl.B, heads or wl.H, wl.grid, wl.d, "bf16", False, wl.seed)
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """float32 -> nearest bfloat16 (ties to even), returned as float32 values.
     Finite inputs below the largest bfloat16 only."""

@@ -108,3 +108,30 @@ def test_pool_classify_reject(lib):
     assert lib.sla_classify(FAKE, FAKE, 1, 1, 8, 128, 0.5, 0.1, None, FAKE, None, None, None) == _lib.SLA_ERR_INVALID_ARG
     assert lib.sla_classify(FAKE, FAKE, 1, 1, 8, 128, 0.5, 0.1, FAKE, None, None, None, None) == _lib.SLA_ERR_INVALID_ARG
     assert lib.sla_classify(FAKE, FAKE, 1, 1, 2433, 128, 0.05, 0.1, FAKE, FAKE, None, None, None) == _lib.SLA_ERR_UNSUPPORTED
+
+
+def test_lvsa_plan_matches_oracle_and_rejects(lib):
+    """sla_lvsa_plan is host arithmetic: T_per, |G_s| and the set size of the
+    LVSA page's frame sets, checked against the oracle's sets."""
+    from oracle import lvsa
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    for T in (1, 3, 10, 21, 41, 121, 481):
+        for C in (4, 7, 21, 33):
+            for W in (0, 1, 3):
+                if C - (2 * W + 1) < 1:
+                    assert lib.sla_lvsa_plan(T, C, W, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) != 0
+                    continue
+                assert lib.sla_lvsa_plan(T, C, W, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
+                sets = lvsa.all_sets(T, C, W, 0)
+                assert a.value == lvsa.period(T, C, W)
+                assert b.value == len(lvsa.globals_at(T, a.value, 0))
+                assert {c.value} == {len(x) for x in sets}
+
+
+def test_lvsa_entry_points_reject_bad_shapes(lib):
+    n = ctypes.c_size_t()
+    assert lib.sla_lvsa_workspace_size(1, 1, 1000, 3, 5, 1, ctypes.byref(n)) != 0    # N % T
+    assert lib.sla_lvsa_workspace_size(1, 1, 1000, 20, 5, 1, ctypes.byref(n)) != 0   # 50-token frames
+    assert lib.sla_lvsa_workspace_size(1, 1, 1000, 10, 3, 1, ctypes.byref(n)) != 0   # C <= 2W + 1
+    assert lib.sla_lvsa_workspace_size(1, 1, 64 * 4096, 64, 21, 3, ctypes.byref(n)) != 0   # 4096 blocks
+    assert lib.sla_lvsa_workspace_size(1, 12, 188760, 121, 21, 3, ctypes.byref(n)) == 0 and n.value > 0

@@ -16,6 +16,13 @@ marginal state; the projection is folded into the state kernel).
 rocprofv3 counter summary, reported only while the kernel source matches.
 `cpu_baseline` times the CPU oracle on whole heads (by default all of them).
 
+With --lvsa it prints instead one JSON line for LVSA frame-level sparse
+attention (the LVSA page's sets A(t) = G_s U W(t)) on a long-video workload:
+Wan2.1-1.3B at 6x its training length, 121 latent frames of 30x52 tokens
+(N = 188760), H=12, d=128, budget C = 21 frames, W = 3, step 0.  A step is
+one sla_forward_lvsa call (frame sets, block schedule, attention); `value`
+counts 4*d flops per (query token, key token) pair the sets allow.
+
 With --quality it prints instead one JSON line for the mask-quality
 diagnostics (sla_block_mass + sla_mask_stats) on the same workload: the
 exact block attention mass kept by the critical, marginal and negligible
@@ -39,6 +46,7 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFMA peak"
 FUSED_SRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc", "fused16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
+LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_lvsa_wan6x_stats.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -52,15 +60,15 @@ def work(B, H, N, d, kc, kn):
     return f_comp, f_fused, pairs, marg_rows
 
 
-def fused_traffic():
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+def fused_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch of the fused kernel from a committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
     calibration), or None when the kernel source has changed since the
     counters were taken."""
     import hashlib
     import re
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
         src = open(FUSED_SRC, "rb").read()
     except OSError:
         return None
@@ -159,6 +167,91 @@ def run_quality(args, wl):
     print(json.dumps(line), flush=True)
 
 
+def run_lvsa(args):
+    import numpy as np
+    import torch
+    import sparse_attention_video_sla_amd as sla
+    from sparse_attention_video_sla_amd import _lib
+    from sparse_attention_video_sla_amd.inputs import LVSA_WORKLOADS, make_lvsa_workload
+
+    wl = LVSA_WORKLOADS["wan6x"]
+    inp = make_lvsa_workload("wan6x")
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    B, H, N, d = q.shape
+    T, P = wl.T, wl.P
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(sla.lvsa_workspace_size(B, H, N, T, wl.C, wl.W), dtype=torch.uint8, device=dev)
+    t_per, n_glob, per_set = sla.lvsa_plan(T, wl.C, wl.W)
+
+    def step():
+        sla.forward_lvsa(q, k, v, T, wl.C, wl.W, wl.step, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L = _lib.load()
+    L.sla_set_stage_timing(1)
+    ms_buf = (ctypes.c_float * 5)()
+    calls = ctypes.c_int()
+    L.sla_stage_times(ms_buf, ctypes.byref(calls))
+    for _ in range(args.steps):
+        step()
+    _lib.check(L.sla_stage_times(ms_buf, ctypes.byref(calls)))
+    L.sla_set_stage_timing(0)
+    stage_ms = {name: ms_buf[i] / max(calls.value, 1) for i, name in enumerate(_lib.STAGES)}
+
+    sets, cnt = sla.lvsa_sets(T, wl.C, wl.W, wl.step)
+    frames_seen = int(cnt.sum().item())                  # sum over query frames of |A(t)|
+    pairs = frames_seen * P * P                          # (query token, key token) pairs per head
+    flops = 4.0 * d * pairs * B * H
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    t_fused = stage_ms["fused"] * 1e-3
+    achieved = flops / t_fused / 1e12 if t_fused > 0 else 0.0
+    dense = 4.0 * d * N * N * B * H
+    line = {
+        "metric": "effective TFLOP/s + ms/call of LVSA frame-level sparse attention fwd, Wan2.1-1.3B 6x length, %MFMA peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; local sinusoid Q/K + noise, V ~ N(0,1))",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64, "T": T, "P": P, "C": wl.C,
+                   "W": wl.W, "step": wl.step, "T_per": t_per, "globals": n_glob, "frames_per_set": per_set,
+                   "density_vs_dense": round(flops / dense, 5), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(LVSA_TRAFFIC_FILE),
+                     "kernel": "fused16_kernel<bf16,f16,128,float,frame marks>", "flops_per_launch": flops,
+                     "avg_launch_ms": round(stage_ms["fused"], 4)},
+        "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
+    }
+    if not args.no_cpu:
+        from oracle import lvsa as olv
+        from sparse_attention_video_sla_amd.inputs import sample_query_blocks
+        Nb = -(-N // 64)
+        rows = sample_query_blocks(B, H, Nb, max(1, args.cpu_heads or 24), 13)
+        t0 = time.perf_counter()
+        ref = olv.attention_lvsa(inp.q, inp.k, inp.v, T, P, wl.C, wl.W, wl.step,
+                                 rows=[tuple(int(x) for x in r) for r in rows])
+        t = time.perf_counter() - t0
+        o = out.reshape(B * H, N, d)
+        err = 0.0
+        for x, (bh, i) in enumerate(rows):
+            r1 = min(N, 64 * (i + 1))
+            err = max(err, float(np.abs(o[bh, 64 * i:r1].double().cpu().numpy() - ref[x, :r1 - 64 * i]).max()))
+        f_rows = 4.0 * d * 64 * per_set * P * len(rows)
+        line["cpu_baseline"] = {"value": round(f_rows / t / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
+                                "kind": "oracle", "seconds": round(t, 3),
+                                "sample": "%d query blocks of 64 tokens (fp64), each against the %d frames of its set"
+                                          % (len(rows), per_set),
+                                "max_abs_diff_vs_gpu": err}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +263,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quality", action="store_true", help="mask-quality diagnostics line instead of the forward line")
+    ap.add_argument("--lvsa", action="store_true", help="LVSA frame-level sparse attention line (long-video workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
@@ -182,6 +276,9 @@ def main():
     from sparse_attention_video_sla_amd import _lib
     from sparse_attention_video_sla_amd.inputs import WORKLOADS, make_workload
 
+    if args.lvsa:
+        run_lvsa(args)
+        return
     wl = WORKLOADS[args.workload]
     if args.quality:
         run_quality(args, wl)

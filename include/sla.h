@@ -197,7 +197,9 @@ sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int 
  * time of a call.  sla_stage_times waits for the recorded
  * events, writes the summed milliseconds per stage to ms[0..4] and the number
  * of calls summed to *calls, and forgets them.  Events are created on first
- * use and kept per thread.  Disabled by default. */
+ * use and kept per thread.  Disabled by default.  sla_forward_lists and
+ * sla_forward_lvsa calls are recorded too: stage 1 is building their block
+ * schedule, stage 4 their attention kernel, the other stages zero. */
 #define SLA_NUM_STAGES 5
 sla_status sla_set_stage_timing(int enable);
 sla_status sla_stage_times(float *ms, int *calls);

@@ -131,6 +131,24 @@ void mark_stage(StageEvents *ev, int i, int end, hipStream_t s) {
     if (ev && (*ev)[2 * i + end]) hipEventRecord((*ev)[2 * i + end], s);
 }
 
+// The event set of a new call while timing is on, else nullptr.
+StageEvents *timed_call() {
+    if (!g_timer.on) return nullptr;
+    StageEvents set;
+    for (auto &e : set) e = g_timer.next();
+    g_timer.calls.push_back(set);
+    return &g_timer.calls.back();
+}
+
+// Calls over a given block schedule: stage 1 is building the schedule, stage
+// 4 the attention kernel; pool, states and assembly do not run (zero time).
+void mark_unused_stages(StageEvents *ev, hipStream_t s) {
+    for (int i : {0, 2, 3}) {
+        mark_stage(ev, i, 0, s);
+        mark_stage(ev, i, 1, s);
+    }
+}
+
 // The side stream of a device (default priority, non-blocking) and the two
 // events that fork it from and join it to the caller's stream.  Created on
 // first use and kept until the process ends.  The fork is recorded and waited
@@ -224,13 +242,20 @@ sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dt
     const int Nb = (N + 63) / 64;
     uint32_t *slots = (uint32_t *)workspace;
     int32_t *pcount = (int32_t *)((char *)workspace + align256(sizeof(uint32_t) * (size_t)BH * ((Nb + 1) / 2) * kmax));
+    StageEvents *ev = timed_call();
+    mark_unused_stages(ev, s);
+    mark_stage(ev, 1, 0, s);
     st = device_status(sla::launch_lists_to_slots(lists, counts, kmax, BH, Nb, slots, pcount, s), "slot schedule launch");
+    mark_stage(ev, 1, 1, s);
     if (st != SLA_OK) return st;
     sla::FusedArgs fa{};
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
-    return device_status(sla::launch_fused16(fa, s), "fused launch");
+    mark_stage(ev, 4, 0, s);
+    st = device_status(sla::launch_fused16(fa, s), "fused launch");
+    mark_stage(ev, 4, 1, s);
+    return st;
 }
 
 // ---- LVSA frame-level sets --------------------------------------------------
@@ -324,15 +349,22 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
     int32_t *lohi = (int32_t *)w;
     uint32_t *slots = (uint32_t *)(w + align256(sizeof(int32_t) * 2 * (size_t)T));
     int32_t *pcount = (int32_t *)((char *)slots + align256(sizeof(uint32_t) * (size_t)Np * kmax));
+    StageEvents *ev = timed_call();
+    mark_unused_stages(ev, s);
+    mark_stage(ev, 1, 0, s);
     st = device_status(sla::launch_lvsa_frames(p, lohi, nullptr, nullptr, 0, s), "frame window launch");
-    if (st != SLA_OK) return st;
-    st = device_status(sla::launch_lvsa_slots(p, P, N, Nb, lohi, kmax, slots, pcount, s), "slot schedule launch");
+    if (st == SLA_OK)
+        st = device_status(sla::launch_lvsa_slots(p, P, N, Nb, lohi, kmax, slots, pcount, s), "slot schedule launch");
+    mark_stage(ev, 1, 1, s);
     if (st != SLA_OK) return st;
     sla::FusedArgs fa{};
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount; fa.bcast = true; fa.fp = P;
     fa.out = out; fa.BH = (long)B * H; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
-    return device_status(sla::launch_fused16(fa, s), "fused launch");
+    mark_stage(ev, 4, 0, s);
+    st = device_status(sla::launch_fused16(fa, s), "fused launch");
+    mark_stage(ev, 4, 1, s);
+    return st;
 }
 
 sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
@@ -436,13 +468,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     int32_t *crit = (int32_t *)(ws + L.crit);
     int32_t *mcount = (int32_t *)(ws + L.mcount);
 
-    StageEvents *ev = nullptr;
-    if (g_timer.on) {
-        StageEvents set;
-        for (auto &e : set) e = g_timer.next();
-        g_timer.calls.push_back(set);
-        ev = &g_timer.calls.back();
-    }
+    StageEvents *ev = timed_call();
     // block states on the side stream, concurrent with pool and classify; a
     // return after the fork still makes the caller's stream wait for the join
     SideStream *ss = nullptr;

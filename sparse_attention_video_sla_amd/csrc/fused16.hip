@@ -317,7 +317,8 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
     auto softmax = [&](uint32_t e1) {
         const uint32_t marks = ((b ? (e1 >> 16) : e1) >> 12) & 0xFu;
         const int j = my_blk(e1);
-        if (marks == 0xFu) {                             // padding: no key of the slot for this row
+        if (marks == 0xFu) [[unlikely]] {               // padding: no key of the slot for this row
+            __builtin_amdgcn_sched_barrier(0);           // (a branch, not 16 selects on every slot)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = NEG_INF;
         } else if (MARKS && marks != 0u) {               // a frame boundary hides some keys

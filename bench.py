@@ -23,6 +23,12 @@ Wan2.1-1.3B at 6x its training length, 121 latent frames of 30x52 tokens
 one sla_forward_lvsa call (frame sets, block schedule, attention); `value`
 counts 4*d flops per (query token, key token) pair the sets allow.
 
+With --sta it prints instead one JSON line for sliding tile attention (the
+VORTA page's STA: a 3D window kept by whole tiles) on a HunyuanVideo-sized
+latent: 30x48x80 tokens (N = 115200, tile-major), tiles (6, 8, 8), window
+(18, 27, 24), H=24, d=128; `value` counts 4*d flops per kept (query, key)
+pair.
+
 With --quality it prints instead one JSON line for the mask-quality
 diagnostics (sla_block_mass + sla_mask_stats) on the same workload: the
 exact block attention mass kept by the critical, marginal and negligible
@@ -47,6 +53,7 @@ METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFM
 FUSED_SRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc", "fused16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
 LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_lvsa_wan6x_stats.md")
+STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_sta_hunyuan_stats.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -252,6 +259,106 @@ def run_lvsa(args):
     print(json.dumps(line), flush=True)
 
 
+STA_WORKLOAD = {"name": "hunyuanvideo-30x48x80-sta", "B": 1, "H": 24, "grid": (30, 48, 80), "d": 128,
+                "tile": (6, 8, 8), "window": (18, 27, 24), "seed": 3001}
+
+
+def sta_pairs(grid, tile, window):
+    """(query, key) pairs the tile window keeps, per head: a product over the
+    axes of the pairs (i, j) whose tile centres differ by 2*delta*t in (-W, W]."""
+    total = 1
+    for n, t, w in zip(grid, tile, window):
+        c = 0
+        for a in range(n // t):
+            for b in range(n // t):
+                if -w < 2 * (b - a) * t <= w:
+                    c += t * t
+        total *= c
+    return total
+
+
+def run_sta(args):
+    import numpy as np
+    import torch
+    import sparse_attention_video_sla_amd as sla
+    from sparse_attention_video_sla_amd import _lib
+    from sparse_attention_video_sla_amd.inputs import make_inputs
+
+    wl = STA_WORKLOAD
+    grid, tile, window, d = wl["grid"], wl["tile"], wl["window"], wl["d"]
+    B, H = wl["B"], wl["H"]
+    N = grid[0] * grid[1] * grid[2]
+    inp = make_inputs(B, H, grid, d, "bf16", seed=wl["seed"])
+    perm = sla.sta_tile_order(grid, tile)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x[:, :, perm])).to(dev).to(torch.bfloat16)
+               for x in (inp.q, inp.k, inp.v))
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(sla.sta_workspace_size(B, H, grid, tile, window), dtype=torch.uint8, device=dev)
+
+    def step():
+        sla.forward_sta(q, k, v, grid, tile, window, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L = _lib.load()
+    L.sla_set_stage_timing(1)
+    ms_buf = (ctypes.c_float * 5)()
+    calls = ctypes.c_int()
+    L.sla_stage_times(ms_buf, ctypes.byref(calls))
+    for _ in range(args.steps):
+        step()
+    _lib.check(L.sla_stage_times(ms_buf, ctypes.byref(calls)))
+    L.sla_set_stage_timing(0)
+    stage_ms = {name: ms_buf[i] / max(calls.value, 1) for i, name in enumerate(_lib.STAGES)}
+
+    pairs = sta_pairs(grid, tile, window)
+    flops = 4.0 * d * pairs * B * H
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    t_fused = stage_ms["fused"] * 1e-3
+    achieved = flops / t_fused / 1e12 if t_fused > 0 else 0.0
+    line = {
+        "metric": "effective TFLOP/s + ms/call of sliding tile attention fwd, HunyuanVideo-sized latent, %MFMA peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; local sinusoid Q/K + noise, V ~ N(0,1)), tile-major tokens",
+        "config": {"workload": wl["name"], "B": B, "H": H, "N": N, "d": d, "block": 64, "grid": list(grid),
+                   "tile": list(tile), "window": list(window), "density_vs_dense": round(pairs / N / N, 5),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(STA_TRAFFIC_FILE),
+                     "kernel": "fused16_kernel<bf16,f16,128,float> (tile schedule)", "flops_per_launch": flops,
+                     "avg_launch_ms": round(stage_ms["fused"], 4)},
+        "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
+    }
+    if not args.no_cpu:
+        from oracle import sta as osta
+        inv = np.empty(N, np.int64)
+        inv[perm] = np.arange(N)
+        rng = np.random.default_rng(17)
+        per_head = max(1, args.cpu_heads or 200)
+        rows = [(bh, int(n)) for bh in range(B * H) for n in rng.choice(N, per_head, replace=False)]
+        t0 = time.perf_counter()
+        ref = osta.attention_sta(inp.q, inp.k, inp.v, grid, tile, window, rows=rows)
+        t = time.perf_counter() - t0
+        o = out.reshape(B * H, N, d)
+        got = np.stack([o[bh, int(inv[n])].double().cpu().numpy() for bh, n in rows])
+        keys = pairs / N
+        f_rows = 4.0 * d * keys * len(rows)
+        line["cpu_baseline"] = {"value": round(f_rows / t / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
+                                "kind": "oracle", "seconds": round(t, 3),
+                                "sample": "%d query tokens (fp64), each against its kept keys" % len(rows),
+                                "max_abs_diff_vs_gpu": float(np.abs(got - ref).max())}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +371,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quality", action="store_true", help="mask-quality diagnostics line instead of the forward line")
     ap.add_argument("--lvsa", action="store_true", help="LVSA frame-level sparse attention line (long-video workload)")
+    ap.add_argument("--sta", action="store_true", help="sliding tile attention line (HunyuanVideo-sized latent)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
@@ -278,6 +386,9 @@ def main():
 
     if args.lvsa:
         run_lvsa(args)
+        return
+    if args.sta:
+        run_sta(args)
         return
     wl = WORKLOADS[args.workload]
     if args.quality:

@@ -166,6 +166,30 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
                             int B, int H, int N, int d, int block, int T, int C, int W, int step, void *out,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Sliding tile attention (the VORTA page, "Key designs", item 1: a 3D
+ * sliding window made block-dense by tiles; linear branch off).  The grid
+ * (F, Hh, Ww) of N = F*Hh*Ww tokens is cut into tiles (tf, th, tw) that
+ * divide it, of tf*th*tw tokens, a multiple of 64; tokens are TILE-MAJOR:
+ * tiles in raster order over the tile grid, tokens in raster order inside a
+ * tile (sla_sta_tile_order gives the permutation).  On every axis a query
+ * tile keeps the key tiles whose centre (floor(i/t)*t + ceil(t/2)) lies in
+ * (c - W/2, c + W/2] of its own centre c, for the axis window W (wf, wh,
+ * ww); tiles past the grid do not exist.  Every query token of a tile
+ * attends every token of the kept tiles, one softmax, scale 1/sqrt(d).
+ *
+ * sla_sta_tile_order: host only: perm[m] = raster index (frames slowest) of
+ *   the m-th token in tile-major order; perm holds N entries.
+ * sla_forward_sta: q, k, v: [B,H,N,d] bf16, tile-major; out: [B,H,N,d] of
+ *   out_dtype (F32 or BF16), tile-major; N/64 <= 4095; workspace of
+ *   sla_sta_workspace_size() bytes, 256-byte aligned, clobbered.  The block
+ *   schedule is built in the stream and shared by every head. */
+sla_status sla_sta_tile_order(int F, int Hh, int Ww, int tf, int th, int tw, int32_t *perm);
+sla_status sla_sta_workspace_size(int B, int H, int F, int Hh, int Ww, int tf, int th, int tw, int wf, int wh, int ww,
+                                  size_t *bytes);
+sla_status sla_forward_sta(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
+                           int B, int H, int d, int block, int F, int Hh, int Ww, int tf, int th, int tw, int wf,
+                           int wh, int ww, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Mask-quality diagnostics (SLA article, section 2: a few attention weights
  * carry most of the mass; SVOO page: attention density as the share of
  * entries that covers 95 % of the cumulative attention mass).  Not part of
@@ -197,9 +221,10 @@ sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int 
  * time of a call.  sla_stage_times waits for the recorded
  * events, writes the summed milliseconds per stage to ms[0..4] and the number
  * of calls summed to *calls, and forgets them.  Events are created on first
- * use and kept per thread.  Disabled by default.  sla_forward_lists and
- * sla_forward_lvsa calls are recorded too: stage 1 is building their block
- * schedule, stage 4 their attention kernel, the other stages zero. */
+ * use and kept per thread.  Disabled by default.  sla_forward_lists,
+ * sla_forward_lvsa and sla_forward_sta calls are recorded too: stage 1 is
+ * building their block schedule, stage 4 their attention kernel, the other
+ * stages zero. */
 #define SLA_NUM_STAGES 5
 sla_status sla_set_stage_timing(int enable);
 sla_status sla_stage_times(float *ms, int *calls);

@@ -16,7 +16,7 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa",
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa", "sta_tile_order", "forward_sta",
            "block_mass", "mask_stats", "version",
            "SlaError"]
 
@@ -193,6 +193,48 @@ def forward_lvsa(q, k, v, T: int, C: int, W: int, step: int, out_dtype=None, out
 def lvsa_workspace_size(B: int, H: int, N: int, T: int, C: int, W: int) -> int:
     n = ctypes.c_size_t()
     _lib.check(_lib.load().sla_lvsa_workspace_size(B, H, N, T, C, W, ctypes.byref(n)))
+    return n.value
+
+
+def sta_tile_order(grid, tile):
+    """numpy int32 [N]: perm[m] = raster index of the m-th token in the
+    tile-major order sla_forward_sta takes (host arithmetic)."""
+    import numpy as np
+    F, Hh, Ww = grid
+    perm = np.empty(F * Hh * Ww, dtype=np.int32)
+    _lib.check(_lib.load().sla_sta_tile_order(F, Hh, Ww, *tile, perm.ctypes.data))
+    return perm
+
+
+def forward_sta(q, k, v, grid, tile, window, out_dtype=None, out=None, workspace=None, block: int = 64):
+    """Sliding tile attention (linear branch off) over q, k, v [B, H, N, d]
+    in tile-major order (sta_tile_order); grid (F, Hh, Ww), tile and window
+    per axis.  Returns out [B, H, N, d] in the same order."""
+    torch = _torch()
+    _check_gpu(q, k, v)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one shape and dtype")
+    B, H, N, d = q.shape
+    if N != grid[0] * grid[1] * grid[2]:
+        raise ValueError("N must equal F * Hh * Ww")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_code = _lib.SLA_F32 if out_dtype == torch.float32 else _dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    L = _lib.load()
+    n = ctypes.c_size_t()
+    _lib.check(L.sla_sta_workspace_size(B, H, *grid, *tile, *window, ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(L.sla_forward_sta(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), out_code, B, H, d, block,
+                                 *grid, *tile, *window, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                 _stream_ptr(q.device)))
+    return out
+
+
+def sta_workspace_size(B: int, H: int, grid, tile, window) -> int:
+    n = ctypes.c_size_t()
+    _lib.check(_lib.load().sla_sta_workspace_size(B, H, *grid, *tile, *window, ctypes.byref(n)))
     return n.value
 
 

@@ -367,6 +367,107 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
     return st;
 }
 
+// ---- STA tiles -----------------------------------------------------------
+
+struct StaShape {
+    sla::StaParams p;
+    int N, Nb, kmax;
+};
+
+static sla_status sta_shape(int F, int Hh, int Ww, int tf, int th, int tw, int wf, int wh, int ww, StaShape *o) {
+    if (F < 1 || Hh < 1 || Ww < 1) return fail(SLA_ERR_INVALID_ARG, "grid must be >= 1 on every axis (got %d, %d, %d)", F, Hh, Ww);
+    if (tf < 1 || th < 1 || tw < 1 || F % tf || Hh % th || Ww % tw)
+        return fail(SLA_ERR_INVALID_ARG, "tiles (%d, %d, %d) must divide the grid (%d, %d, %d)", tf, th, tw, F, Hh, Ww);
+    if (wf < 1 || wh < 1 || ww < 1) return fail(SLA_ERR_INVALID_ARG, "windows must be >= 1 (got %d, %d, %d)", wf, wh, ww);
+    const long vol = (long)tf * th * tw;
+    if (vol % 64) return fail(SLA_ERR_UNSUPPORTED, "a tile of %ld tokens is not whole 64-token blocks", vol);
+    const long N = (long)F * Hh * Ww;
+    if (N > 64L * MAX_NB_LISTS) return fail(SLA_ERR_UNSUPPORTED, "N = %ld gives more than %d blocks", N, MAX_NB_LISTS);
+    sla::StaParams &p = o->p;
+    p.tf = tf; p.th = th; p.tw = tw; p.wf = wf; p.wh = wh; p.ww = ww;
+    p.gf = F / tf; p.gh = Hh / th; p.gw = Ww / tw; p.vol = (int)vol;
+    p.rf = std::min(wf / (2 * tf) + 1, p.gf);
+    p.rh = std::min(wh / (2 * th) + 1, p.gh);
+    p.rw = std::min(ww / (2 * tw) + 1, p.gw);
+    // kept tile offsets per axis: 2*delta*t in (-W, W]
+    auto count = [](int t, int W, int r) {
+        int c = 0;
+        for (int d = -r; d <= r; ++d) c += (2 * d * t > -W && 2 * d * t <= W);
+        return c;
+    };
+    const long tiles = (long)count(tf, wf, p.rf) * count(th, wh, p.rh) * count(tw, ww, p.rw);
+    o->N = (int)N;
+    o->Nb = (int)(N / 64);
+    o->kmax = (int)std::max<long>(1, std::min<long>(o->Nb, tiles * (vol / 64)));
+    return SLA_OK;
+}
+
+sla_status sla_sta_tile_order(int F, int Hh, int Ww, int tf, int th, int tw, int32_t *perm) {
+    if (!perm) return fail(SLA_ERR_INVALID_ARG, "perm must not be NULL");
+    if (F < 1 || Hh < 1 || Ww < 1 || tf < 1 || th < 1 || tw < 1 || F % tf || Hh % th || Ww % tw)
+        return fail(SLA_ERR_INVALID_ARG, "tiles (%d, %d, %d) must divide the grid (%d, %d, %d)", tf, th, tw, F, Hh, Ww);
+    const int gh = Hh / th, gw = Ww / tw;
+    long m = 0;
+    for (int gf_ = 0; gf_ < F / tf; ++gf_)
+        for (int gh_ = 0; gh_ < gh; ++gh_)
+            for (int gw_ = 0; gw_ < gw; ++gw_)
+                for (int f = 0; f < tf; ++f)
+                    for (int h = 0; h < th; ++h)
+                        for (int w = 0; w < tw; ++w)
+                            perm[m++] = (int32_t)(((long)(gf_ * tf + f) * Hh + gh_ * th + h) * Ww + gw_ * tw + w);
+    return SLA_OK;
+}
+
+sla_status sla_sta_workspace_size(int B, int H, int F, int Hh, int Ww, int tf, int th, int tw, int wf, int wh, int ww,
+                                  size_t *bytes) {
+    if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
+    if (B < 1 || H < 1) return fail(SLA_ERR_INVALID_ARG, "B, H must be >= 1 (got %d, %d)", B, H);
+    StaShape sh;
+    sla_status st = sta_shape(F, Hh, Ww, tf, th, tw, wf, wh, ww, &sh);
+    if (st != SLA_OK) return st;
+    const size_t Np = (size_t)(sh.Nb + 1) / 2;
+    *bytes = align256(sizeof(uint32_t) * Np * sh.kmax) + align256(sizeof(int32_t) * Np);
+    return SLA_OK;
+}
+
+sla_status sla_forward_sta(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
+                           int B, int H, int d, int block, int F, int Hh, int Ww, int tf, int th, int tw, int wf,
+                           int wh, int ww, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    StaShape sh;
+    sla_status st = sta_shape(F, Hh, Ww, tf, th, tw, wf, wh, ww, &sh);
+    if (st != SLA_OK) return st;
+    st = check_shape(B, H, sh.N, d, block, MAX_NB_LISTS);
+    if (st != SLA_OK) return st;
+    if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "sliding tile attention takes bf16 inputs");
+    if (out_dtype != SLA_F32 && out_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "output dtype must be F32 or BF16");
+    size_t need = 0;
+    st = sla_sta_workspace_size(B, H, F, Hh, Ww, tf, th, tw, wf, wh, ww, &need);
+    if (st != SLA_OK) return st;
+    if (!workspace) return fail(SLA_ERR_INVALID_ARG, "null workspace");
+    if (workspace_bytes < need)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int Np = (sh.Nb + 1) / 2;
+    uint32_t *slots = (uint32_t *)workspace;
+    int32_t *pcount = (int32_t *)((char *)workspace + align256(sizeof(uint32_t) * (size_t)Np * sh.kmax));
+    StageEvents *ev = timed_call();
+    mark_unused_stages(ev, s);
+    mark_stage(ev, 1, 0, s);
+    st = device_status(sla::launch_sta_slots(sh.p, sh.Nb, sh.kmax, slots, pcount, s), "slot schedule launch");
+    mark_stage(ev, 1, 1, s);
+    if (st != SLA_OK) return st;
+    sla::FusedArgs fa{};
+    fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = sh.kmax; fa.pcount = pcount; fa.bcast = true;
+    fa.out = out; fa.BH = (long)B * H; fa.N = sh.N; fa.Nb = sh.Nb; fa.D = d;
+    fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
+    mark_stage(ev, 4, 0, s);
+    st = device_status(sla::launch_fused16(fa, s), "fused launch");
+    mark_stage(ev, 4, 1, s);
+    return st;
+}
+
 sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
                           float *mass, void *stream) {
     if (!q || !k || !mass) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");

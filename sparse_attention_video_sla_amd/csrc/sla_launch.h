@@ -89,6 +89,12 @@ struct LvsaParams {
 };
 hipError_t launch_lvsa_frames(const LvsaParams &p, int32_t *lohi, int32_t *sets, int32_t *counts, int max_frames,
                               hipStream_t st);
+// STA tiles: tile sizes, windows, tile grid, tile volume and the largest
+// |delta| per axis worth testing (2*delta*t <= W)
+struct StaParams {
+    int tf, th, tw, wf, wh, ww, gf, gh, gw, vol, rf, rh, rw;
+};
+hipError_t launch_sta_slots(const StaParams &p, int Nb, int kmax, uint32_t *slots, int32_t *pcount, hipStream_t st);
 hipError_t launch_lvsa_slots(const LvsaParams &p, int P, int N, int Nb, const int32_t *lohi, int kmax,
                              uint32_t *slots, int32_t *pcount, hipStream_t st);
 hipError_t launch_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, hipStream_t st);

@@ -135,3 +135,20 @@ def test_lvsa_entry_points_reject_bad_shapes(lib):
     assert lib.sla_lvsa_workspace_size(1, 1, 1000, 10, 3, 1, ctypes.byref(n)) != 0   # C <= 2W + 1
     assert lib.sla_lvsa_workspace_size(1, 1, 64 * 4096, 64, 21, 3, ctypes.byref(n)) != 0   # 4096 blocks
     assert lib.sla_lvsa_workspace_size(1, 12, 188760, 121, 21, 3, ctypes.byref(n)) == 0 and n.value > 0
+
+
+def test_sta_tile_order_matches_oracle_and_shapes_are_checked(lib):
+    """sla_sta_tile_order is host arithmetic: the tile-major permutation,
+    against the oracle's; the STA entry points reject bad shapes on the host."""
+    import numpy as np
+    from oracle import sta
+    for grid, tile in (((4, 6, 8), (2, 3, 4)), ((30, 48, 80), (6, 8, 8)), ((3, 4, 16), (1, 4, 16))):
+        perm = np.empty(grid[0] * grid[1] * grid[2], np.int32)
+        assert lib.sla_sta_tile_order(*grid, *tile, perm.ctypes.data) == 0
+        assert np.array_equal(perm, sta.tile_order(grid, tile))
+    n = ctypes.c_size_t()
+    assert lib.sla_sta_workspace_size(1, 1, 30, 48, 80, 6, 8, 8, 18, 27, 24, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.sla_sta_workspace_size(1, 1, 30, 48, 80, 4, 8, 8, 18, 27, 24, ctypes.byref(n)) != 0   # 4 does not divide 30
+    assert lib.sla_sta_workspace_size(1, 1, 30, 48, 80, 6, 8, 5, 18, 27, 24, ctypes.byref(n)) != 0   # 5 does not divide 80
+    assert lib.sla_sta_workspace_size(1, 1, 6, 6, 6, 3, 3, 3, 18, 27, 24, ctypes.byref(n)) != 0      # 27-token tiles
+    assert lib.sla_sta_workspace_size(1, 1, 30, 48, 80, 6, 8, 8, 0, 27, 24, ctypes.byref(n)) != 0    # empty window

@@ -116,6 +116,23 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
                        void *out, int8_t *mask_out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Gradients of sla_forward (SLA article, section 三: FlashAttention
+ * gradients for the sparse part, linear-attention gradients for the linear
+ * part).  The block labels are those sla_forward forms from the same q, k
+ * and fractions and are held fixed (no gradient flows through the
+ * selection).  q, k, v, dout: [B,H,N,d] bf16 (float32: SLA_ERR_UNSUPPORTED);
+ * w_proj [d,d] float32 as in sla_forward; dq, dk, dv: [B,H,N,d] float32
+ * outputs, dw: [d,d] float32 output (summed over batch and heads).  The call
+ * runs the forward pass again inside (labels, lists, marginal states, the
+ * sparse output and its log-sum-exp), then the gradient kernels.  Workspace:
+ * sla_backward_workspace_size() bytes, 256-byte aligned, clobbered. */
+sla_status sla_backward_workspace_size(int B, int H, int N, int d, int block, double crit_frac, double negl_frac,
+                                       size_t *bytes);
+sla_status sla_backward(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                        sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                        double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* Sparse attention over block lists given by the caller, with the linear
  * branch off (a mask source other than the scores, e.g. the LVSA page's
  * frame-level sets A(t) = G_s U W(t) turned into key blocks; block-sparse

@@ -16,7 +16,7 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa", "sta_tile_order", "forward_sta",
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa", "sta_tile_order", "forward_sta", "backward",
            "block_mass", "mask_stats", "version",
            "SlaError"]
 
@@ -235,6 +235,39 @@ def forward_sta(q, k, v, grid, tile, window, out_dtype=None, out=None, workspace
 def sta_workspace_size(B: int, H: int, grid, tile, window) -> int:
     n = ctypes.c_size_t()
     _lib.check(_lib.load().sla_sta_workspace_size(B, H, *grid, *tile, *window, ctypes.byref(n)))
+    return n.value
+
+
+def backward(q, k, v, w, dout, crit_frac: float = 0.05, negl_frac: float = 0.10, workspace=None, block: int = 64):
+    """Gradients (dq, dk, dv [B, H, N, d] float32, dw [d, d] float32) of
+    forward(q, k, v, w, crit_frac, negl_frac) for the output gradient dout,
+    with the block labels held fixed.  bf16 inputs."""
+    torch = _torch()
+    _check_gpu(q, k, v, w, dout)
+    if not (q.shape == k.shape == v.shape == dout.shape) or not (q.dtype == k.dtype == v.dtype == dout.dtype):
+        raise ValueError("q, k, v, dout must have one shape and dtype")
+    B, H, N, d = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (d, d):
+        raise ValueError("w must be float32 [d, d]")
+    L = _lib.load()
+    n = ctypes.c_size_t()
+    _lib.check(L.sla_backward_workspace_size(B, H, N, d, block, crit_frac, negl_frac, ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    dw = torch.empty((d, d), dtype=torch.float32, device=q.device)
+    _lib.check(L.sla_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(), dout.data_ptr(), _dtype_code(q),
+                              B, H, N, d, block, crit_frac, negl_frac, _lib.SLA_PHI_SOFTMAX, dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), dw.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                              _stream_ptr(q.device)))
+    return dq, dk, dv, dw
+
+
+def backward_workspace_size(B: int, H: int, N: int, d: int, crit_frac: float = 0.05, negl_frac: float = 0.10) -> int:
+    n = ctypes.c_size_t()
+    _lib.check(_lib.load().sla_backward_workspace_size(B, H, N, d, 64, crit_frac, negl_frac, ctypes.byref(n)))
     return n.value
 
 

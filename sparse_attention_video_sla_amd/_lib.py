@@ -19,7 +19,8 @@ SLA_PHI_SOFTMAX = 0
 EXPORTS = ("sla_version", "sla_counts", "sla_workspace_size", "sla_pool", "sla_classify",
            "sla_forward", "sla_lists_workspace_size", "sla_forward_lists", "sla_lvsa_plan", "sla_lvsa_sets",
            "sla_lvsa_workspace_size", "sla_forward_lvsa", "sla_sta_tile_order",
-           "sla_sta_workspace_size", "sla_forward_sta", "sla_block_mass", "sla_mask_stats", "sla_set_stage_timing", "sla_stage_times",
+           "sla_sta_workspace_size", "sla_forward_sta", "sla_backward_workspace_size",
+           "sla_backward", "sla_block_mass", "sla_mask_stats", "sla_set_stage_timing", "sla_stage_times",
            "sla_last_error")
 STAGES = ("pool", "classify", "state", "assemble", "fused")
 
@@ -74,6 +75,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.sla_sta_workspace_size.argtypes = [I] * 11 + [ctypes.POINTER(SZ)]
     L.sla_forward_sta.restype = I
     L.sla_forward_sta.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P]
+    D_ = ctypes.c_double
+    L.sla_backward_workspace_size.restype = I
+    L.sla_backward_workspace_size.argtypes = [I, I, I, I, I, D_, D_, ctypes.POINTER(SZ)]
+    L.sla_backward.restype = I
+    L.sla_backward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D_, D_, I, P, P, P, P, P, SZ, P]
     L.sla_block_mass.restype = I
     L.sla_block_mass.argtypes = [P, P, I, I, I, I, I, I, P, P]
     L.sla_mask_stats.restype = I

@@ -539,10 +539,13 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
     return device_status(sla::launch_classify(a, (hipStream_t)stream), "classify launch");
 }
 
-sla_status sla_forward(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
-                       sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
-                       double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+// The forward pass; with lse_out the fused kernel also writes each row's
+// log-sum-exp, and with linear_off it leaves the linear branch out of `out`
+// (the states and the marginal sums are still formed), as the backward needs.
+static sla_status forward_impl(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
+                               sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                               double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *workspace,
+                               size_t workspace_bytes, void *stream, float *lse_out, bool linear_off) {
     if (!q || !k || !v || !w_proj || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
     sla_status st = check_shape(B, H, N, d, block);
     if (st != SLA_OK) return st;
@@ -637,12 +640,104 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
     sla::FusedArgs fa{};
     fa.q = q; fa.k = k; fa.v = v; fa.ulist = (const uint32_t *)(ws + L.ulist);
     fa.ucount = (const int32_t *)(ws + L.ucount); fa.slots = (const uint32_t *)(ws + L.slots); fa.kc = kc;
-    fa.hhat = ws + L.hhat; fa.mcount = states ? mcount : nullptr; fa.Lp = L.Lp;
-    fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
+    fa.hhat = ws + L.hhat; fa.mcount = states && !linear_off ? mcount : nullptr; fa.Lp = L.Lp;
+    fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d; fa.lse = lse_out;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;
     st = device_status(f32 ? sla::launch_fused(fa, s) : sla::launch_fused16(fa, s), "fused launch");
     mark_stage(ev, 4, 1, s);
     return st;
+}
+
+sla_status sla_forward(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
+                       sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                       double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return forward_impl(q, k, v, w_proj, in_dtype, out_dtype, B, H, N, d, block, crit_frac, negl_frac, phi, out,
+                        mask_out, workspace, workspace_bytes, stream, nullptr, false);
+}
+
+// ---- backward ----------------------------------------------------------------
+
+struct BwdLayout {
+    size_t fwd, o_s, lse, dbuf, tlist, tcnt, margT, unit, dhrow, dhs, total;
+};
+
+static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_frac, double negl_frac,
+                             BwdLayout *o, Layout *L, int *kc, int *kn) {
+    sla_status st = check_shape(B, H, N, d, block);
+    if (st != SLA_OK) return st;
+    const int Nb = (N + 63) / 64;
+    st = counts_impl(Nb, crit_frac, negl_frac, kc, kn);
+    if (st != SLA_OK) return st;
+    *L = make_layout(B, H, N, d, false, *kc, *kn);
+    const size_t BH = (size_t)B * H;
+    size_t off = align256(L->total);
+    auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+    o->fwd = 0;
+    o->o_s = take(sizeof(float) * BH * N * d);
+    o->lse = take(sizeof(float) * BH * N);
+    o->dbuf = take(sizeof(float) * BH * N);
+    o->tlist = take(sizeof(uint16_t) * BH * Nb * Nb);
+    o->tcnt = take(sizeof(int32_t) * BH * Nb);
+    o->margT = take(sizeof(float) * BH * Nb * L->Nbc);
+    o->unit = take(sizeof(int32_t) * BH * Nb);
+    o->dhrow = take(sizeof(float) * BH * L->Nbc * L->Lp);
+    o->dhs = take(sizeof(float) * BH * Nb * L->Lp);
+    o->total = off;
+    return SLA_OK;
+}
+
+sla_status sla_backward_workspace_size(int B, int H, int N, int d, int block, double crit_frac, double negl_frac,
+                                       size_t *bytes) {
+    if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
+    BwdLayout o;
+    Layout L;
+    int kc, kn;
+    sla_status st = bwd_layout(B, H, N, d, block, crit_frac, negl_frac, &o, &L, &kc, &kn);
+    if (st != SLA_OK) return st;
+    *bytes = o.total;
+    return SLA_OK;
+}
+
+sla_status sla_backward(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                        sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                        double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !w_proj || !dout || !dq || !dk || !dv || !dw)
+        return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs");
+    if (phi != SLA_PHI_SOFTMAX) return fail(SLA_ERR_UNSUPPORTED, "feature map %d not supported", (int)phi);
+    BwdLayout o;
+    Layout L;
+    int kc, kn;
+    sla_status st = bwd_layout(B, H, N, d, block, crit_frac, negl_frac, &o, &L, &kc, &kn);
+    if (st != SLA_OK) return st;
+    if (!workspace) return fail(SLA_ERR_INVALID_ARG, "null workspace");
+    if (workspace_bytes < o.total)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, o.total);
+    if (((uintptr_t)workspace & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    char *ws = (char *)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    const int Nb = (N + 63) / 64;
+    float *o_s = (float *)(ws + o.o_s), *lse = (float *)(ws + o.lse);
+    // the forward again: labels, critical lists, marginal states, and the
+    // sparse output with its log-sum-exp
+    st = forward_impl(q, k, v, w_proj, SLA_BF16, SLA_F32, B, H, N, d, block, crit_frac, negl_frac, phi, o_s, nullptr,
+                      ws, L.total, stream, lse, true);
+    if (st != SLA_OK) return st;
+    sla::BackwardArgs a{};
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.w = w_proj; a.o_s = o_s; a.lse = lse;
+    a.crit = (const int32_t *)(ws + L.crit); a.kc = kc; a.mask = (const int8_t *)(ws + L.mask);
+    a.hhat = ws + L.hhat; a.mcount = (const int32_t *)(ws + L.mcount);
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbuf = (float *)(ws + o.dbuf);
+    a.tlist = (uint16_t *)(ws + o.tlist); a.tcnt = (int32_t *)(ws + o.tcnt);
+    a.margT = (float *)(ws + o.margT); a.unit = (int32_t *)(ws + o.unit);
+    a.dhrow = (float *)(ws + o.dhrow); a.dhs = (float *)(ws + o.dhs);
+    a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Lp = L.Lp; a.D = d;
+    st = device_status(sla::launch_backward_sparse(a, s), "backward (sparse) launch");
+    if (st != SLA_OK) return st;
+    if (kc + kn < Nb) return device_status(sla::launch_backward_linear(a, s), "backward (linear) launch");
+    return device_status(sla::launch_zero(dw, (long)d * d, s), "backward launch");
 }
 
 }  // extern "C"

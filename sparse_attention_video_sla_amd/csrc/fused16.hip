@@ -55,6 +55,7 @@
 // takes a contiguous run of (head, pair).
 #include "sla_device.h"
 #include "sla_launch.h"
+#include "tile_common.h"
 
 #include <type_traits>
 
@@ -71,39 +72,6 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float
     v4<bf16> v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
     __builtin_memcpy(p, &v, sizeof(v));
 }
-
-// Workgroup barrier that waits for this wave's LDS (and scalar) traffic
-// only: global loads issued before it stay in flight.  The wait goes through
-// the builtin so that the compiler's own wait placement knows about it; the
-// memory clobber keeps the compiler from moving memory accesses across the
-// barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-}
-
-// maximum that propagates NaN instead of quieting it (v_maximum3_f32 on
-// gfx950): it takes MFMA results without canonicalising them first
-__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
-// max and sum across the two 32-lane halves of the wave
-__device__ __forceinline__ float half_swap_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-
-
-// 16 bytes per lane from a buffer into LDS at lds + 16 * lane (lds is wave-uniform)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
 
 // slot entry: the half of row 2p in the low 16 bits, of row 2p+1 in the
 // high 16 bits.  A half holds a key block index in its low 12 bits (clamped
@@ -131,9 +99,6 @@ __device__ __forceinline__ int frame_split(int blk, int fp) {
     return bnd < 64 ? bnd : 64;
 }
 
-// swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
-template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-
 }  // namespace
 
 // MARKS: the slots may carry frame marks (schedules from frame sets); without
@@ -145,8 +110,8 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
                                                          const int32_t *__restrict__ pcount, int bcast, int fp,
                                                          const S *__restrict__ hhat,
                                                          const int32_t *__restrict__ mcount, int Lp,
-                                                         TO *__restrict__ out, long G, int per_xcd, int N,
-                                                         int Nb, float sl2) {
+                                                         TO *__restrict__ out, float *__restrict__ lse, long G,
+                                                         int per_xcd, int N, int Nb, float sl2) {
     static_assert(__is_same(T, bf16), "bf16 inputs");
     constexpr int TILE = 64 * D;                         // elements of one tile (no padding)
     constexpr int NB1 = D / 32;                          // 1 KB loads per kh = 0 wave per tile
@@ -458,6 +423,9 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
         const float ao = (mm == NEG_INF) ? 0.f : fast_exp2(mo - mm);
         const float lt = l * as + lo * ao;
         const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+        // log-sum-exp of the row's sparse softmax in the kernel's log2 units
+        // (P = exp2(s * log2(e) / sqrt(d) - lse)), +inf for a row with no key
+        if (lse && kh == 0 && hh == 0 && qvalid) lse[bh * N + qrow] = lt > 0.f ? mm + __log2f(lt) : __builtin_inff();
 #pragma unroll
         for (int t = 0; t < NCH; ++t)
 #pragma unroll
@@ -468,6 +436,7 @@ __global__ __launch_bounds__(512, 1) void fused16_kernel(const T *__restrict__ q
                     mine[t][4 * g + e] = (mine[t][4 * g + e] * as + y[e] * ao) * inv;
             }
     }
+    if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * N + qrow] = __builtin_inff();
     if (!bvalid) return;
 
     if (lin) {
@@ -532,7 +501,7 @@ static hipError_t launch_fused16_t(const FusedArgs &a, hipStream_t st) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
     fused16_kernel<T, S, D, TO, MARKS><<<(unsigned)(8L * per), 512, 0, st>>>(
         (const T *)a.q, (const T *)a.k, (const T *)a.v, a.slots, a.kc, a.pcount, a.bcast ? 1 : 0, a.fp,
-        (const S *)a.hhat, a.mcount, a.Lp, (TO *)a.out, G, per, a.N, a.Nb, sl2);
+        (const S *)a.hhat, a.mcount, a.Lp, (TO *)a.out, a.lse, G, per, a.N, a.Nb, sl2);
     return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ struct FusedArgs {
     const int32_t *pcount;   // nullable: slots used per pair ([BH][ceil(Nb/2)], or [ceil(Nb/2)] with bcast)
     bool bcast;              // one schedule shared by every head
     int fp;                  // tokens per frame for the frame marks in the slots (0: no marks)
+    float *lse;              // nullable: [BH][N] log-sum-exp of each row's sparse softmax (log2 units)
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere
     int Lp;
@@ -89,6 +90,31 @@ struct LvsaParams {
 };
 hipError_t launch_lvsa_frames(const LvsaParams &p, int32_t *lohi, int32_t *sets, int32_t *counts, int max_frames,
                               hipStream_t st);
+// backward: inputs, the forward's recomputed pieces, outputs and scratch
+struct BackwardArgs {
+    const void *q, *k, *v, *dout;     // [BH][N][D] bf16
+    const float *w;                   // [D][D]
+    const float *o_s, *lse;           // sparse output and its log-sum-exp (log2 units)
+    const int32_t *crit;              // [BH][Nb][kc]
+    int kc;
+    const int8_t *mask;               // [BH][Nb][Nb] labels
+    const void *hhat;                 // [BH][Nb][Lp] f16 marginal states (Ĥ'^T, Ẑ; / m_i)
+    const int32_t *mcount;            // [BH][Nb] marginal tokens per row
+    float *dq, *dk, *dv, *dw;         // gradients
+    float *dbuf;                      // [BH][N] D_r = dO_r . O_s,r
+    uint16_t *tlist;                  // [BH][Nb][Nb] transposed critical lists
+    int32_t *tcnt;                    // [BH][Nb]
+    float *margT;                     // [BH][Nb][Nbc] transposed marginal indicator
+    int32_t *unit;                    // [BH][Nb] = 64
+    float *dhrow;                     // [BH][Nbc][Lp] per-row state gradients
+    float *dhs;                       // [BH][Nb][Lp] per-key-block state gradients
+    long BH;
+    int N, Nb, Nbc, Lp, D;
+};
+hipError_t launch_backward_sparse(const BackwardArgs &a, hipStream_t st);
+hipError_t launch_backward_linear(const BackwardArgs &a, hipStream_t st);
+hipError_t launch_zero(float *p, long n, hipStream_t st);
+
 // STA tiles: tile sizes, windows, tile grid, tile volume and the largest
 // |delta| per axis worth testing (2*delta*t <= W)
 struct StaParams {

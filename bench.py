@@ -29,6 +29,13 @@ latent: 30x48x80 tokens (N = 115200, tile-major), tiles (6, 8, 8), window
 (18, 27, 24), H=24, d=128; `value` counts 4*d flops per kept (query, key)
 pair.
 
+With --backward it prints instead one JSON line for the SLA backward pass
+(sla_backward: the forward recomputed inside, then dQ, dK, dV, dW) on the
+same Wan2.1 480p workload; `value` counts the forward's F plus 10*64*64*d per
+critical pair (five products), 6*64*d*d per query block and 10*64*d*d per
+key block of the linear branch, and (d*d + d) per marginal pair (the
+transposed sums).
+
 With --quality it prints instead one JSON line for the mask-quality
 diagnostics (sla_block_mass + sla_mask_stats) on the same workload: the
 exact block attention mass kept by the critical, marginal and negligible
@@ -56,6 +63,7 @@ LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_lvsa_wan6x_stats.md"
 STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_sta_hunyuan_stats.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 
 
 def work(B, H, N, d, kc, kn):
@@ -359,6 +367,110 @@ def run_sta(args):
     print(json.dumps(line), flush=True)
 
 
+BWD_STAGES = ("forward", "dq", "dkv", "linear_rows", "linear_keys")
+
+
+def run_backward(args, wl):
+    import numpy as np
+    import torch
+    import sparse_attention_video_sla_amd as sla
+    from sparse_attention_video_sla_amd import _lib
+    from sparse_attention_video_sla_amd.inputs import make_workload, round_bf16
+
+    rc = args.crit if args.crit is not None else wl.fracs[0][0]
+    rn = args.negl if args.negl is not None else wl.fracs[0][1]
+    inp = make_workload(args.workload)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    w = torch.from_numpy(inp.w).to(dev)
+    rng = np.random.default_rng(wl.seed + 7)
+    dout_h = round_bf16(rng.standard_normal(inp.q.shape).astype(np.float32))
+    dout = torch.from_numpy(dout_h).to(dev).to(torch.bfloat16)
+    B, H, N, d = q.shape
+    Nb = -(-N // 64)
+    kc, kn = sla.counts(Nb, rc, rn)
+    ws = torch.empty(sla.backward_workspace_size(B, H, N, d, rc, rn), dtype=torch.uint8, device=dev)
+
+    def step():
+        sla.backward(q, k, v, w, dout, rc, rn, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L = _lib.load()
+    L.sla_set_stage_timing(1)
+    ms_buf = (ctypes.c_float * 5)()
+    calls = ctypes.c_int()
+    L.sla_stage_times(ms_buf, ctypes.byref(calls))
+    for _ in range(args.steps):
+        step()
+    _lib.check(L.sla_stage_times(ms_buf, ctypes.byref(calls)))
+    L.sla_set_stage_timing(0)
+    st_ms = {name: ms_buf[i] / max(calls.value, 1) for i, name in enumerate(BWD_STAGES)}
+
+    f_fwd, _, pairs, marg_rows = work(B, H, N, d, kc, kn)
+    lin = kc + kn < Nb
+    marg_pairs = B * H * Nb * (Nb - kc - kn) if lin else 0
+    f_sparse = 10.0 * 64 * 64 * d * pairs
+    f_rows = 6.0 * 64 * d * d * marg_rows
+    f_keys = 10.0 * 64 * d * d * B * H * Nb if lin else 0.0
+    f_sums = float(marg_pairs) * (d * d + d)
+    total = f_fwd + f_sparse + f_rows + f_keys + f_sums
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = total / (ms * 1e-3) / 1e12
+    per_stage = {
+        "forward": (f_fwd, "mfma"), "dq": (6.0 * 64 * 64 * d * pairs, "mfma"), "dkv": (8.0 * 64 * 64 * d * pairs, "mfma"),
+        "linear_rows": (f_rows + f_sums, "alu"), "linear_keys": (f_keys, "alu")}
+    stages = {}
+    for name in BWD_STAGES:
+        fl, bound = per_stage[name]
+        stages[name] = {"ms": round(st_ms[name], 4),
+                        "TFLOP/s": round(fl / max(st_ms[name], 1e-9) / 1e9, 1), "bound": bound}
+    dom = max(BWD_STAGES, key=lambda n: st_ms[n])
+    fl, bound = per_stage[dom]
+    peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_VALU_TFLOPS
+    achieved = fl / max(st_ms[dom], 1e-9) / 1e9
+    line = {
+        "metric": "effective TFLOP/s + ms/call of the SLA backward (forward recomputed + dQ, dK, dV, dW) at N=32760",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; local sinusoid Q/K + noise, V ~ N(0,1); dO ~ N(0,1))",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64, "crit_frac": rc,
+                   "negl_frac": rn, "k_c": kc, "k_n": kn, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "backward stage " + dom,
+                     "flops_per_launch": fl, "avg_launch_ms": round(st_ms[dom], 4)},
+        "stages": stages,
+    }
+    if not args.no_cpu:
+        from oracle import backward as ob
+        from oracle import oracle as orc
+        n_tok, heads = 8192, 2
+        sub = make_workload(args.workload, n_tokens=n_tok)
+        sq, sk, sv = (x[:, :heads] for x in (sub.q, sub.k, sub.v))
+        sd = dout_h[:, :heads, :n_tok]
+        t0 = time.perf_counter()
+        mask = orc.classify(orc.pool(sq), orc.pool(sk), rc, rn)["mask"]
+        ob.gradients(sq, sk, sv, sub.w, mask, sd)
+        t = time.perf_counter() - t0
+        nb = -(-n_tok // 64)
+        kcs, kns = sla.counts(nb, rc, rn)
+        ff, _, pp, mr = work(1, heads, n_tok, d, kcs, kns)
+        fs = ff + 10.0 * 64 * 64 * d * pp + 6.0 * 64 * d * d * mr + 10.0 * 64 * d * d * heads * nb + \
+            float(heads * nb * (nb - kcs - kns)) * (d * d + d)
+        line["cpu_baseline"] = {"value": round(fs / t / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
+                                "kind": "oracle", "seconds": round(t, 3),
+                                "sample": "the first %d tokens of heads 0-%d (the token-level oracle is quadratic in N): "
+                                          "labels, then autograd of the fp64 forward; F counted the same way"
+                                          % (n_tok, heads - 1)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +484,7 @@ def main():
     ap.add_argument("--quality", action="store_true", help="mask-quality diagnostics line instead of the forward line")
     ap.add_argument("--lvsa", action="store_true", help="LVSA frame-level sparse attention line (long-video workload)")
     ap.add_argument("--sta", action="store_true", help="sliding tile attention line (HunyuanVideo-sized latent)")
+    ap.add_argument("--backward", action="store_true", help="SLA backward line (same workload as the forward)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
@@ -391,6 +504,9 @@ def main():
         run_sta(args)
         return
     wl = WORKLOADS[args.workload]
+    if args.backward:
+        run_backward(args, wl)
+        return
     if args.quality:
         run_quality(args, wl)
         return

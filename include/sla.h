@@ -241,7 +241,10 @@ sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int 
  * use and kept per thread.  Disabled by default.  sla_forward_lists,
  * sla_forward_lvsa and sla_forward_sta calls are recorded too: stage 1 is
  * building their block schedule, stage 4 their attention kernel, the other
- * stages zero. */
+ * stages zero.  sla_backward calls record: 0 the forward recomputed inside,
+ * 1 the transposed lists and dQ of the sparse part, 2 dK and dV of the
+ * sparse part, 3 the linear part's rows and transposed sums, 4 its keys and
+ * dW. */
 #define SLA_NUM_STAGES 5
 sla_status sla_set_stage_timing(int enable);
 sla_status sla_stage_times(float *ms, int *calls);

@@ -545,7 +545,8 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
 static sla_status forward_impl(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
                                sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
                                double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *workspace,
-                               size_t workspace_bytes, void *stream, float *lse_out, bool linear_off) {
+                               size_t workspace_bytes, void *stream, float *lse_out, bool linear_off,
+                               bool timed = true) {
     if (!q || !k || !v || !w_proj || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
     sla_status st = check_shape(B, H, N, d, block);
     if (st != SLA_OK) return st;
@@ -572,7 +573,7 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     int32_t *crit = (int32_t *)(ws + L.crit);
     int32_t *mcount = (int32_t *)(ws + L.mcount);
 
-    StageEvents *ev = timed_call();
+    StageEvents *ev = timed ? timed_call() : nullptr;
     // block states on the side stream, concurrent with pool and classify; a
     // return after the fork still makes the caller's stream wait for the join
     SideStream *ss = nullptr;
@@ -720,10 +721,13 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
     hipStream_t s = (hipStream_t)stream;
     const int Nb = (N + 63) / 64;
     float *o_s = (float *)(ws + o.o_s), *lse = (float *)(ws + o.lse);
+    StageEvents *ev = timed_call();
     // the forward again: labels, critical lists, marginal states, and the
     // sparse output with its log-sum-exp
+    mark_stage(ev, 0, 0, s);
     st = forward_impl(q, k, v, w_proj, SLA_BF16, SLA_F32, B, H, N, d, block, crit_frac, negl_frac, phi, o_s, nullptr,
-                      ws, L.total, stream, lse, true);
+                      ws, L.total, stream, lse, true, false);
+    mark_stage(ev, 0, 1, s);
     if (st != SLA_OK) return st;
     sla::BackwardArgs a{};
     a.q = q; a.k = k; a.v = v; a.dout = dout; a.w = w_proj; a.o_s = o_s; a.lse = lse;
@@ -734,10 +738,24 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
     a.margT = (float *)(ws + o.margT); a.unit = (int32_t *)(ws + o.unit);
     a.dhrow = (float *)(ws + o.dhrow); a.dhs = (float *)(ws + o.dhs);
     a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Lp = L.Lp; a.D = d;
-    st = device_status(sla::launch_backward_sparse(a, s), "backward (sparse) launch");
+    mark_stage(ev, 1, 0, s);
+    st = device_status(sla::launch_backward_dq(a, s), "backward dq launch");
+    mark_stage(ev, 1, 1, s);
     if (st != SLA_OK) return st;
-    if (kc + kn < Nb) return device_status(sla::launch_backward_linear(a, s), "backward (linear) launch");
-    return device_status(sla::launch_zero(dw, (long)d * d, s), "backward launch");
+    mark_stage(ev, 2, 0, s);
+    st = device_status(sla::launch_backward_dkv(a, s), "backward dk/dv launch");
+    mark_stage(ev, 2, 1, s);
+    if (st != SLA_OK) return st;
+    const bool linear = kc + kn < Nb;
+    mark_stage(ev, 3, 0, s);
+    st = device_status(linear ? sla::launch_backward_lin_rows(a, s) : sla::launch_zero(dw, (long)d * d, s),
+                       "backward linear rows launch");
+    mark_stage(ev, 3, 1, s);
+    if (st != SLA_OK) return st;
+    mark_stage(ev, 4, 0, s);
+    if (linear) st = device_status(sla::launch_backward_lin_keys(a, s), "backward linear keys launch");
+    mark_stage(ev, 4, 1, s);
+    return st;
 }
 
 }  // extern "C"

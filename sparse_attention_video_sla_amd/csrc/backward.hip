@@ -718,27 +718,35 @@ hipError_t launch_zero(float *p, long n, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_backward_sparse(const BackwardArgs &a, hipStream_t st) {
+hipError_t launch_backward_dq(const BackwardArgs &a, hipStream_t st) {
     const long Gq = a.BH * a.Nb;
     const int per = (int)((Gq + 7) / 8);
     const float sl2 = 1.4426950408889634f / sqrtf((float)a.D), scale = 1.f / sqrtf((float)a.D);
     const unsigned g1 = (unsigned)((a.BH * a.Nb + 255) / 256);
     bwd_tlists_kernel<<<g1, 256, 0, st>>>(a.mask, a.BH, a.Nb, a.tlist, a.tcnt);
-    if (a.D == 64) {
+    if (a.D == 64)
         bwd_dq_kernel<64><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
             (const bf16 *)a.dout, a.o_s, a.lse, a.crit, a.kc, a.dq, a.dbuf, Gq, per, a.N, a.Nb, sl2, scale);
-        bwd_dkv_kernel<64><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-            (const bf16 *)a.dout, a.lse, a.dbuf, a.tlist, a.tcnt, a.dk, a.dv, Gq, per, a.N, a.Nb, sl2, scale);
-    } else {
+    else
         bwd_dq_kernel<128><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
             (const bf16 *)a.dout, a.o_s, a.lse, a.crit, a.kc, a.dq, a.dbuf, Gq, per, a.N, a.Nb, sl2, scale);
-        bwd_dkv_kernel<128><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-            (const bf16 *)a.dout, a.lse, a.dbuf, a.tlist, a.tcnt, a.dk, a.dv, Gq, per, a.N, a.Nb, sl2, scale);
-    }
     return hipGetLastError();
 }
 
-hipError_t launch_backward_linear(const BackwardArgs &a, hipStream_t st) {
+hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st) {
+    const long Gq = a.BH * a.Nb;
+    const int per = (int)((Gq + 7) / 8);
+    const float sl2 = 1.4426950408889634f / sqrtf((float)a.D), scale = 1.f / sqrtf((float)a.D);
+    if (a.D == 64)
+        bwd_dkv_kernel<64><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+            (const bf16 *)a.dout, a.lse, a.dbuf, a.tlist, a.tcnt, a.dk, a.dv, Gq, per, a.N, a.Nb, sl2, scale);
+    else
+        bwd_dkv_kernel<128><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+            (const bf16 *)a.dout, a.lse, a.dbuf, a.tlist, a.tcnt, a.dk, a.dv, Gq, per, a.N, a.Nb, sl2, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st) {
     // zero dW, the transposed indicator and its unit counts
     bwd_zero_kernel<<<(unsigned)((a.D * a.D + 255) / 256), 256, 0, st>>>(a.dw, (long)a.D * a.D);
     const long nt = a.BH * a.Nb * (long)a.Nbc;
@@ -755,8 +763,10 @@ hipError_t launch_backward_linear(const BackwardArgs &a, hipStream_t st) {
     AssembleArgs as{};
     as.marg = a.margT; as.hs = a.dhrow; as.mcount = a.unit; as.hhat = a.dhs;
     as.BH = a.BH; as.Nb = a.Nb; as.Nbc = a.Nbc; as.Nbp = a.Nbc; as.Lp = a.Lp; as.f32 = true;
-    e = launch_assemble(as, st);
-    if (e != hipSuccess) return e;
+    return launch_assemble(as, st);
+}
+
+hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st) {
     int dev = 0, cus = 0;
     hipGetDevice(&dev);
     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -111,8 +111,10 @@ struct BackwardArgs {
     long BH;
     int N, Nb, Nbc, Lp, D;
 };
-hipError_t launch_backward_sparse(const BackwardArgs &a, hipStream_t st);
-hipError_t launch_backward_linear(const BackwardArgs &a, hipStream_t st);
+hipError_t launch_backward_dq(const BackwardArgs &a, hipStream_t st);        // transposed lists + dQ (sparse)
+hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st);       // dK, dV (sparse)
+hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st);  // linear rows + transposed sums
+hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st);  // linear keys + dW
 hipError_t launch_zero(float *p, long n, hipStream_t st);
 
 // STA tiles: tile sizes, windows, tile grid, tile volume and the largest

@@ -63,7 +63,6 @@ LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_lvsa_wan6x_stats.md"
 STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_sta_hunyuan_stats.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 
 
 def work(B, H, N, d, kc, kn):
@@ -425,7 +424,7 @@ def run_backward(args, wl):
     value = total / (ms * 1e-3) / 1e12
     per_stage = {
         "forward": (f_fwd, "mfma"), "dq": (6.0 * 64 * 64 * d * pairs, "mfma"), "dkv": (8.0 * 64 * 64 * d * pairs, "mfma"),
-        "linear_rows": (f_rows + f_sums, "alu"), "linear_keys": (f_keys, "alu")}
+        "linear_rows": (f_rows + f_sums, "mfma"), "linear_keys": (f_keys, "mfma")}
     stages = {}
     for name in BWD_STAGES:
         fl, bound = per_stage[name]
@@ -433,7 +432,7 @@ def run_backward(args, wl):
                         "TFLOP/s": round(fl / max(st_ms[name], 1e-9) / 1e9, 1), "bound": bound}
     dom = max(BWD_STAGES, key=lambda n: st_ms[n])
     fl, bound = per_stage[dom]
-    peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_VALU_TFLOPS
+    peak = PEAK_BF16_TFLOPS
     achieved = fl / max(st_ms[dom], 1e-9) / 1e9
     line = {
         "metric": "effective TFLOP/s + ms/call of the SLA backward (forward recomputed + dQ, dK, dV, dW) at N=32760",

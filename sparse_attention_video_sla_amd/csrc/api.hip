@@ -660,7 +660,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
 // ---- backward ----------------------------------------------------------------
 
 struct BwdLayout {
-    size_t fwd, o_s, lse, dbuf, tlist, tcnt, margT, unit, dhrow, dhs, total;
+    size_t fwd, o_s, lse, dbuf, tlist, tcnt, mbitsT, unit, dh2, dhs, total;
 };
 
 static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_frac, double negl_frac,
@@ -680,9 +680,9 @@ static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_
     o->dbuf = take(sizeof(float) * BH * N);
     o->tlist = take(sizeof(uint16_t) * BH * Nb * Nb);
     o->tcnt = take(sizeof(int32_t) * BH * Nb);
-    o->margT = take(sizeof(float) * BH * Nb * L->Nbc);
+    o->mbitsT = take(sizeof(uint32_t) * BH * (2 * L->Nbc / 32) * L->Nbp);
     o->unit = take(sizeof(int32_t) * BH * Nb);
-    o->dhrow = take(sizeof(float) * BH * L->Nbc * L->Lp);
+    o->dh2 = take(sizeof(uint16_t) * BH * 2 * L->Nbc * L->Lp);
     o->dhs = take(sizeof(float) * BH * Nb * L->Lp);
     o->total = off;
     return SLA_OK;
@@ -735,9 +735,9 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
     a.hhat = ws + L.hhat; a.mcount = (const int32_t *)(ws + L.mcount);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbuf = (float *)(ws + o.dbuf);
     a.tlist = (uint16_t *)(ws + o.tlist); a.tcnt = (int32_t *)(ws + o.tcnt);
-    a.margT = (float *)(ws + o.margT); a.unit = (int32_t *)(ws + o.unit);
-    a.dhrow = (float *)(ws + o.dhrow); a.dhs = (float *)(ws + o.dhs);
-    a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Lp = L.Lp; a.D = d;
+    a.mbitsT = (uint32_t *)(ws + o.mbitsT); a.unit = (int32_t *)(ws + o.unit);
+    a.dh2 = ws + o.dh2; a.dhs = (float *)(ws + o.dhs);
+    a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Nbp = L.Nbp; a.Lp = L.Lp; a.D = d;
     mark_stage(ev, 1, 0, s);
     st = device_status(sla::launch_backward_dq(a, s), "backward dq launch");
     mark_stage(ev, 1, 1, s);

@@ -33,7 +33,9 @@
 // as bits (32 key blocks per word); each lane reads the words of its own
 // rows from the stage and expands them into the fp16 B operand in registers.  The output tile of a wave is
 // scaled, staged through LDS (8-byte units swizzled by row) and written as
-// whole contiguous row segments.
+// whole contiguous row segments.  The same kernel takes bf16 rows with a
+// float output (the backward pass sums its state gradients this way, as
+// bf16 pairs hi + lo over twice the rows).
 #include "sla_device.h"
 #include "sla_launch.h"
 
@@ -66,7 +68,8 @@ constexpr int AT_VM = AT_NA + AT_NW;                     // memory operations pe
 // one K-step into a stage: this wave's two 1 KB pieces of the Hs rows (four
 // 256-byte rows each) and its two 256-byte pieces of the indicator words
 // (word h of rows 64 i .. 64 i + 63 of the tile at 64 (8 h + i))
-__device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rb, f16 *S,
+template <typename T>
+__device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rb, T *S,
                                          const uint32_t (&va)[AT_NA], const uint32_t (&vw)[AT_NW], int w,
                                          uint32_t aoff, uint32_t woff) {
 #pragma unroll
@@ -76,24 +79,27 @@ __device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buf
     for (int u = 0; u < AT_NW; ++u) dma4(rb, W + 64 * (AT_NW * w + u), vw[u] + woff);
 }
 
-// 8 indicator bits -> 8 fp16 values (1.0 = 0x3C00): each dword takes two bits
-// y, spread to bit 0 and bit 16 by (y * 0x8001) & 0x10001, times 0x3C00
-__device__ __forceinline__ v8<f16> expand_bits(uint32_t x) {
+// 8 indicator bits -> 8 16-bit values 0 or 1 (1.0 = 0x3C00 in fp16, 0x3F80
+// in bf16): each dword takes two bits y, spread to bit 0 and bit 16 by
+// (y * 0x8001) & 0x10001, times the bits of 1.0
+template <typename T> __device__ __forceinline__ v8<T> expand_bits(uint32_t x) {
+    constexpr uint32_t one = __is_same(T, f16) ? 0x3C00u : 0x3F80u;
     uint32_t d[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const uint32_t y = (x >> (2 * e)) & 3u;
-        d[e] = __umul24(__umul24(y, 0x8001u) & 0x10001u, 0x3C00u);
+        d[e] = __umul24(__umul24(y, 0x8001u) & 0x10001u, one);
     }
-    v8<f16> r;
+    v8<T> r;
     __builtin_memcpy(&r, d, sizeof(r));
     return r;
 }
 
 // the 32 MFMAs of one K-step for a wave's 128 x 64 tile (rows 64 w .. 64 w + 63)
-__device__ __forceinline__ void at_compute(const f16 *S, f32x16 (&acc)[4][2], int w, int lane) {
+template <typename T>
+__device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int w, int lane) {
     const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4, L = lane & 15;
-    const f16 *A = S;
+    const T *A = S;
     const uint32_t *W = reinterpret_cast<const uint32_t *>(S + AT_HS);
     uint32_t bw[2][2];                                   // word h of row nt: key blocks 32 h .. 32 h + 31
 #pragma unroll
@@ -102,20 +108,20 @@ __device__ __forceinline__ void at_compute(const f16 *S, f32x16 (&acc)[4][2], in
         for (int h = 0; h < 2; ++h) bw[nt][h] = W[AT_TN * h + 64 * w + 32 * nt + l32];
 #pragma unroll
     for (int s = 0; s < AT_TK / 16; ++s) {
-        v8<f16> b[2];
+        v8<T> b[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)                  // key blocks 16 s + 8 hh .. + 7 of the lane's row
-            b[nt] = expand_bits(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
+            b[nt] = expand_bits<T>(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int n = 32 * mt + 16 * (grp & 1) + 4 * (L & 3);              // state column of this lane's run
-            v4<f16> h[2];
+            v4<T> h[2];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int k = 16 * s + 8 * (grp >> 1) + 4 * x + (L >> 2);      // key block within the step
-                h[x] = lds_tr_raw<f16>(&A[k * AT_TM + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7)]);
+                h[x] = lds_tr_raw<T>(&A[k * AT_TM + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7)]);
             }
-            const v8<f16> a = cat8<f16>(h[0], h[1]);
+            const v8<T> a = cat8<T>(h[0], h[1]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) mma16(acc[mt][nt], a, b[nt]);
         }
@@ -124,14 +130,18 @@ __device__ __forceinline__ void at_compute(const f16 *S, f32x16 (&acc)[4][2], in
 
 }  // namespace
 
+// T: the 16-bit type of the states; O: f16 (rows scaled by 64 / m_i, staged
+// through LDS) or float (written from the accumulators as they are, 16 bytes
+// per lane)
+template <typename T, typename O>
 __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restrict__ mbits,
-                                                         const f16 *__restrict__ hs,
+                                                         const T *__restrict__ hs,
                                                          const int32_t *__restrict__ mcount,
-                                                         f16 *__restrict__ hhat, int Nb, int Nbc, int Nbp, int Lp,
+                                                         O *__restrict__ hhat, int Nb, int Nbc, int Nbp, int Lp,
                                                          int tiles_m, int tiles_n, long G, int per_xcd) {
     // four stages; separate arrays so that reads of one stage never wait for
     // loads still landing in another
-    __shared__ __attribute__((aligned(1024))) f16 S0[AT_STAGE], S1[AT_STAGE], S2[AT_STAGE], S3[AT_STAGE];
+    __shared__ __attribute__((aligned(1024))) T S0[AT_STAGE], S1[AT_STAGE], S2[AT_STAGE], S3[AT_STAGE];
 
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restr
     // the end (they read zeros): every step then issues the same number of
     // memory operations, which the wait counts, and the compiler tells the
     // stages apart and adds no waits of its own before the reads of a stage.
-    auto stage = [&](int st, const f16 *S, f16 *Sn) {
+    auto stage = [&](int st, const T *S, T *Sn) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * AT_VM));   // vmcnt(8)
         lds_barrier();
         at_issue(rh, rb, Sn, va, vw, wave, (uint32_t)(st + 3) * astep, (uint32_t)(st + 3) * wstep);
@@ -196,10 +206,30 @@ __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restr
     __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
     lds_barrier();                                       // every wave is done with the stages
     if (!active) return;
+    if constexpr (sizeof(O) == 4) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int i = wrow + 32 * nt + l32;
+            if (i >= Nb) continue;
+            const int mc = mcount[bh * Nb + i];
+            const float sc = mc > 0 ? 64.f / (float)mc : 0.f;
+            O *orow = hhat + (bh * Nb + i) * (long)Lp + col0;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 y = {acc[mt][nt][4 * g] * sc, acc[mt][nt][4 * g + 1] * sc,
+                                     acc[mt][nt][4 * g + 2] * sc, acc[mt][nt][4 * g + 3] * sc};
+                    *reinterpret_cast<f32x4 *>(orow + 32 * mt + 8 * g + 4 * hh) = y;
+                }
+        }
+        return;
+    }
 
     // epilogue: the wave's 32-row halves go through a private 8 KB LDS slice,
     // 8-byte unit u of row r at unit u ^ r (conflict-free both ways)
-    f16 *stg = (wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) + (wave & 1) * 4096;
+    T *stg0 = (wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) + (wave & 1) * 4096;
+    O *stg = reinterpret_cast<O *>(stg0);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int i = wrow + 32 * nt + l32;
@@ -210,16 +240,16 @@ __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restr
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int u = 8 * mt + 2 * g + hh;       // 8-byte unit: columns 4u .. 4u + 3 of the tile
-                v4<f16> y;
+                v4<O> y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = (f16)(acc[mt][nt][4 * g + e] * sc);
+                for (int e = 0; e < 4; ++e) y[e] = (O)(acc[mt][nt][4 * g + e] * sc);
                 __builtin_memcpy(&stg[l32 * AT_TM + 4 * (u ^ l32)], &y, sizeof(y));
             }
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int r = 2 * x + hh, u = l32;           // row r, unit u of the staged half
             const int ir = wrow + 32 * nt + r;
-            const v4<f16> y = ld4<f16>(&stg[r * AT_TM + 4 * (u ^ r)]);
+            const v4<O> y = ld4<O>(&stg[r * AT_TM + 4 * (u ^ r)]);
             if (ir < Nb) __builtin_memcpy(hhat + (bh * Nb + ir) * (long)Lp + col0 + 4 * u, &y, sizeof(y));
         }
     }
@@ -349,8 +379,14 @@ hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st) {
         const int tiles_n = (a.Nb + AT_TN - 1) / AT_TN;
         const long G = a.BH * tiles_m * tiles_n;
         const int per = (int)((G + 7) / 8);
-        assemble16_kernel<<<(unsigned)(8L * per), 512, 0, st>>>(a.mbits, (const f16 *)a.hs, a.mcount, (f16 *)a.hhat,
-                                                                a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G, per);
+        if (a.bf16_f32)
+            assemble16_kernel<bf16, float><<<(unsigned)(8L * per), 512, 0, st>>>(
+                a.mbits, (const bf16 *)a.hs, a.mcount, (float *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G,
+                per);
+        else
+            assemble16_kernel<f16, f16><<<(unsigned)(8L * per), 512, 0, st>>>(
+                a.mbits, (const f16 *)a.hs, a.mcount, (f16 *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G,
+                per);
     }
     return hipGetLastError();
 }

@@ -35,33 +35,51 @@ constexpr float NEG_INF_B = -__builtin_inff();
 
 // ---- transposed lists and indicator ------------------------------------------
 
-// thread per (head, key block j): the query blocks i with j critical, ascending
+// one wave per (head, key block j): the query blocks i with j critical, ascending
 __global__ __launch_bounds__(256) void bwd_tlists_kernel(const int8_t *__restrict__ mask, long BH, int Nb,
                                                          uint16_t *__restrict__ tlist, int32_t *__restrict__ tcnt) {
-    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= BH * Nb) return;
+    const int lane = threadIdx.x & 63;
     const long bh = t / Nb;
     const int j = (int)(t % Nb);
     const int8_t *m = mask + bh * Nb * (long)Nb + j;
     uint16_t *out = tlist + t * (long)Nb;
     int c = 0;
-    for (int i = 0; i < Nb; ++i)
-        if (m[(long)i * Nb] == 1) out[c++] = (uint16_t)i;
-    tcnt[t] = c;
+    for (int i0 = 0; i0 < Nb; i0 += 64) {
+        const int i = i0 + lane;
+        const bool hit = i < Nb && m[(long)i * Nb] == 1;
+        const uint64_t bal = __ballot(hit);
+        if (hit) out[c + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)i;
+        c += __popcll(bal);
+    }
+    if (lane == 0) tcnt[t] = c;
 }
 
-// margT[bh][j][i] = 1 when key block j is marginal for query block i (i < Nbc, 0 past Nb);
-// unit[bh][j] = 64 so that the marginal-state product applies no row scale
-__global__ __launch_bounds__(256) void bwd_margT_kernel(const int8_t *__restrict__ mask, long BH, int Nb, int Nbc,
-                                                        float *__restrict__ margT, int32_t *__restrict__ unit) {
+// mbits[bh][w][j] (w < 2 Nbc / 32, j < Nbp): bit b set when key block j is
+// marginal for query block i = 32 (w mod Nbc / 32) + b (i, j < Nb): the
+// transposed marginal indicator as bits, its words repeated for the lo rows
+// of the state gradients; unit[bh][j] = 64 so that the product applies no
+// row scale
+__global__ __launch_bounds__(256) void bwd_mbitsT_kernel(const int8_t *__restrict__ mask, long BH, int Nb, int Nbc,
+                                                         int Nbp, uint32_t *__restrict__ mbits,
+                                                         int32_t *__restrict__ unit) {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    if (t >= BH * Nb * (long)Nbc) return;
-    const int i = (int)(t % Nbc);
-    const long r = t / Nbc;
-    const int j = (int)(r % Nb);
-    const long bh = r / Nb;
-    margT[t] = (i < Nb && mask[(bh * Nb + i) * (long)Nb + j] == 0) ? 1.f : 0.f;
-    if (i == 0) unit[r] = 64;
+    const int nw = 2 * Nbc / 32;
+    if (t >= BH * nw * (long)Nbp) return;
+    const int j = (int)(t % Nbp);
+    const long r = t / Nbp;
+    const int wd = (int)(r % nw);
+    const long bh = r / nw;
+    const int i0 = 32 * (wd % (Nbc / 32));
+    uint32_t bits = 0;
+    if (j < Nb)
+        for (int b = 0; b < 32; ++b) {
+            const int i = i0 + b;
+            if (i < Nb && mask[(bh * Nb + i) * (long)Nb + j] == 0) bits |= 1u << b;
+        }
+    mbits[t] = bits;
+    if (wd == 0 && j < Nb) unit[bh * Nb + j] = 64;
 }
 
 __global__ __launch_bounds__(256) void bwd_zero_kernel(float *__restrict__ p, long n) {
@@ -445,270 +463,448 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
 // ---- linear part --------------------------------------------------------------
 
 namespace {
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
     return x;
 }
+// power of two that brings the largest magnitude m of a tile into [0.5, 1)
+// (1 for m = 0 or not finite), so that f16 operands keep their precision
+// whatever the scale of the gradient
+__device__ __forceinline__ float pow2_scale(float m) {
+    if (!(m > 0.f) || !(m < __builtin_inff())) return 1.f;
+    int ex = 0;
+    frexpf(m, &ex);
+    return ldexpf(1.f, -max(ex, -125));
+}
+// x as the pair hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split_store(bf16 *hi, bf16 *lo, long at, float x) {
+    const bf16 h = (bf16)x;
+    hi[at] = h;
+    lo[at] = (bf16)(x - (float)h);
+}
 }  // namespace
 
-// One workgroup per query block i (rows past Nb, and rows without marginal
-// blocks, write zero states).  Rows: wave w takes rows 16w .. +15, each lane
-// D/64 channels.  Then dĤ' (stored transposed like Ĥ': [c][a]) and dẐ.
+// One workgroup of 4 waves per query block i (blocks past Nb and rows without
+// marginal blocks write zero state gradients).
+//  1. VALU, a thread per 8-channel chunk of a row: Pn_r = phi(q_r) / den_r
+//     and s dO_r (s a power of two shared by the block) as f16 rows in LDS,
+//     with Ĥ'_i^T (stored [c][a]).
+//  2. matrix core, wave (rh, ch): y^T = H Pn^T (channels c of half ch,
+//     tokens of half rh) and s X^T = H^T (s dO)^T (channels a of half ch);
+//     per token g = dO.y, e_a = X_a - g Ẑ_a, t = Pn.e (the two channel halves
+//     summed through LDS), dq_a += Pn_a (e_a - den t).
+//  3. matrix core: dĤ'_i = dO^T Pn / m_i, VALU: dẐ_i = -g^T Pn / m_i, both
+//     written as bf16 pairs (hi in row i, lo in row Nbc + i of the head).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_lin_row_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ dout,
-                                                          const f16 *__restrict__ hhat, const int32_t *__restrict__ mcount,
-                                                          int Lp, float *__restrict__ dq, float *__restrict__ dhrow,
-                                                          long BH, int N, int Nb, int Nbc) {
-    constexpr int CPL = D / 64;                          // channels per lane
-    constexpr int HS = D + 1;                            // padded row stride of Hs
-    __shared__ float Hs[D * HS];                         // stored [c][a]
-    __shared__ float Zs[D];
-    __shared__ float Pn[64 * D];                         // phi(q_r) / den_r (scaled states)
-    __shared__ float Do[64 * D];
-    __shared__ float Gr[64];
+__global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ dout,
+                                                             const f16 *__restrict__ hhat,
+                                                             const int32_t *__restrict__ mcount, int Lp,
+                                                             float *__restrict__ dq, bf16 *__restrict__ dh2, long BH,
+                                                             int N, int Nb, int Nbc) {
+    constexpr int STR = D + 8;                           // padded row stride of the f16 tiles
+    constexpr int CPR = D / 8, RPP = 256 / CPR, NP = 64 / RPP;
+    constexpr int NCT = D / 64;                          // 32-channel tiles per channel half
+    constexpr int TPW = (D / 32) * (D / 32) / 4;         // dĤ' tiles per wave
+    __shared__ __attribute__((aligned(16))) f16 Hs[D * STR];
+    __shared__ __attribute__((aligned(16))) f16 Pn[64 * STR];
+    __shared__ __attribute__((aligned(16))) f16 Ds[64 * STR];
+    __shared__ float Zs[D], Dn[64], Gr[64], Gx[2][64], Tx[2][64], Red[4];
+
     const long blk = blockIdx.x;
     const long bh = blk / Nbc;
     const int i = (int)(blk % Nbc);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float *drow = dhrow + blk * (long)Lp;
+    const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
+    bf16 *hi = dh2 + (bh * 2 * Nbc + i) * (long)Lp;
+    bf16 *lo = hi + (long)Nbc * Lp;
     const int mc = i < Nb ? mcount[bh * Nb + i] : 0;
     if (mc == 0) {
-        for (int x = tid; x < Lp; x += 256) drow[x] = 0.f;
+        for (int x = tid; x < Lp / 8; x += 256) {
+            st_chunk(hi + 8 * x, zero_chunk());
+            st_chunk(lo + 8 * x, zero_chunk());
+        }
         return;
     }
     const f16 *hr = hhat + (bh * Nb + i) * (long)Lp;
-    for (int x = tid; x < D * D; x += 256) Hs[(x / D) * HS + (x % D)] = (float)hr[x];
-    for (int x = tid; x < D; x += 256) Zs[x] = (float)hr[D * D + x];
-    for (int x = D * D + D + tid; x < Lp; x += 256) drow[x] = 0.f;
-    __syncthreads();
-    for (int rr = 0; rr < 16; ++rr) {
-        const int r = 16 * wave + rr;
-        const int row = 64 * i + r;
-        float ph[CPL], dov[CPL];
-        if (row < N) {
-            const long base = (bh * N + row) * (long)D;
-            float qv[CPL], mx = NEG_INF_B;
+    for (int x = tid; x < D * CPR; x += 256) st_chunk(&Hs[(x / CPR) * STR + 8 * (x % CPR)], ld_chunk(hr + 8 * x));
+    if (tid < D) Zs[tid] = (float)hr[D * D + tid];
+
+    // 1. rows
+    const int p = tid % CPR;
+    float zf[8];
+    {
+        const Chunk zc = ld_chunk(hr + D * D + 8 * p);
+        const f16 *z = reinterpret_cast<const f16 *>(&zc);
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                qv[e] = to_f32<bf16>(q[base + lane + 64 * e]);
-                dov[e] = to_f32<bf16>(dout[base + lane + 64 * e]);
-                mx = fmaxf(mx, qv[e]);
-            }
-            mx = wave_max(mx);
-            float se = 0.f;
+        for (int e = 0; e < 8; ++e) zf[e] = (float)z[e];
+    }
+    Chunk dc[NP];
+    float dmax = 0.f;
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                ph[e] = __expf(qv[e] - mx);
-                se += ph[e];
-            }
-            se = wave_sum(se);
+    for (int n = 0; n < NP; ++n) {
+        const int r = RPP * n + tid / CPR, row = 64 * i + r;
+        const bool ok = row < N;
+        const long base = (bh * N + row) * (long)D + 8 * p;
+        const Chunk qc = ok ? ld_chunk(q + base) : zero_chunk();
+        dc[n] = ok ? ld_chunk(dout + base) : zero_chunk();
+        const bf16 *qx = reinterpret_cast<const bf16 *>(&qc);
+        float ph[8], mx = NEG_INF_B;
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                ph[e] /= se;
-                Pn[r * D + lane + 64 * e] = ph[e];
-                Do[r * D + lane + 64 * e] = dov[e];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                ph[e] = 0.f;
-                dov[e] = 0.f;
-                Pn[r * D + lane + 64 * e] = 0.f;
-                Do[r * D + lane + 64 * e] = 0.f;
-            }
+        for (int e = 0; e < 8; ++e) {
+            ph[e] = (float)qx[e];
+            mx = fmaxf(mx, ph[e]);
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        if (row >= N) {
-            if (lane == 0) Gr[r] = 0.f;
-            continue;
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float se = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ph[e] = __expf(ph[e] - mx);
+            se += ph[e];
         }
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) se += __shfl_xor(se, o);
+        const float ise = 1.f / se;
         float den = 0.f;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) den += ph[e] * Zs[lane + 64 * e];
-        den = wave_sum(den);
-        // y[c] = sum_a phi_a H[c][a] / den (this lane's c), g = dO . y
-        float g = 0.f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int c = lane + 64 * e;
-            float y = 0.f;
-            for (int a = 0; a < D; ++a) y += Pn[r * D + a] * Hs[c * HS + a];
-            g += dov[e] * y / den;
+        for (int e = 0; e < 8; ++e) {
+            ph[e] *= ise;
+            den += ph[e] * zf[e];
         }
-        g = wave_sum(g);
-        // dphi[a] = (sum_c H[c][a] dO_c - g Z[a]) / den (this lane's a)
-        float dph[CPL], pd = 0.f;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int a = lane + 64 * e;
-            float x = 0.f;
-            for (int c = 0; c < D; ++c) x += Hs[c * HS + a] * Do[r * D + c];
-            dph[e] = (x - g * Zs[a]) / den;
-            pd += ph[e] * dph[e];
-        }
-        pd = wave_sum(pd);
-        float *qg = dq + (bh * N + row) * (long)D;
+        for (int o = 1; o < CPR; o <<= 1) den += __shfl_xor(den, o);
+        const float inv = ok ? 1.f / den : 0.f;
+        f16 pn[8];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) qg[lane + 64 * e] += ph[e] * (dph[e] - pd);
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        for (int e = 0; e < 8; ++e) pn[e] = (f16)(ph[e] * inv);
+        __builtin_memcpy(&Pn[r * STR + 8 * p], pn, sizeof(pn));
+        if (p == 0) Dn[r] = ok ? den : 1.f;
+        const bf16 *dx = reinterpret_cast<const bf16 *>(&dc[n]);
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) Pn[r * D + lane + 64 * e] = ph[e] / den;
-        if (lane == 0) Gr[r] = g;
+        for (int e = 0; e < 8; ++e) dmax = fmaxf(dmax, fabsf((float)dx[e]));
+    }
+    dmax = wave_max(dmax);
+    if (lane == 0) Red[wave] = dmax;
+    __syncthreads();
+    const float sc = pow2_scale(fmaxf(fmaxf(Red[0], Red[1]), fmaxf(Red[2], Red[3])));
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+        const int r = RPP * n + tid / CPR;
+        const bf16 *dx = reinterpret_cast<const bf16 *>(&dc[n]);
+        f16 ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds[e] = (f16)((float)dx[e] * sc);
+        __builtin_memcpy(&Ds[r * STR + 8 * p], ds, sizeof(ds));
     }
     __syncthreads();
-    // dĤ'[c][a] = (1/m) sum_r Pn[r][a] Do[r][c]; wave w: a = lane + 64 (w & 1) ... per D
-    const float inv_m = 1.f / (float)mc;
-    constexpr int AW = D / 64;                           // waves along a
-    constexpr int CB = D / (4 / AW);                     // c's per wave
-    const int a = lane + 64 * (wave % AW);
-    const int c0 = (wave / AW) * CB;
-    float acc[CB];
+
+    // 2. y^T and s X^T for the wave's channel half and token half
+    const int rh = wave & 1, chh = wave >> 1;
+    const int r = 32 * rh + l32;                         // this lane's token
+    f32x16 yt[NCT], xt[NCT];
 #pragma unroll
-    for (int x = 0; x < CB; ++x) acc[x] = 0.f;
-    float zacc = 0.f;
-    for (int r = 0; r < 64; ++r) {
-        const float p = Pn[r * D + a];
+    for (int mt = 0; mt < NCT; ++mt)
 #pragma unroll
-        for (int x = 0; x < CB; ++x) acc[x] += p * Do[r * D + c0 + x];
-        zacc += Gr[r] * p;
+        for (int x = 0; x < 16; ++x) yt[mt][x] = xt[mt][x] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        const int k0 = 16 * s + 8 * hh;
+        const v8<f16> bp = ld8<f16>(&Pn[r * STR + k0]);
+        const v8<f16> bd = ld8<f16>(&Ds[r * STR + k0]);
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt) {
+            const int t0 = (D / 2) * chh + 32 * mt, n0 = t0 + 16 * (grp & 1);
+            mma16(yt[mt], ld8<f16>(&Hs[(t0 + l32) * STR + k0]), bp);
+            mma16(xt[mt], cat8<f16>(lds_col4<f16>(Hs, STR, k0, n0, lane), lds_col4<f16>(Hs, STR, k0 + 4, n0, lane)), bd);
+        }
     }
+    // lane (r, hh) holds channels 64 ch + 32 mt + 8 g + 4 hh + 0..3 of token r
+    float gp = 0.f;
 #pragma unroll
-    for (int x = 0; x < CB; ++x) drow[(c0 + x) * D + a] = acc[x] * inv_m;
-    if (wave / AW == 0) drow[D * D + a] = -zacc * inv_m;
+    for (int mt = 0; mt < NCT; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const v4<f16> dd = ld4<f16>(&Ds[r * STR + (D / 2) * chh + 32 * mt + 8 * g + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gp += (float)dd[e] * yt[mt][4 * g + e];
+        }
+    gp = half_swap_sum(gp);
+    if (hh == 0) Gx[chh][r] = gp;
+    __syncthreads();
+    const float gs = Gx[0][r] + Gx[1][r];                // s g_r
+    v4<f16> pn4[NCT][4];
+    float tp = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NCT; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int a0 = (D / 2) * chh + 32 * mt + 8 * g + 4 * hh;
+            pn4[mt][g] = ld4<f16>(&Pn[r * STR + a0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xt[mt][4 * g + e] -= gs * Zs[a0 + e];    // s e_a
+                tp += (float)pn4[mt][g][e] * xt[mt][4 * g + e];
+            }
+        }
+    tp = half_swap_sum(tp);
+    if (hh == 0) {
+        Tx[chh][r] = tp;
+        if (chh == 0) Gr[r] = gs / sc;
+    }
+    __syncthreads();
+    const float dts = Dn[r] * (Tx[0][r] + Tx[1][r]), isc = 1.f / sc;
+    const int row = 64 * i + r;
+    if (row < N) {
+        float *qg = dq + (bh * N + row) * (long)D;
+#pragma unroll
+        for (int mt = 0; mt < NCT; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int a0 = (D / 2) * chh + 32 * mt + 8 * g + 4 * hh;
+                f32x4 cur = *reinterpret_cast<const f32x4 *>(qg + a0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cur[e] += (float)pn4[mt][g][e] * (xt[mt][4 * g + e] - dts) * isc;
+                *reinterpret_cast<f32x4 *>(qg + a0) = cur;
+            }
+    }
+
+    // 3. dĤ'[c][a] = sum_r dO[r][c] Pn[r][a] / m: tiles (ct, at), K = the 64 tokens
+    const float osc = 1.f / ((float)mc * sc), inv_m = 1.f / (float)mc;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int x = wave * TPW + t, ct = x / (D / 32), at = x % (D / 32);
+        const int nc = 32 * ct + 16 * (grp & 1), na = 32 * at + 16 * (grp & 1);
+        f32x16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int k0 = 16 * s + 8 * hh;
+            mma16(acc, cat8<f16>(lds_col4<f16>(Ds, STR, k0, nc, lane), lds_col4<f16>(Ds, STR, k0 + 4, nc, lane)),
+                  cat8<f16>(lds_col4<f16>(Pn, STR, k0, na, lane), lds_col4<f16>(Pn, STR, k0 + 4, na, lane)));
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int c = 32 * ct + 8 * (e >> 2) + 4 * hh + (e & 3);
+            split_store(hi, lo, (long)c * D + 32 * at + l32, acc[e] * osc);
+        }
+    }
+    if (tid < D) {
+        float z = 0.f;
+        for (int r2 = 0; r2 < 64; ++r2) z += Gr[r2] * (float)Pn[r2 * STR + tid];
+        split_store(hi, lo, D * D + tid, -z * inv_m);
+    }
+    for (int x = D * D + D + tid; x < Lp; x += 256) hi[x] = lo[x] = (bf16)0.f;
 }
 
-// One workgroup per key block j, persistent over a stride of blocks so that
-// dW is added once per workgroup.  W and dh' (stored [c][a]) live in LDS
-// with padded rows; the 64 rows of a block go in four passes of 16.
+// Linear part, keys: persistent workgroups of D/16 waves over the key blocks
+// j (W as f16 in LDS once per workgroup; dW summed in registers and added
+// once at the end).  Per block, with dh'_j (stored [c][a]) times a power of
+// two s as f16 in LDS:
+//  1. VALU: phi(k_u) and v_u as f16 rows.
+//  2. matrix core, wave (x, ut), x a 32-channel tile, ut a 32-token half:
+//     v'^T = W V^T and s dv'^T = (s dh') phi^T, both to LDS as rows [u][c].
+//  3. matrix core: s dphi^T = (s dh')^T v'^T (a tile x), s dv^T = W^T s dv'^T
+//     (e tile x), dW tiles += s dv'^T V / s; VALU: dphi = (.)/s + dz,
+//     pd = phi.dphi (tiles summed through LDS), dk += phi (dphi - pd),
+//     dv += (.)/s.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_lin_key_kernel(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-                                                          const float *__restrict__ w, const float *__restrict__ dhs,
-                                                          int Lp, float *__restrict__ dk, float *__restrict__ dv,
-                                                          float *__restrict__ dw, long BH, int N, int Nb) {
-    constexpr int CPL = D / 64;
-    constexpr int HS = D + 1;
-    constexpr int RB = 16;                               // rows per pass
-    __shared__ float Wl[D * HS];
-    __shared__ float Dh[D * HS];
-    __shared__ float Dz[D];
-    __shared__ float Ph[RB * D];                         // phi(k_u)
-    __shared__ float Vr[RB * D];                         // v_u
-    __shared__ float Vp[RB * D];                         // v'_u = W v_u, then dv'_u
+__global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+                                                            const float *__restrict__ w, const float *__restrict__ dhs,
+                                                            int Lp, float *__restrict__ dk, float *__restrict__ dv,
+                                                            float *__restrict__ dw, long BH, int N, int Nb) {
+    constexpr int NT = 4 * D, NW = NT / 64;              // threads, waves (2 tiles of tokens x D/32 of channels)
+    constexpr int STR = D + 8;
+    constexpr int CPR = D / 8, RPP = NT / CPR, NP = 64 / RPP;
+    constexpr int HPT = D * D / 4 / NT;                  // float4 of dh' per thread
+    constexpr int TPW = (D / 32) * (D / 32) / NW;        // dW tiles per wave
+    __shared__ __attribute__((aligned(16))) f16 Wh[D * STR];
+    __shared__ __attribute__((aligned(16))) f16 Dh[D * STR];
+    __shared__ __attribute__((aligned(16))) f16 Pk[64 * STR];
+    __shared__ __attribute__((aligned(16))) f16 Vs[64 * STR];
+    __shared__ __attribute__((aligned(16))) f16 Vp[64 * STR];
+    __shared__ __attribute__((aligned(16))) f16 Dv[64 * STR];
+    __shared__ float Dz[D], Px[D / 32][64], Red[NW];
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int x = tid; x < D * D; x += 256) Wl[(x / D) * HS + (x % D)] = w[x];
-    constexpr int WC = D * D / 256;                      // dW accumulators: (c block, e = tid % D)
-    const int we = tid % D, wc0 = (tid / D) * WC;
-    float wacc[WC];
+    const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
+    const int ut = wave & 1, xt = wave >> 1, u = 32 * ut + l32;
+    const int p = tid % CPR;
+    for (int x = tid; x < D * D; x += NT) Wh[(x / D) * STR + x % D] = (f16)w[x];
+    f32x16 wacc[TPW];
 #pragma unroll
-    for (int x = 0; x < WC; ++x) wacc[x] = 0.f;
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wacc[t][e] = 0.f;
     const long total = BH * Nb;
     for (long blk = blockIdx.x; blk < total; blk += gridDim.x) {
         const long bh = blk / Nb;
         const int j = (int)(blk % Nb);
         const float *hrow = dhs + blk * (long)Lp;
+        __syncthreads();                                 // the previous block's reads of the tiles are done
+        f32x4 hv[HPT];
+        float hmax = 0.f;
+#pragma unroll
+        for (int x = 0; x < HPT; ++x) {
+            hv[x] = *reinterpret_cast<const f32x4 *>(hrow + 4 * (tid + NT * x));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hmax = fmaxf(hmax, fabsf(hv[x][e]));
+        }
+        if (tid < D) Dz[tid] = hrow[D * D + tid];
+        // 1. phi(k_u), v_u
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            const int r = RPP * n + tid / CPR, row = 64 * j + r;
+            const bool ok = row < N;
+            const long base = (bh * N + row) * (long)D + 8 * p;
+            const Chunk kc = ok ? ld_chunk(k + base) : zero_chunk();
+            const Chunk vc = ok ? ld_chunk(v + base) : zero_chunk();
+            const bf16 *kx = reinterpret_cast<const bf16 *>(&kc);
+            const bf16 *vx = reinterpret_cast<const bf16 *>(&vc);
+            float ph[8], mx = NEG_INF_B;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[e] = (float)kx[e];
+                mx = fmaxf(mx, ph[e]);
+            }
+#pragma unroll
+            for (int o = 1; o < CPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            float se = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[e] = __expf(ph[e] - mx);
+                se += ph[e];
+            }
+#pragma unroll
+            for (int o = 1; o < CPR; o <<= 1) se += __shfl_xor(se, o);
+            const float ise = ok ? 1.f / se : 0.f;
+            f16 pk[8], vv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pk[e] = (f16)(ph[e] * ise);
+                vv[e] = (f16)(float)vx[e];
+            }
+            __builtin_memcpy(&Pk[r * STR + 8 * p], pk, sizeof(pk));
+            __builtin_memcpy(&Vs[r * STR + 8 * p], vv, sizeof(vv));
+        }
+        hmax = wave_max(hmax);
+        if (lane == 0) Red[wave] = hmax;
         __syncthreads();
-        for (int x = tid; x < D * D; x += 256) Dh[(x / D) * HS + (x % D)] = hrow[x];
-        for (int x = tid; x < D; x += 256) Dz[x] = hrow[D * D + x];
-        for (int pass = 0; pass < 64 / RB; ++pass) {
-            __syncthreads();
-            // rows of this pass: phi(k_u), v_u (wave w: rows 4w .. 4w+3)
-            for (int rr = 0; rr < RB / 4; ++rr) {
-                const int r = (RB / 4) * wave + rr;
-                const int row = 64 * j + RB * pass + r;
-                if (row < N) {
-                    const long base = (bh * N + row) * (long)D;
-                    float kv[CPL], mx = NEG_INF_B;
+        float bm = Red[0];
 #pragma unroll
-                    for (int e = 0; e < CPL; ++e) {
-                        kv[e] = to_f32<bf16>(k[base + lane + 64 * e]);
-                        Vr[r * D + lane + 64 * e] = to_f32<bf16>(v[base + lane + 64 * e]);
-                        mx = fmaxf(mx, kv[e]);
-                    }
-                    mx = wave_max(mx);
-                    float se = 0.f;
+        for (int x = 1; x < NW; ++x) bm = fmaxf(bm, Red[x]);
+        const float sc = pow2_scale(bm), isc = 1.f / sc;
 #pragma unroll
-                    for (int e = 0; e < CPL; ++e) {
-                        kv[e] = __expf(kv[e] - mx);
-                        se += kv[e];
-                    }
-                    se = wave_sum(se);
+        for (int x = 0; x < HPT; ++x) {
+            const int e0 = 4 * (tid + NT * x);
+            v4<f16> h;
 #pragma unroll
-                    for (int e = 0; e < CPL; ++e) Ph[r * D + lane + 64 * e] = kv[e] / se;
-                } else {
+            for (int e = 0; e < 4; ++e) h[e] = (f16)(hv[x][e] * sc);
+            __builtin_memcpy(&Dh[(e0 / D) * STR + e0 % D], &h, sizeof(h));
+        }
+        __syncthreads();
+
+        // 2. v'^T and s dv'^T, channel tile xt, tokens of half ut
+        {
+            f32x16 av, ad;
 #pragma unroll
-                    for (int e = 0; e < CPL; ++e) {
-                        Ph[r * D + lane + 64 * e] = 0.f;
-                        Vr[r * D + lane + 64 * e] = 0.f;
-                    }
+            for (int e = 0; e < 16; ++e) av[e] = ad[e] = 0.f;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const int k0 = 16 * s + 8 * hh;
+                mma16(av, ld8<f16>(&Wh[(32 * xt + l32) * STR + k0]), ld8<f16>(&Vs[u * STR + k0]));
+                mma16(ad, ld8<f16>(&Dh[(32 * xt + l32) * STR + k0]), ld8<f16>(&Pk[u * STR + k0]));
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = 32 * xt + 8 * g + 4 * hh;
+                v4<f16> y1, y2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y1[e] = (f16)av[4 * g + e];
+                    y2[e] = (f16)ad[4 * g + e];
                 }
+                __builtin_memcpy(&Vp[u * STR + c0], &y1, sizeof(y1));
+                __builtin_memcpy(&Dv[u * STR + c0], &y2, sizeof(y2));
             }
-            __syncthreads();
-            // v'_u[c] = sum_e W[c][e] v_u[e]: thread (c = tid % D, rows tid / D + (256 / D) n)
-            for (int r = tid / D; r < RB; r += 256 / D) {
-                const int c = tid % D;
-                float x = 0.f;
-                for (int e = 0; e < D; ++e) x += Wl[c * HS + e] * Vr[r * D + e];
-                Vp[r * D + c] = x;
-            }
-            __syncthreads();
-            // dphi[a] = sum_c dh[c][a] v'[c] + dz[a]; dk += phi * (dphi - phi . dphi)
-            for (int rr = 0; rr < RB / 4; ++rr) {
-                const int r = (RB / 4) * wave + rr;
-                const int row = 64 * j + RB * pass + r;
-                if (row >= N) continue;
-                float dph[CPL], pd = 0.f;
+        }
+        __syncthreads();
+
+        // 3. s dphi^T (a tile xt), s dv^T (e tile xt), dW tiles
+        f32x16 ap, aq;
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) {
-                    const int a = lane + 64 * e;
-                    float x = Dz[a];
-                    for (int c = 0; c < D; ++c) x += Dh[c * HS + a] * Vp[r * D + c];
-                    dph[e] = x;
-                    pd += Ph[r * D + a] * x;
+        for (int e = 0; e < 16; ++e) ap[e] = aq[e] = 0.f;
+        const int n0 = 32 * xt + 16 * (grp & 1);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const int k0 = 16 * s + 8 * hh;
+            mma16(ap, cat8<f16>(lds_col4<f16>(Dh, STR, k0, n0, lane), lds_col4<f16>(Dh, STR, k0 + 4, n0, lane)),
+                  ld8<f16>(&Vp[u * STR + k0]));
+            mma16(aq, cat8<f16>(lds_col4<f16>(Wh, STR, k0, n0, lane), lds_col4<f16>(Wh, STR, k0 + 4, n0, lane)),
+                  ld8<f16>(&Dv[u * STR + k0]));
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int x = wave * TPW + t, ct = x / (D / 32), et = x % (D / 32);
+            const int nc = 32 * ct + 16 * (grp & 1), ne = 32 * et + 16 * (grp & 1);
+            f32x16 tmp;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tmp[e] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k0 = 16 * s + 8 * hh;
+                mma16(tmp, cat8<f16>(lds_col4<f16>(Dv, STR, k0, nc, lane), lds_col4<f16>(Dv, STR, k0 + 4, nc, lane)),
+                      cat8<f16>(lds_col4<f16>(Vs, STR, k0, ne, lane), lds_col4<f16>(Vs, STR, k0 + 4, ne, lane)));
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) wacc[t][e] += tmp[e] * isc;
+        }
+        // lane (u, hh) holds channels 32 xt + 8 g + 4 hh + 0..3 of token u
+        v4<f16> ph4[4];
+        float pp = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int a0 = 32 * xt + 8 * g + 4 * hh;
+            ph4[g] = ld4<f16>(&Pk[u * STR + a0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ap[4 * g + e] = ap[4 * g + e] * isc + Dz[a0 + e];
+                pp += (float)ph4[g][e] * ap[4 * g + e];
+            }
+        }
+        pp = half_swap_sum(pp);
+        if (hh == 0) Px[xt][u] = pp;
+        __syncthreads();
+        float pd = 0.f;
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) pd += Px[x][u];
+        const int row = 64 * j + u;
+        if (row < N) {
+            float *kg = dk + (bh * N + row) * (long)D;
+            float *vg = dv + (bh * N + row) * (long)D;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int a0 = 32 * xt + 8 * g + 4 * hh;
+                f32x4 ck = *reinterpret_cast<const f32x4 *>(kg + a0);
+                f32x4 cv = *reinterpret_cast<const f32x4 *>(vg + a0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ck[e] += (float)ph4[g][e] * (ap[4 * g + e] - pd);
+                    cv[e] += aq[4 * g + e] * isc;
                 }
-                pd = wave_sum(pd);
-                float *kg = dk + (bh * N + row) * (long)D;
-#pragma unroll
-                for (int e = 0; e < CPL; ++e) {
-                    const int a = lane + 64 * e;
-                    kg[a] += Ph[r * D + a] * (dph[e] - pd);
-                }
-            }
-            __syncthreads();
-            // dv'_u[c] = sum_a phi_a dh[c][a], kept in Vp
-            for (int r = tid / D; r < RB; r += 256 / D) {
-                const int c = tid % D;
-                float x = 0.f;
-                for (int a = 0; a < D; ++a) x += Ph[r * D + a] * Dh[c * HS + a];
-                Vp[r * D + c] = x;
-            }
-            __syncthreads();
-            // dv_u[e] += sum_c dv'_u[c] W[c][e]
-            for (int r = tid / D; r < RB; r += 256 / D) {
-                const int e = tid % D;
-                const int row = 64 * j + RB * pass + r;
-                if (row >= N) continue;
-                float x = 0.f;
-                for (int c = 0; c < D; ++c) x += Vp[r * D + c] * Wl[c * HS + e];
-                dv[(bh * N + row) * (long)D + e] += x;
-            }
-            // dW[c][e] += sum_u dv'_u[c] v_u[e]
-            for (int r = 0; r < RB; ++r) {
-                const float ve = Vr[r * D + we];
-#pragma unroll
-                for (int x = 0; x < WC; ++x) wacc[x] += Vp[r * D + wc0 + x] * ve;
+                *reinterpret_cast<f32x4 *>(kg + a0) = ck;
+                *reinterpret_cast<f32x4 *>(vg + a0) = cv;
             }
         }
     }
 #pragma unroll
-    for (int x = 0; x < WC; ++x) atomicAdd(&dw[(wc0 + x) * D + we], wacc[x]);
+    for (int t = 0; t < TPW; ++t) {
+        const int x = wave * TPW + t, ct = x / (D / 32), et = x % (D / 32);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            atomicAdd(&dw[(32 * ct + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + 32 * et + l32], wacc[t][e]);
+    }
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -722,8 +918,7 @@ hipError_t launch_backward_dq(const BackwardArgs &a, hipStream_t st) {
     const long Gq = a.BH * a.Nb;
     const int per = (int)((Gq + 7) / 8);
     const float sl2 = 1.4426950408889634f / sqrtf((float)a.D), scale = 1.f / sqrtf((float)a.D);
-    const unsigned g1 = (unsigned)((a.BH * a.Nb + 255) / 256);
-    bwd_tlists_kernel<<<g1, 256, 0, st>>>(a.mask, a.BH, a.Nb, a.tlist, a.tcnt);
+    bwd_tlists_kernel<<<(unsigned)((a.BH * a.Nb + 3) / 4), 256, 0, st>>>(a.mask, a.BH, a.Nb, a.tlist, a.tcnt);
     if (a.D == 64)
         bwd_dq_kernel<64><<<(unsigned)(8L * per), 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
             (const bf16 *)a.dout, a.o_s, a.lse, a.crit, a.kc, a.dq, a.dbuf, Gq, per, a.N, a.Nb, sl2, scale);
@@ -747,22 +942,24 @@ hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st) {
-    // zero dW, the transposed indicator and its unit counts
+    // zero dW; the transposed indicator bits and unit counts
     bwd_zero_kernel<<<(unsigned)((a.D * a.D + 255) / 256), 256, 0, st>>>(a.dw, (long)a.D * a.D);
-    const long nt = a.BH * a.Nb * (long)a.Nbc;
-    bwd_margT_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, st>>>(a.mask, a.BH, a.Nb, a.Nbc, a.margT, a.unit);
+    const long nt = a.BH * (2 * a.Nbc / 32) * (long)a.Nbp;
+    bwd_mbitsT_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, st>>>(a.mask, a.BH, a.Nb, a.Nbc, a.Nbp, a.mbitsT, a.unit);
     const unsigned rows = (unsigned)(a.BH * a.Nbc);
     if (a.D == 64)
         bwd_lin_row_kernel<64><<<rows, 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.dout, (const f16 *)a.hhat,
-                                                     a.mcount, a.Lp, a.dq, a.dhrow, a.BH, a.N, a.Nb, a.Nbc);
+                                                     a.mcount, a.Lp, a.dq, (bf16 *)a.dh2, a.BH, a.N, a.Nb, a.Nbc);
     else
         bwd_lin_row_kernel<128><<<rows, 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.dout, (const f16 *)a.hhat,
-                                                      a.mcount, a.Lp, a.dq, a.dhrow, a.BH, a.N, a.Nb, a.Nbc);
+                                                      a.mcount, a.Lp, a.dq, (bf16 *)a.dh2, a.BH, a.N, a.Nb, a.Nbc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // dh'_j = sum over the query blocks i with j marginal of (hi_i + lo_i):
+    // the 0/1 product over the 2 Nbc rows of hi and lo pairs
     AssembleArgs as{};
-    as.marg = a.margT; as.hs = a.dhrow; as.mcount = a.unit; as.hhat = a.dhs;
-    as.BH = a.BH; as.Nb = a.Nb; as.Nbc = a.Nbc; as.Nbp = a.Nbc; as.Lp = a.Lp; as.f32 = true;
+    as.mbits = a.mbitsT; as.hs = a.dh2; as.mcount = a.unit; as.hhat = a.dhs;
+    as.BH = a.BH; as.Nb = a.Nb; as.Nbc = 2 * a.Nbc; as.Nbp = a.Nbp; as.Lp = a.Lp; as.bf16_f32 = true;
     return launch_assemble(as, st);
 }
 
@@ -770,13 +967,14 @@ hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st) {
     int dev = 0, cus = 0;
     hipGetDevice(&dev);
     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const unsigned gk = (unsigned)std::min<long>(a.BH * a.Nb, (long)std::max(cus, 1));
+    const long per_cu = a.D == 64 ? 2 : 1;               // workgroups that fit a compute unit's LDS
+    const unsigned gk = (unsigned)std::min<long>(a.BH * a.Nb, per_cu * std::max(cus, 1));
     if (a.D == 64)
         bwd_lin_key_kernel<64><<<gk, 256, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk, a.dv,
                                                    a.dw, a.BH, a.N, a.Nb);
     else
-        bwd_lin_key_kernel<128><<<gk, 256, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk, a.dv,
-                                                    a.dw, a.BH, a.N, a.Nb);
+        bwd_lin_key_kernel<128><<<gk, 512, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk,
+                                                    a.dv, a.dw, a.BH, a.N, a.Nb);
     return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@ struct AssembleArgs {
     long BH;
     int Nb, Nbc, Nbp, Lp;
     bool f32;
+    bool bf16_f32;           // bf16 states, bits indicator, float output (no row scale with counts of 64)
 };
 
 struct FusedArgs {
@@ -104,12 +105,12 @@ struct BackwardArgs {
     float *dbuf;                      // [BH][N] D_r = dO_r . O_s,r
     uint16_t *tlist;                  // [BH][Nb][Nb] transposed critical lists
     int32_t *tcnt;                    // [BH][Nb]
-    float *margT;                     // [BH][Nb][Nbc] transposed marginal indicator
+    uint32_t *mbitsT;                 // [BH][2 Nbc / 32][Nbp] transposed marginal indicator bits
     int32_t *unit;                    // [BH][Nb] = 64
-    float *dhrow;                     // [BH][Nbc][Lp] per-row state gradients
+    void *dh2;                        // [BH][2 Nbc][Lp] bf16 per-row state gradients (hi rows, then lo rows)
     float *dhs;                       // [BH][Nb][Lp] per-key-block state gradients
     long BH;
-    int N, Nb, Nbc, Lp, D;
+    int N, Nb, Nbc, Nbp, Lp, D;
 };
 hipError_t launch_backward_dq(const BackwardArgs &a, hipStream_t st);        // transposed lists + dQ (sparse)
 hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st);       // dK, dV (sparse)

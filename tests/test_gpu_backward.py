@@ -62,3 +62,25 @@ def test_backward_matches_oracle(sla, B, H, N, d, rc, rn):
         assert np.isfinite(g).all()
         worst = max(worst, rel)
     assert worst <= 1e-2
+
+
+@pytest.mark.parametrize("gscale", [2.0 ** -40, 2.0 ** 20])
+def test_backward_gradient_scale(sla, gscale):
+    """The same bar for an output gradient scaled far from 1: the linear
+    part's f16 operands take a power-of-two scale per block, so the relative
+    error does not depend on the gradient's magnitude."""
+    B, H, N, d, rc, rn = 1, 1, 1100, 128, 0.1, 0.2
+    say("backward scale", gscale)
+    inp = make_inputs(B, H, (1, 1, N), d, "bf16", seed=31)
+    rng = np.random.default_rng(32)
+    dout = round_bf16((rng.standard_normal((B, H, N, d)) * gscale).astype(np.float32))
+    mask = orc.classify(orc.pool(inp.q), orc.pool(inp.k), rc, rn)["mask"]
+    _, rq, rk, rv, rw = ob.gradients(inp.q, inp.k, inp.v, inp.w, mask, dout)
+    w = torch.from_numpy(inp.w).cuda()
+    dq, dk, dv, dw = sla.backward(dev(inp.q), dev(inp.k), dev(inp.v), w, dev(dout), rc, rn)
+    torch.cuda.synchronize()
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)):
+        g = got.double().cpu().numpy()
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        say("  %s rel %.3g" % (name, rel))
+        assert np.isfinite(g).all() and rel <= 1e-2

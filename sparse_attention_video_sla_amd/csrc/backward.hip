@@ -91,31 +91,37 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float *__restrict__ p, lo
 
 namespace {
 
-// 1 KB block u of this wave's share of a 64 x D tile: source offsets of its
-// lane in the K layout (rows of 2D bytes, 16-byte chunks swizzled) and the V
-// layout (groups of 4 rows, chunk-major inside a group)
+// 1 KB block u of this wave's share of a 64 x D tile: source offset of its
+// lane in the K layout (rows of 2D bytes, 16-byte chunks swizzled)
 template <int D> __device__ __forceinline__ uint32_t off_klayout(int byte) {
     const int r = byte / (2 * D), pk = (byte % (2 * D)) / 16;
     return (uint32_t)(r * 2 * D + (pk ^ kswz<D>(r)) * 16);
 }
-template <int D> __device__ __forceinline__ uint32_t off_vlayout(int byte) {
-    const int g = byte / (8 * D), qv = (byte % (8 * D)) / 16;
-    return (uint32_t)((4 * g + (qv & 3)) * 2 * D + (qv >> 2) * 16);
+// Transposing reads of a K-layout tile as the A operand [channel][row] of
+// rows 32 half .. +31, rows in the accumulator order of a 32 x 32 tile: k
+// slot e of step ks is row 16 ks + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4).
+// Lane L of a 16-lane group points at row 8 x + 4 hh + L / 4 of the step and
+// channels 32 ct + 16 (group & 1) + 4 (L % 4) .. +3, found through the
+// row's chunk swizzle (which only depends on the row modulo 16).
+template <int D> __device__ __forceinline__ void tr_offsets(int lane, int (&toff)[D / 32][2]) {
+    const int grp = lane >> 4, L = lane & 15, hh = lane >> 5;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int rr = 8 * x + 4 * hh + (L >> 2);
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct)
+            toff[ct][x] = rr * D + ((4 * ct + 2 * (grp & 1) + ((L & 3) >> 1)) ^ kswz<D>(rr)) * 8 + 4 * (L & 1);
+    }
 }
-// transposing reads of rows 32*half .. +31 of a V-layout tile as the A
-// operand [channel][row], rows in the accumulator order of a 32 x 32 tile
 template <typename T, int D>
-__device__ __forceinline__ void read_tr(const T *tile, int vb, v8<T> (&a)[D / 32][2]) {
-    const T *Vs = tile + vb;
+__device__ __forceinline__ void read_tr(const T *tile, int half, const int (&toff)[D / 32][2], v8<T> (&a)[D / 32][2]) {
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            a[ct][ks] = cat8<T>(lds_tr_raw<T>(Vs + ks * 16 * D + ct * 128), lds_tr_raw<T>(Vs + ks * 16 * D + 8 * D + ct * 128));
-}
-__device__ __forceinline__ int vbase_of(int half, int lane, int D) {
-    const int grp = lane >> 4, L = lane & 15;
-    return ((8 * half + (grp >> 1)) * 8 * D + ((2 * (grp & 1) + ((L & 3) >> 1)) * 4 + (L >> 2)) * 16 + (L & 1) * 8) / 2;
+        for (int ks = 0; ks < 2; ++ks) {
+            const T *base = tile + (32 * half + 16 * ks) * D;
+            a[ct][ks] = cat8<T>(lds_tr_raw<T>(base + toff[ct][0]), lds_tr_raw<T>(base + toff[ct][1]));
+        }
 }
 
 }  // namespace
@@ -123,10 +129,11 @@ __device__ __forceinline__ int vbase_of(int half, int lane, int D) {
 // One workgroup of 4 waves per query block i: wave (rh, kh) takes query rows
 // 32rh .. +31 against key half kh of every critical block.  Per block: S^T =
 // K Q^T and dP^T = V dO^T on the matrix core (K, V rows from LDS, Q and dO
-// in registers), dS^T in the VALU, dQ^T += K^T dS^T (transposing reads of K).
-// Tiles go global -> LDS through a two-slot ring, one barrier per block.
+// in registers), dS^T in the VALU, dQ^T += K^T dS^T (transposing reads of the
+// same K tile).  Tiles go global -> LDS through a two-slot ring, one barrier
+// per block; 64 KB of LDS lets two workgroups share a compute unit.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                                         const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
                                                         const float *__restrict__ o_s, const float *__restrict__ lse,
                                                         const int32_t *__restrict__ crit, int kc,
@@ -135,7 +142,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const bf16 *__restrict__
     using T = bf16;
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
     __shared__ __attribute__((aligned(1024))) T Kk[2][TILE];
-    __shared__ __attribute__((aligned(1024))) T Kv[2][TILE];
     __shared__ __attribute__((aligned(1024))) T Vk[2][TILE];
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
@@ -168,14 +174,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const bf16 *__restrict__
         const int r = 32 * kh + l32;
         koff[s] = r * D + ((2 * s + hh) ^ kswz<D>(r)) * 8;
     }
-    const int vb = vbase_of(kh, lane, D);
-    uint32_t ok_[NBW], ov_[NBW];
+    int toff[NCT][2];
+    tr_offsets<D>(lane, toff);
+    uint32_t ok_[NBW];
 #pragma unroll
-    for (int u = 0; u < NBW; ++u) {
-        const int byte = (wave * NBW + u) * 1024 + 16 * lane;
-        ok_[u] = off_klayout<D>(byte);
-        ov_[u] = off_vlayout<D>(byte);
-    }
+    for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
     const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * N * (long)D, head_bytes);
@@ -185,7 +188,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const bf16 *__restrict__
 #pragma unroll
         for (int u = 0; u < NBW; ++u) {
             dma16(rk, &Kk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
-            dma16(rk, &Kv[slot][(wave * NBW + u) * 512], ov_[u] + off, 0);
             dma16(rv, &Vk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
         }
     };
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const bf16 *__restrict__
             dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - Dr));
         }
         v8<T> at[NCT][2];
-        read_tr<T, D>(Kv[slot], vb, at);
+        read_tr<T, D>(Kk[slot], kh, toff, at);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const bf16 *__restrict__
 // +31 against query rows 32rh .. +31 of every query block that chose j.  Per
 // query block: S = Q K^T and dP = dO V^T on the matrix core (Q, dO rows from
 // LDS, K and V rows in registers), dS in the VALU, dV^T += dO^T P and dK^T +=
-// Q^T dS (transposing reads of dO and Q).
+// Q^T dS (transposing reads of the same dO and Q tiles).
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                                          const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
@@ -296,9 +298,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
     using T = bf16;
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
     __shared__ __attribute__((aligned(1024))) T Qk[2][TILE];
-    __shared__ __attribute__((aligned(1024))) T Qv[2][TILE];
     __shared__ __attribute__((aligned(1024))) T Ok[2][TILE];
-    __shared__ __attribute__((aligned(1024))) T Ov[2][TILE];
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
     const long bh = logical / Nb;
@@ -321,14 +321,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
         const int r = 32 * rh + l32;
         koff[s] = r * D + ((2 * s + hh) ^ kswz<D>(r)) * 8;
     }
-    const int vb = vbase_of(rh, lane, D);
-    uint32_t ok_[NBW], ov_[NBW];
+    int toff[NCT][2];
+    tr_offsets<D>(lane, toff);
+    uint32_t ok_[NBW];
 #pragma unroll
-    for (int u = 0; u < NBW; ++u) {
-        const int byte = (wave * NBW + u) * 1024 + 16 * lane;
-        ok_[u] = off_klayout<D>(byte);
-        ov_[u] = off_vlayout<D>(byte);
-    }
+    for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
     const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + bh * N * (long)D, head_bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(dout + bh * N * (long)D, head_bytes);
@@ -339,9 +336,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
 #pragma unroll
         for (int u = 0; u < NBW; ++u) {
             dma16(rq, &Qk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
-            dma16(rq, &Qv[slot][(wave * NBW + u) * 512], ov_[u] + off, 0);
             dma16(ro, &Ok[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
-            dma16(ro, &Ov[slot][(wave * NBW + u) * 512], ov_[u] + off, 0);
         }
     };
     f32x16 dvt[NCT], dkt[NCT];
@@ -379,12 +374,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
             dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - dr[r]));
         }
         v8<T> at[NCT][2];
-        read_tr<T, D>(Ov[slot], vb, at);
+        read_tr<T, D>(Ok[slot], rh, toff, at);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) mma16(dvt[ct], at[ct][ks], pb[ks]);
-        read_tr<T, D>(Qv[slot], vb, at);
+        read_tr<T, D>(Qk[slot], rh, toff, at);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll

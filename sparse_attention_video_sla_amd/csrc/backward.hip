@@ -282,13 +282,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
     }
 }
 
-// One workgroup of 4 waves per key block j: wave (kh, rh) takes keys 32kh ..
-// +31 against query rows 32rh .. +31 of every query block that chose j.  Per
-// query block: S = Q K^T and dP = dO V^T on the matrix core (Q, dO rows from
-// LDS, K and V rows in registers), dS in the VALU, dV^T += dO^T P and dK^T +=
-// Q^T dS (transposing reads of the same dO and Q tiles).
+// One workgroup of 4 waves per key block j, two workgroups per compute unit.
+// Per query block i of j's list, in two steps with a barrier between them:
+//   produce, wave (kh, rh): keys 32kh .. +31 against query rows 32rh .. +31:
+//     S = Q K^T and dP = dO V^T on the matrix core (Q, dO rows from LDS, K
+//     and V rows in registers), P and dS = P (dP - D) in the VALU, written as
+//     bf16 MFMA operands to the wave's LDS slot;
+//   consume, wave (kh, ch): for both row halves, dV^T += dO^T P and dK^T +=
+//     Q^T dS for the channels of half ch (transposing reads of the same dO
+//     and Q tiles, P and dS from the producers' slots).
+// Each wave thus owns a quarter of dK and dV, so no partial sums are merged.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                                          const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
                                                          const float *__restrict__ lse, const float *__restrict__ dbuf,
                                                          const uint16_t *__restrict__ tlist,
@@ -299,13 +304,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
     __shared__ __attribute__((aligned(1024))) T Qk[2][TILE];
     __shared__ __attribute__((aligned(1024))) T Ok[2][TILE];
+    __shared__ __attribute__((aligned(16))) v8<T> PB[4][4][64];     // [wave][pb0, pb1, ds0, ds1][lane]
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
     const long bh = logical / Nb;
     const int j = (int)(logical % Nb);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    const int kh = wave >> 1, rh = wave & 1;
+    const int kh = wave >> 1, rh = wave & 1, ch = wave & 1;
     const int krow = 64 * j + 32 * kh + l32;
     const bool kvalid = krow < N;
     v8<T> kf[NS], vf[NS];
@@ -323,6 +329,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
     }
     int toff[NCT][2];
     tr_offsets<D>(lane, toff);
+    int tofc[NCH][2];                                    // the consumer's channel tiles only
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+        tofc[c2][0] = ch ? toff[NCH + c2][0] : toff[c2][0];
+        tofc[c2][1] = ch ? toff[NCH + c2][1] : toff[c2][1];
+    }
     uint32_t ok_[NBW];
 #pragma unroll
     for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
@@ -339,12 +351,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
             dma16(ro, &Ok[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
         }
     };
-    f32x16 dvt[NCT], dkt[NCT];
+    f32x16 dvt[NCH], dkt[NCH];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dvt[ct][r] = dkt[ct][r] = 0.f;
-    auto compute = [&](int c, int slot) __attribute__((always_inline)) {
+    auto produce = [&](int c, int slot) __attribute__((always_inline)) {
         const int i = tl[c];
         // the rows of the accumulator this lane holds, their lse and D
         float lr[16], dr[16];
@@ -354,18 +366,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
             lr[r] = row < N ? lse[bh * N + row] : __builtin_inff();
             dr[r] = row < N ? dbuf[bh * N + row] : 0.f;
         }
-        v8<T> a[NS];
         f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) a[s] = ld8<T>(&Qk[slot][koff[s]]);
+        for (int s = 0; s < NS; ++s) mma16(sacc, ld8<T>(&Qk[slot][koff[s]]), kf[s]);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma16(sacc, a[s], kf[s]);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) a[s] = ld8<T>(&Ok[slot][koff[s]]);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) mma16(pacc, a[s], vf[s]);
+        for (int s = 0; s < NS; ++s) mma16(pacc, ld8<T>(&Ok[slot][koff[s]]), vf[s]);
         v8<T> pb[2], dsb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -373,17 +380,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
             pb[r >> 3][r & 7] = from_f32<T>(p);
             dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - dr[r]));
         }
-        v8<T> at[NCT][2];
-        read_tr<T, D>(Ok[slot], rh, toff, at);
+        PB[wave][0][lane] = pb[0];
+        PB[wave][1][lane] = pb[1];
+        PB[wave][2][lane] = dsb[0];
+        PB[wave][3][lane] = dsb[1];
+    };
+    auto consume = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int src = 2 * kh + r2;
+            const v8<T> p0 = PB[src][0][lane], p1 = PB[src][1][lane];
+            const v8<T> d0 = PB[src][2][lane], d1 = PB[src][3][lane];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) mma16(dvt[ct], at[ct][ks], pb[ks]);
-        read_tr<T, D>(Qk[slot], rh, toff, at);
+            for (int c2 = 0; c2 < NCH; ++c2) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) mma16(dkt[ct], at[ct][ks], dsb[ks]);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const T *bo = &Ok[slot][(32 * r2 + 16 * ks) * D];
+                    const T *bq = &Qk[slot][(32 * r2 + 16 * ks) * D];
+                    mma16(dvt[c2], cat8<T>(lds_tr_raw<T>(bo + tofc[c2][0]), lds_tr_raw<T>(bo + tofc[c2][1])),
+                          ks ? p1 : p0);
+                    mma16(dkt[c2], cat8<T>(lds_tr_raw<T>(bq + tofc[c2][0]), lds_tr_raw<T>(bq + tofc[c2][1])),
+                          ks ? d1 : d0);
+                }
+            }
+        }
     };
     if (cnt > 0) {
         load(0, 0);
@@ -392,63 +412,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const bf16 *__restrict_
         int c = 0;
         for (; c + 1 < cnt; c += 2) {
             load(c + 1, 1);
-            compute(c, 0);
+            produce(c, 0);
+            lds_barrier();
+            consume(0);
             wait_vm0();
             lds_barrier();
             if (c + 2 < cnt) load(c + 2, 0);
-            compute(c + 1, 1);
+            produce(c + 1, 1);
+            lds_barrier();
+            consume(1);
             wait_vm0();
             lds_barrier();
         }
         if (c < cnt) {
-            compute(c, 0);
+            produce(c, 0);
             lds_barrier();
+            consume(0);
         }
     }
-    wait_vm0();
-    // sum the two row halves: wave rh keeps channel tiles NCH*rh .. +NCH-1 of dV and dK
-    float *xv = reinterpret_cast<float *>(&Qk[0][0]);     // [4 waves][NCH*4][64] f32x4 (dV)
-    float *xk = reinterpret_cast<float *>(&Ok[0][0]);     // same for dK
-    f32x16 mv[NCH], mk[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        mv[c] = rh == 0 ? dvt[c] : dvt[NCH + c];
-        mk[c] = rh == 0 ? dkt[c] : dkt[NCH + c];
-        const f32x16 gv = rh == 0 ? dvt[NCH + c] : dvt[c];
-        const f32x16 gk = rh == 0 ? dkt[NCH + c] : dkt[c];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 y = {gv[4 * g], gv[4 * g + 1], gv[4 * g + 2], gv[4 * g + 3]};
-            const f32x4 z = {gk[4 * g], gk[4 * g + 1], gk[4 * g + 2], gk[4 * g + 3]};
-            *reinterpret_cast<f32x4 *>(xv + ((wave * NCH * 4 + c * 4 + g) * 64 + lane) * 4) = y;
-            *reinterpret_cast<f32x4 *>(xk + ((wave * NCH * 4 + c * 4 + g) * 64 + lane) * 4) = z;
-        }
-    }
-    lds_barrier();
-    const int partner = wave ^ 1;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 y = *reinterpret_cast<const f32x4 *>(xv + ((partner * NCH * 4 + c * 4 + g) * 64 + lane) * 4);
-            const f32x4 z = *reinterpret_cast<const f32x4 *>(xk + ((partner * NCH * 4 + c * 4 + g) * 64 + lane) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                mv[c][4 * g + e] += y[e];
-                mk[c][4 * g + e] += z[e];
-            }
-        }
     if (!kvalid) return;
     float *vrow = dv + (bh * N + krow) * (long)D;
     float *krw = dk + (bh * N + krow) * (long)D;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int c0 = 32 * (NCH * rh + c);
+    for (int c2 = 0; c2 < NCH; ++c2) {
+        const int c0 = 32 * (NCH * ch + c2);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 y = {mv[c][4 * g], mv[c][4 * g + 1], mv[c][4 * g + 2], mv[c][4 * g + 3]};
-            const f32x4 z = {mk[c][4 * g] * scale, mk[c][4 * g + 1] * scale, mk[c][4 * g + 2] * scale,
-                             mk[c][4 * g + 3] * scale};
+            const f32x4 y = {dvt[c2][4 * g], dvt[c2][4 * g + 1], dvt[c2][4 * g + 2], dvt[c2][4 * g + 3]};
+            const f32x4 z = {dkt[c2][4 * g] * scale, dkt[c2][4 * g + 1] * scale, dkt[c2][4 * g + 2] * scale,
+                             dkt[c2][4 * g + 3] * scale};
             *reinterpret_cast<f32x4 *>(vrow + c0 + 8 * g + 4 * hh) = y;
             *reinterpret_cast<f32x4 *>(krw + c0 + 8 * g + 4 * hh) = z;
         }

@@ -63,3 +63,64 @@ def gradients(q, k, v, w, mask, dout, blk: int = 64):
     shape = (B, H, N, d)
     return (out.detach().numpy().reshape(shape), dq.numpy().reshape(shape), dk.numpy().reshape(shape),
             dv.numpy().reshape(shape), dw.numpy())
+
+
+def gradients_blocks(q, k, v, w, mask, dout, qblocks, kblocks, blk: int = 64):
+    """Exact gradients of the SLA forward of ONE head at any N, on selected
+    blocks.  q, k, v, dout: [N, d] (numpy, any float); w [d, d]; mask
+    [Nb, Nb] int8 labels of this head.  Returns (dq_rows, dk_rows, dv_rows,
+    dw_head): dq of the tokens of the query blocks `qblocks`, dk and dv of
+    the tokens of the key blocks `kblocks` (each [len(rows), d], rows in
+    ascending block order, a ragged last block shorter), and this head's dW.
+
+    The same forward as forward_tokens, arranged so that only what these
+    gradients depend on is built: the sparse softmax at token level for the
+    query blocks in `qblocks` and for every query block that has one of
+    `kblocks` critical (no other row's sparse output involves those keys),
+    and the linear branch for all rows with its sums grouped by key block,
+    H_i = sum over marginal j of phi(K_j)^T (V_j W^T), Z_i = sum of phi(K_j)
+    (the token sums of forward_tokens, added block by block)."""
+    N, d = q.shape
+    Nb = -(-N // blk)
+    Np = Nb * blk
+    f64 = lambda x: torch.tensor(np.asarray(x, np.float64))
+    pad = lambda x: torch.cat([x, torch.zeros(Np - N, d, dtype=torch.float64)]) if Np > N else x
+    tq, tk, tv, tw = f64(q).requires_grad_(), f64(k).requires_grad_(), f64(v).requires_grad_(), f64(w).requires_grad_()
+    g = pad(f64(dout))
+    lab = torch.from_numpy(np.asarray(mask).astype(np.int64))
+    crit = lab == 1
+    marg = (lab == 0).to(torch.float64)
+
+    # linear branch, all rows
+    phq = torch.softmax(pad(tq), dim=-1).reshape(Nb, blk, d)
+    valid = (torch.arange(Np) < N).to(torch.float64).reshape(Nb, blk, 1)
+    phk = torch.softmax(pad(tk), dim=-1).reshape(Nb, blk, d) * valid
+    vp = (pad(tv) @ tw.transpose(0, 1)).reshape(Nb, blk, d)
+    hj = phk.transpose(1, 2) @ vp                        # [Nb, d, d]
+    zj = phk.sum(dim=1)                                  # [Nb, d]
+    Hi = (marg @ hj.reshape(Nb, d * d)).reshape(Nb, d, d)
+    Zi = marg @ zj
+    num = phq @ Hi                                       # [Nb, blk, d]
+    den = (phq * Zi[:, None, :]).sum(dim=-1, keepdim=True)
+    has = marg.sum(dim=1).reshape(Nb, 1, 1) > 0
+    o_l = torch.where(has, num / torch.where(has, den, torch.ones_like(den)), torch.zeros_like(num))
+    loss = (o_l.reshape(Np, d) * g).sum()
+
+    # sparse branch, the query blocks that matter
+    kset = set(int(j) for j in kblocks)
+    rows_i = sorted(set(int(i) for i in qblocks) |
+                    {i for i in range(Nb) if any(bool(crit[i, j]) for j in kset)})
+    scale = 1.0 / math.sqrt(d)
+    for i in rows_i:
+        keys = [j for j in range(Nb) if bool(crit[i, j])]
+        if not keys:
+            continue
+        r0, r1 = i * blk, min(N, (i + 1) * blk)
+        ku = torch.cat([tk[j * blk:min(N, (j + 1) * blk)] for j in keys])
+        vu = torch.cat([tv[j * blk:min(N, (j + 1) * blk)] for j in keys])
+        p = torch.softmax(tq[r0:r1] @ ku.transpose(0, 1) * scale, dim=-1)
+        loss = loss + ((p @ vu) * g[r0:r1]).sum()
+
+    dq, dk, dv, dw = torch.autograd.grad(loss, (tq, tk, tv, tw))
+    take = lambda x, blocks: np.concatenate([x[b * blk:min(N, (b + 1) * blk)].numpy() for b in sorted(blocks)])
+    return take(dq, qblocks), take(dk, kblocks), take(dv, kblocks), dw.numpy()

@@ -73,3 +73,23 @@ def test_all_critical_is_sdpa_backward():
     gq, gk, gv = torch.autograd.grad(o, (tq, tk, tv), torch.from_numpy(dout))
     assert np.allclose(dq, gq.numpy(), atol=1e-10) and np.allclose(dk, gk.numpy(), atol=1e-10)
     assert np.allclose(dv, gv.numpy(), atol=1e-10) and np.abs(dw).max() == 0.0
+
+
+@pytest.mark.parametrize("N,d,rc,rn,seed", [(300, 16, 0.25, 0.25, 1), (200, 8, 0.0, 0.5, 2), (450, 8, 0.3, 0.0, 3),
+                                            (260, 16, 0.4, 0.2, 4)])
+def test_block_gradients_match_full(N, d, rc, rn, seed):
+    """gradients_blocks (sparse rows restricted to the blocks that matter,
+    linear sums grouped by key block) gives the full autograd gradients of
+    those rows, and the head's whole dW."""
+    q, k, v, w = rand(1, 1, N, d, seed)
+    mask = orc.forward(q, k, v, w, 64, rc, rn)["mask"]
+    dout = np.random.default_rng(seed + 50).standard_normal((1, 1, N, d))
+    _, dq, dk, dv, dw = ob.gradients(q, k, v, w, mask, dout)
+    Nb = -(-N // 64)
+    qb, kb = [0, Nb - 1], [1, Nb - 1]
+    gq, gk, gv, gw = ob.gradients_blocks(q[0, 0], k[0, 0], v[0, 0], w, mask[0, 0], dout[0, 0], qb, kb)
+    rows = lambda blocks: np.concatenate([np.arange(b * 64, min(N, (b + 1) * 64)) for b in sorted(blocks)])
+    assert np.allclose(gq, dq[0, 0, rows(qb)], atol=1e-10, rtol=0)
+    assert np.allclose(gk, dk[0, 0, rows(kb)], atol=1e-10, rtol=0)
+    assert np.allclose(gv, dv[0, 0, rows(kb)], atol=1e-10, rtol=0)
+    assert np.allclose(gw, dw, atol=1e-10, rtol=0)

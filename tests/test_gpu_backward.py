@@ -84,3 +84,31 @@ def test_backward_gradient_scale(sla, gscale):
         rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
         say("  %s rel %.3g" % (name, rel))
         assert np.isfinite(g).all() and rel <= 1e-2
+
+
+def test_backward_full_size_sampled_blocks(sla):
+    """The Wan2.1 480p workload (B=1, H=12, N=32760, d=128, 5 % / 10 %) in one
+    call, as the backward bench runs it; the oracle computes one head's
+    gradients on sampled blocks exactly (gradients_blocks): dq of the first,
+    an interior and the ragged last query block, dk and dv of three key
+    blocks.  Same bar per gradient over the sampled rows."""
+    from sparse_attention_video_sla_amd.inputs import make_workload
+    inp = make_workload(1)
+    B, H, N, d = inp.q.shape
+    rc, rn = 0.05, 0.10
+    rng = np.random.default_rng(77)
+    dout = round_bf16(rng.standard_normal((B, H, N, d)).astype(np.float32))
+    say("backward full size", B, H, N, d)
+    w = torch.from_numpy(inp.w).cuda()
+    dq, dk, dv, dw = sla.backward(dev(inp.q), dev(inp.k), dev(inp.v), w, dev(dout), rc, rn)
+    torch.cuda.synchronize()
+    mask = orc.classify(orc.pool(inp.q), orc.pool(inp.k), rc, rn)["mask"]
+    Nb = -(-N // 64)
+    h, qb, kb = 5, [0, 137, Nb - 1], [0, 300, Nb - 1]
+    gq, gk, gv, _ = ob.gradients_blocks(inp.q[0, h], inp.k[0, h], inp.v[0, h], inp.w, mask[0, h], dout[0, h], qb, kb)
+    rows = lambda blocks: np.concatenate([np.arange(b * 64, min(N, (b + 1) * 64)) for b in blocks])
+    for name, got, ref, blocks in (("dq", dq, gq, qb), ("dk", dk, gk, kb), ("dv", dv, gv, kb)):
+        g = got[0, h].double().cpu().numpy()[rows(blocks)]
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        say("  %s rel %.3g max|d| %.3g max|ref| %.3g" % (name, rel, np.abs(g - ref).max(), np.abs(ref).max()))
+        assert np.isfinite(g).all() and rel <= 1e-2

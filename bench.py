@@ -57,7 +57,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFMA peak"
-FUSED_SRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc", "fused16.hip")
+CSRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
 LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_lvsa_wan6x_stats.md")
 STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_sta_hunyuan_stats.md")
@@ -74,8 +74,8 @@ def work(B, H, N, d, kc, kn):
     return f_comp, f_fused, pairs, marg_rows
 
 
-def fused_traffic(path=TRAFFIC_FILE):
-    """HBM bytes per launch of the fused kernel from a committed rocprofv3
+def fused_traffic(path=TRAFFIC_FILE, kernel="fused16s_kernel", source="fused16s.hip"):
+    """HBM bytes per launch of a fused kernel from a committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
     calibration), or None when the kernel source has changed since the
     counters were taken."""
@@ -83,10 +83,10 @@ def fused_traffic(path=TRAFFIC_FILE):
     import re
     try:
         text = open(path).read()
-        src = open(FUSED_SRC, "rb").read()
+        src = open(os.path.join(CSRC, source), "rb").read()
     except OSError:
         return None
-    m = re.search(r"fused16_kernel HBM bytes per launch: (\d+) \(source sha256 ([0-9a-f]{16})\)", text)
+    m = re.search(kernel + r" HBM bytes per launch: (\d+) \(source sha256 ([0-9a-f]{16})\)", text)
     if not m or hashlib.sha256(src).hexdigest()[:16] != m.group(2):
         return None
     return int(m.group(1))
@@ -238,7 +238,8 @@ def run_lvsa(args):
                    "W": wl.W, "step": wl.step, "T_per": t_per, "globals": n_glob, "frames_per_set": per_set,
                    "density_vs_dense": round(flops / dense, 5), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(LVSA_TRAFFIC_FILE),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": fused_traffic(LVSA_TRAFFIC_FILE, "fused16_kernel", "fused16.hip"),
                      "kernel": "fused16_kernel<bf16,f16,128,float,frame marks>", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
@@ -340,7 +341,8 @@ def run_sta(args):
                    "tile": list(tile), "window": list(window), "density_vs_dense": round(pairs / N / N, 5),
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(STA_TRAFFIC_FILE),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": fused_traffic(STA_TRAFFIC_FILE, "fused16_kernel", "fused16.hip"),
                      "kernel": "fused16_kernel<bf16,f16,128,float> (tile schedule)", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
@@ -583,7 +585,7 @@ def main():
         "mfma_frac_fused": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(),
-                     "kernel": "fused16_kernel<bf16,f16,128,float>",
+                     "kernel": "fused16s_kernel<bf16,f16,128,float>",
                      "flops_per_launch": f_fused, "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": stages,
     }

@@ -644,7 +644,8 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     fa.hhat = ws + L.hhat; fa.mcount = states && !linear_off ? mcount : nullptr; fa.Lp = L.Lp;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d; fa.lse = lse_out;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;
-    st = device_status(f32 ? sla::launch_fused(fa, s) : sla::launch_fused16(fa, s), "fused launch");
+    fa.crit = (const int32_t *)(ws + L.crit);
+    st = device_status(f32 ? sla::launch_fused(fa, s) : sla::launch_fused16s(fa, s), "fused launch");
     mark_stage(ev, 4, 1, s);
     return st;
 }

@@ -1,0 +1,321 @@
+// fused16s.hip -- the SLA forward's fused kernel with one query block per
+// workgroup, for bf16 inputs (SLA article, section 3: exact block-sparse
+// FlashAttention over the critical blocks and the linear read-out of the
+// marginal states, with the learnable projection folded into them).
+//
+// One workgroup of 4 waves per query block i of one head, three workgroups
+// per compute unit (48 KB of LDS and at most 168 registers per lane each, so
+// every SIMD runs three independent waves).  Wave (qh, kh): query rows
+// 32qh .. +31 against keys 32kh .. +31 of every critical block of row i, with
+// its own online softmax (running max m, output O, row sum l); the two key
+// halves of a row merge at the end, each wave keeping half of the output
+// channels.  Per critical block:
+//   S^T = K Q^T on the matrix core (K rows from LDS, Q held in registers);
+//   the softmax in the VALU: the tile's row max (a lane holds 16 keys of one
+//   query column, the other 16 of the half sit in the partner lane 32
+//   away), a lazy rescale of O and l when the tile exceeds the running max
+//   by TAU (log2 units), P = exp2(S log2(e)/sqrt(d) - m) added to l and
+//   converted to bf16 in the MFMA operand layout;
+//   O^T += V^T P^T on the matrix core, V^T by transposing reads of the V
+//   tile.
+// K and V tiles go from global memory straight into LDS: K through a
+// two-slot ring, V through one slot, with two barriers per block (after the
+// scores: V(c) and K(c+1) visible, K(c)'s slot free for K(c+2); after the
+// accumulation: V's slot free for V(c+1)), so each load has a phase or two
+// to land.  Both tiles use the K layout (16-byte chunks swizzled by row),
+// which serves the row reads of K and the transposing reads of V (the
+// latter with two-way bank conflicts: a conflict-free layout for V, groups
+// of 4 rows chunk-major, measured 12 % slower in this kernel).  Every
+// workgroup reads its own tiles; with three workgroups per compute unit the
+// softmax of one overlaps the matrix work of another without any schedule
+// between them.  Workgroups are ordered so that each XCD (own L2) takes a
+// contiguous run of (head, query block).
+#include "sla_device.h"
+#include "sla_launch.h"
+#include "tile_common.h"
+
+namespace sla {
+
+namespace {
+
+template <typename TO> __device__ __forceinline__ void store4s(TO *p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4s<float>(float *p, float a, float b, float c, float d) {
+    f32x4 v = {a, b, c, d};
+    *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <> __device__ __forceinline__ void store4s<bf16>(bf16 *p, float a, float b, float c, float d) {
+    v4<bf16> v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    __builtin_memcpy(p, &v, sizeof(v));
+}
+
+}  // namespace
+
+template <typename T, typename S, int D, typename TO>
+__global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                          const T *__restrict__ v, const int32_t *__restrict__ crit,
+                                                          int kc, const S *__restrict__ hhat,
+                                                          const int32_t *__restrict__ mcount, int Lp,
+                                                          TO *__restrict__ out, float *__restrict__ lse, long G,
+                                                          int per_xcd, int N, int Nb, float sl2) {
+    static_assert(__is_same(T, bf16), "bf16 inputs");
+    constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
+    constexpr float NEG_INF = -__builtin_inff();
+    // Lazy rescale threshold: P may reach 2^TAU; P is bf16 (the float exponent
+    // range) and O and l accumulate in fp32 over at most 64 * Nb < 2^18 keys,
+    // so every value stays below 2^90.
+    constexpr float TAU = 64.f;
+    __shared__ __attribute__((aligned(1024))) T Kk[2][TILE];
+    __shared__ __attribute__((aligned(1024))) T Vk[TILE];
+
+    const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (logical >= G) return;
+    const long bh = logical / Nb;
+    const int i = (int)(logical % Nb);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int qh = wave >> 1, kh = wave & 1;
+    const int qrow = 64 * i + 32 * qh + l32;
+    const bool qvalid = qrow < N;
+    const long rid = bh * Nb + i;
+    const bool lin = mcount != nullptr && mcount[rid] > 0;
+    v8<T> qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        qf[s] = qvalid ? ld8<T>(q + (bh * N + qrow) * (long)D + 16 * s + 8 * hh) : zero8<T>();
+
+    float m = NEG_INF, l = 0.f;                          // l: this lane's share of the row sum
+    f32x16 o[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ct][r] = 0.f;
+
+    const int32_t *cl = crit + rid * (long)kc;
+    const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * N * (long)D, head_bytes);
+    int koff[NS];                                        // K operand reads: key row 32kh + l32
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int r = 32 * kh + l32;
+        koff[s] = r * D + ((2 * s + hh) ^ kswz<D>(r)) * 8;
+    }
+    int toff[NCT][2];
+    tr_offsets<D>(lane, toff);
+    uint32_t ok_[NBW];
+#pragma unroll
+    for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
+    // this wave's NBW 1 KB pieces of the K or V tile of block c of the list;
+    // the tile offset goes into the per-lane offset, which the buffer's bounds
+    // check covers (a ragged last tile reads zeros)
+    auto load_k = [&](int c, int slot) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)(64L * cl[c] * D * sizeof(T));
+#pragma unroll
+        for (int u = 0; u < NBW; ++u) dma16(rk, &Kk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
+    };
+    auto load_v = [&](int c) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)(64L * cl[c] * D * sizeof(T));
+#pragma unroll
+        for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ok_[u] + off, 0);
+    };
+    v8<T> pb[2];
+    // S^T = K Q^T of block c and its softmax: P^T in pb
+    auto score = [&](int c, int slot) __attribute__((always_inline)) {
+        const int j = cl[c];
+        v8<T> ak[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ak[s] = ld8<T>(&Kk[slot][koff[s]]);
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) mma16(sacc, ak[s], qf[s]);
+        if (64 * j + 64 > N) {                           // ragged last block: keys past N score -inf
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 64 * j + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= N) sacc[r] = NEG_INF;
+            }
+        }
+        float mx = vmax(sacc[0], sacc[1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = vmax(mx, sacc[r]);
+        mx = half_swap_max(mx) * sl2;
+        if (__ballot(mx > m + TAU)) {
+            const float mnew = fmaxf(m, mx);
+            const float alpha = (mnew == NEG_INF) ? 1.f : fast_exp2(m - mnew);
+            l *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+            m = mnew;
+        }
+        const float msub = (m == NEG_INF) ? 0.f : m;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(__builtin_fmaf(sacc[r], sl2, -msub));
+            l += p;
+            pb[r >> 3][r & 7] = from_f32<T>(p);
+        }
+    };
+    // O^T += V^T P^T
+    auto accumulate = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const T *base = &Vk[(32 * kh + 16 * ks) * D];
+                mma16(o[ct], cat8<T>(lds_tr_raw<T>(base + toff[ct][0]), lds_tr_raw<T>(base + toff[ct][1])), pb[ks]);
+            }
+    };
+    // Block c: score (K(c) visible; V(c) and K(c+1) in flight), wait for
+    // both and barrier (V(c) visible, the K slot of c free), load K(c+2)
+    // into it, accumulate, barrier (the V tile free), load V(c+1).  Each
+    // load has a whole phase or two to land.
+    auto block = [&](int c, int slot) __attribute__((always_inline)) {
+        score(c, slot);
+        wait_vm0();
+        lds_barrier();
+        if (c + 2 < kc) load_k(c + 2, slot);
+        accumulate();
+        lds_barrier();
+        if (c + 1 < kc) load_v(c + 1);
+    };
+    if (kc > 0) {
+        load_k(0, 0);
+        if (kc > 1) load_k(1, 1);
+        wait_vm0();
+        load_v(0);
+        lds_barrier();
+        int c = 0;
+        for (; c + 1 < kc; c += 2) {
+            block(c, 0);
+            block(c + 1, 1);
+        }
+        if (c < kc) block(c, 0);
+    }
+    wait_vm0();                                          // no load into LDS outlives the loop
+
+    // merge the two key halves: wave kh keeps channel tiles NCH*kh .. +NCH-1.
+    // Exchange area: 4*NCH f32x4 per lane and wave in Kk, m and l in Vk.
+    l = half_swap_sum(l);                                // the row sum over the wave's 32 keys
+    float *xo = reinterpret_cast<float *>(&Kk[0][0]);
+    float *xm = reinterpret_cast<float *>(&Vk[0]);       // [4 waves][64]
+    float *xl = xm + 4 * 64;
+    const int partner = wave ^ 1;
+    f32x16 mine[NCH], give[NCH];
+#pragma unroll
+    for (int t = 0; t < NCH; ++t) {
+        mine[t] = kh == 0 ? o[t] : o[NCH + t];
+        give[t] = kh == 0 ? o[NCH + t] : o[t];
+    }
+    if (kc > 0) {
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 y = {give[t][4 * g], give[t][4 * g + 1], give[t][4 * g + 2], give[t][4 * g + 3]};
+                *reinterpret_cast<f32x4 *>(xo + ((wave * 4 * NCH + 4 * t + g) * 64 + lane) * 4) = y;
+            }
+        xm[wave * 64 + lane] = m;
+        xl[wave * 64 + lane] = l;
+    }
+
+    const S *hr = hhat + rid * (long)Lp;
+    if (kc > 0) {
+        lds_barrier();
+        const float mo = xm[partner * 64 + lane], lo = xl[partner * 64 + lane];
+        const float mm = fmaxf(m, mo);
+        const float as = (mm == NEG_INF) ? 0.f : fast_exp2(m - mm);
+        const float ao = (mm == NEG_INF) ? 0.f : fast_exp2(mo - mm);
+        const float lt = l * as + lo * ao;
+        const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+        // log-sum-exp of the row's sparse softmax in the kernel's log2 units
+        // (P = exp2(s * log2(e) / sqrt(d) - lse)), +inf for a row with no key
+        if (lse && kh == 0 && hh == 0 && qvalid) lse[bh * N + qrow] = lt > 0.f ? mm + __log2f(lt) : __builtin_inff();
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(xo + ((partner * 4 * NCH + 4 * t + g) * 64 + lane) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mine[t][4 * g + e] = (mine[t][4 * g + e] * as + y[e] * ao) * inv;
+            }
+    }
+    if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * N + qrow] = __builtin_inff();
+
+    if (lin) {
+        constexpr float LOG2E = 1.4426950408889634f;
+        float mq = NEG_INF;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mq = fmaxf(mq, to_f32<T>(qf[s][e]));
+        mq = half_swap_max(mq);
+        float ex[NS][8];
+        float se = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ex[s][e] = fast_exp2((to_f32<T>(qf[s][e]) - mq) * LOG2E);
+                se += ex[s][e];
+            }
+        se = half_swap_sum(se);
+        const float inv_se = 1.f / se;
+        v8<S> ph[NS];
+        float den = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const v8<S> hz = ld8<S>(hr + D * D + 16 * s + 8 * hh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[s][e] = from_f32<S>(ex[s][e] * inv_se);
+                den += to_f32<S>(ph[s][e]) * to_f32<S>(hz[e]);
+            }
+        }
+        den = half_swap_sum(den);
+        const float rden = 1.f / den;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            f32x16 y;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) mma16(y, ld8<S>(hr + (32 * (NCH * kh + t) + l32) * D + 16 * s + 8 * hh), ph[s]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[t][r] += y[r] * rden;
+        }
+    }
+
+    if (qvalid) {
+        TO *orow = out + (bh * N + qrow) * (long)D;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const int c0 = 32 * (NCH * kh + t);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store4s<TO>(orow + c0 + 8 * g + 4 * hh, mine[t][4 * g], mine[t][4 * g + 1], mine[t][4 * g + 2],
+                            mine[t][4 * g + 3]);
+        }
+    }
+}
+
+template <int D, typename TO>
+static hipError_t launch_fused16s_t(const FusedArgs &a, hipStream_t st) {
+    const long G = a.BH * a.Nb;
+    const int per = (int)((G + 7) / 8);
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+    fused16s_kernel<bf16, f16, D, TO><<<(unsigned)(8L * per), 256, 0, st>>>(
+        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.crit, a.kc, (const f16 *)a.hhat, a.mcount, a.Lp,
+        (TO *)a.out, a.lse, G, per, a.N, a.Nb, sl2);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused16s(const FusedArgs &a, hipStream_t st) {
+    if (a.bf16_out) return a.D == 64 ? launch_fused16s_t<64, bf16>(a, st) : launch_fused16s_t<128, bf16>(a, st);
+    return a.D == 64 ? launch_fused16s_t<64, float>(a, st) : launch_fused16s_t<128, float>(a, st);
+}
+
+}  // namespace sla

@@ -1,7 +1,7 @@
 // tile_common.h -- small device helpers shared by the attention kernels
 // (forward and backward): workgroup barrier on LDS traffic, NaN-propagating
 // max, cross-half reductions, loads straight into LDS, and the swizzle of
-// K-layout tiles.
+// K-layout tiles with the offsets of their row and transposing reads.
 #pragma once
 #include "sla_device.h"
 
@@ -43,6 +43,40 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 // swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
 template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
+// 1 KB block u of this wave's share of a 64 x D tile: source offset of its
+// lane in the K layout (rows of 2D bytes, 16-byte chunks swizzled)
+template <int D> __device__ __forceinline__ uint32_t off_klayout(int byte) {
+    const int r = byte / (2 * D), pk = (byte % (2 * D)) / 16;
+    return (uint32_t)(r * 2 * D + (pk ^ kswz<D>(r)) * 16);
+}
+// Transposing reads of a K-layout tile as the A operand [channel][row] of
+// rows 32 half .. +31, rows in the accumulator order of a 32 x 32 tile: k
+// slot e of step ks is row 16 ks + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4).
+// Lane L of a 16-lane group points at row 8 x + 4 hh + L / 4 of the step and
+// channels 32 ct + 16 (group & 1) + 4 (L % 4) .. +3, found through the
+// row's chunk swizzle (which only depends on the row modulo 16).
+template <int D> __device__ __forceinline__ void tr_offsets(int lane, int (&toff)[D / 32][2]) {
+    const int grp = lane >> 4, L = lane & 15, hh = lane >> 5;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int rr = 8 * x + 4 * hh + (L >> 2);
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct)
+            toff[ct][x] = rr * D + ((4 * ct + 2 * (grp & 1) + ((L & 3) >> 1)) ^ kswz<D>(rr)) * 8 + 4 * (L & 1);
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void read_tr(const T *tile, int half, const int (&toff)[D / 32][2], v8<T> (&a)[D / 32][2]) {
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const T *base = tile + (32 * half + 16 * ks) * D;
+            a[ct][ks] = cat8<T>(lds_tr_raw<T>(base + toff[ct][0]), lds_tr_raw<T>(base + toff[ct][1]));
+        }
+}
 
 }  // namespace
 }  // namespace sla

@@ -22,10 +22,13 @@
 // two-slot ring, V through one slot, with two barriers per block (after the
 // scores: V(c) and K(c+1) visible, K(c)'s slot free for K(c+2); after the
 // accumulation: V's slot free for V(c+1)), so each load has a phase or two
-// to land.  Both tiles use the K layout (16-byte chunks swizzled by row),
-// which serves the row reads of K and the transposing reads of V (the
-// latter with two-way bank conflicts: a conflict-free layout for V, groups
-// of 4 rows chunk-major, measured 12 % slower in this kernel).  Every
+// to land.  Both tiles are stored by rows with their 16-byte chunks
+// swizzled by row, K by kswz (its row reads touch every bank once) and V by
+// vswz (its transposing reads, 8 rows x 4 chunks per instruction, touch
+// every bank twice, the minimum); the loads into LDS read whole rows.  (A V
+// layout of 4-row groups stored chunk-major, also free of conflicts, was
+// 12 % slower here: each of its loads gathers 16-byte pieces of four rows.)
+// Every
 // workgroup reads its own tiles; with three workgroups per compute unit the
 // softmax of one overlaps the matrix work of another without any schedule
 // between them.  Workgroups are ordered so that each XCD (own L2) takes a
@@ -100,11 +103,14 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const int r = 32 * kh + l32;
         koff[s] = r * D + ((2 * s + hh) ^ kswz<D>(r)) * 8;
     }
-    int toff[NCT][2];
-    tr_offsets<D>(lane, toff);
-    uint32_t ok_[NBW];
+    int toff[NCT][2];                                    // V transposing reads (V-swizzled rows)
+    tr_offsets<D, true>(lane, toff);
+    uint32_t ok_[NBW], ov_[NBW];
 #pragma unroll
-    for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
+    for (int u = 0; u < NBW; ++u) {
+        ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
+        ov_[u] = off_klayout<D, true>((wave * NBW + u) * 1024 + 16 * lane);
+    }
     // this wave's NBW 1 KB pieces of the K or V tile of block c of the list;
     // the tile offset goes into the per-lane offset, which the buffer's bounds
     // check covers (a ragged last tile reads zeros)
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     auto load_v = [&](int c) __attribute__((always_inline)) {
         const uint32_t off = (uint32_t)(64L * cl[c] * D * sizeof(T));
 #pragma unroll
-        for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ok_[u] + off, 0);
+        for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov_[u] + off, 0);
     };
     v8<T> pb[2];
     // S^T = K Q^T of block c and its softmax: P^T in pb

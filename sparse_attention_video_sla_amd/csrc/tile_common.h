@@ -44,11 +44,17 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
 template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
+// swizzle of a tile that is only read transposed (V): chunk c of row r sits
+// at chunk c ^ vswz(r), so that the 8 rows x 4 chunks of one transposing read
+// (see tr_offsets) land on every bank exactly twice
+template <int D> __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
 // 1 KB block u of this wave's share of a 64 x D tile: source offset of its
-// lane in the K layout (rows of 2D bytes, 16-byte chunks swizzled)
-template <int D> __device__ __forceinline__ uint32_t off_klayout(int byte) {
+// lane in the K layout (rows of 2D bytes, 16-byte chunks swizzled by kswz,
+// or by vswz with V = true)
+template <int D, bool V = false> __device__ __forceinline__ uint32_t off_klayout(int byte) {
     const int r = byte / (2 * D), pk = (byte % (2 * D)) / 16;
-    return (uint32_t)(r * 2 * D + (pk ^ kswz<D>(r)) * 16);
+    return (uint32_t)(r * 2 * D + (pk ^ (V ? vswz<D>(r) : kswz<D>(r))) * 16);
 }
 // Transposing reads of a K-layout tile as the A operand [channel][row] of
 // rows 32 half .. +31, rows in the accumulator order of a 32 x 32 tile: k
@@ -56,14 +62,15 @@ template <int D> __device__ __forceinline__ uint32_t off_klayout(int byte) {
 // Lane L of a 16-lane group points at row 8 x + 4 hh + L / 4 of the step and
 // channels 32 ct + 16 (group & 1) + 4 (L % 4) .. +3, found through the
 // row's chunk swizzle (which only depends on the row modulo 16).
-template <int D> __device__ __forceinline__ void tr_offsets(int lane, int (&toff)[D / 32][2]) {
+template <int D, bool V = false> __device__ __forceinline__ void tr_offsets(int lane, int (&toff)[D / 32][2]) {
     const int grp = lane >> 4, L = lane & 15, hh = lane >> 5;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int rr = 8 * x + 4 * hh + (L >> 2);
+        const int sw = V ? vswz<D>(rr) : kswz<D>(rr);
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct)
-            toff[ct][x] = rr * D + ((4 * ct + 2 * (grp & 1) + ((L & 3) >> 1)) ^ kswz<D>(rr)) * 8 + 4 * (L & 1);
+            toff[ct][x] = rr * D + ((4 * ct + 2 * (grp & 1) + ((L & 3) >> 1)) ^ sw) * 8 + 4 * (L & 1);
     }
 }
 

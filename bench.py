@@ -59,8 +59,8 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFMA peak"
 CSRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
-LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_lvsa_wan6x_stats.md")
-STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16_sta_hunyuan_stats.md")
+LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16s_lvsa_wan6x_stats.md")
+STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16s_sta_hunyuan_stats.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -239,8 +239,8 @@ def run_lvsa(args):
                    "density_vs_dense": round(flops / dense, 5), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": fused_traffic(LVSA_TRAFFIC_FILE, "fused16_kernel", "fused16.hip"),
-                     "kernel": "fused16_kernel<bf16,f16,128,float,frame marks>", "flops_per_launch": flops,
+                     "traffic": fused_traffic(LVSA_TRAFFIC_FILE),
+                     "kernel": "fused16s_kernel<bf16,f16,128,float,slots,frame marks>", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
     }
@@ -342,8 +342,8 @@ def run_sta(args):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": fused_traffic(STA_TRAFFIC_FILE, "fused16_kernel", "fused16.hip"),
-                     "kernel": "fused16_kernel<bf16,f16,128,float> (tile schedule)", "flops_per_launch": flops,
+                     "traffic": fused_traffic(STA_TRAFFIC_FILE),
+                     "kernel": "fused16s_kernel<bf16,f16,128,float,slots> (tile schedule)", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
     }

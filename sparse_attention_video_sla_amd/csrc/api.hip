@@ -253,7 +253,7 @@ sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dt
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
     mark_stage(ev, 4, 0, s);
-    st = device_status(sla::launch_fused16(fa, s), "fused launch");
+    st = device_status(sla::launch_fused16s(fa, s), "fused launch");
     mark_stage(ev, 4, 1, s);
     return st;
 }
@@ -362,7 +362,7 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
     fa.out = out; fa.BH = (long)B * H; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
     mark_stage(ev, 4, 0, s);
-    st = device_status(sla::launch_fused16(fa, s), "fused launch");
+    st = device_status(sla::launch_fused16s(fa, s), "fused launch");
     mark_stage(ev, 4, 1, s);
     return st;
 }
@@ -463,7 +463,7 @@ sla_status sla_forward_sta(const void *q, const void *k, const void *v, sla_dtyp
     fa.out = out; fa.BH = (long)B * H; fa.N = sh.N; fa.Nb = sh.Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
     mark_stage(ev, 4, 0, s);
-    st = device_status(sla::launch_fused16(fa, s), "fused launch");
+    st = device_status(sla::launch_fused16s(fa, s), "fused launch");
     mark_stage(ev, 4, 1, s);
     return st;
 }

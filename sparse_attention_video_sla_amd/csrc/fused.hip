@@ -293,7 +293,7 @@ static hipError_t launch_fused_t(const FusedArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st) {
-    if (a.bf16_in) return hipErrorInvalidValue;           // 16-bit inputs run fused16_kernel
+    if (a.bf16_in) return hipErrorInvalidValue;           // 16-bit inputs run fused16s_kernel
     return a.D == 64 ? launch_fused_t<float, float, 64, float>(a, st) : launch_fused_t<float, float, 128, float>(a, st);
 }
 

@@ -53,10 +53,18 @@ template <> __device__ __forceinline__ void store4s<bf16>(bf16 *p, float a, floa
 
 }  // namespace
 
-template <typename T, typename S, int D, typename TO>
+// SLOTS: the blocks come from a slot schedule of row pairs (the workgroup
+// takes its row's half of each slot: a key block index in the low 12 bits,
+// frame marks or 0xF for padding in the top 4) instead of critical lists;
+// MARKS: those halves may carry frame marks (bit 2a + c set: query part a
+// does not see key part c, part 1 being what follows a frame boundary inside
+// the block).
+template <typename T, typename S, int D, typename TO, bool SLOTS, bool MARKS>
 __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                           const T *__restrict__ v, const int32_t *__restrict__ crit,
-                                                          int kc, const S *__restrict__ hhat,
+                                                          int kc, const uint32_t *__restrict__ slots,
+                                                          const int32_t *__restrict__ pcount, int bcast, int fp,
+                                                          const S *__restrict__ hhat,
                                                           const int32_t *__restrict__ mcount, int Lp,
                                                           TO *__restrict__ out, float *__restrict__ lse, long G,
                                                           int per_xcd, int N, int Nb, float sl2) {
@@ -94,6 +102,25 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         for (int r = 0; r < 16; ++r) o[ct][r] = 0.f;
 
     const int32_t *cl = crit + rid * (long)kc;
+    const uint32_t *sl = nullptr;
+    int hb = 0;                                          // which half of a slot entry is this row's
+    if constexpr (SLOTS) {
+        const int Np = (Nb + 1) / 2, pr = i >> 1;
+        const long pair = bcast ? pr : bh * Np + pr;
+        sl = slots + pair * (long)kc;
+        hb = 16 * (i & 1);
+        if (pcount) kc = __builtin_amdgcn_readfirstlane(min(max(pcount[pair], 0), kc));
+    }
+    // key block of list entry c, and its frame marks (0xF: padding)
+    auto blk_of = [&](int c) __attribute__((always_inline)) {
+        if constexpr (SLOTS) return min((int)((sl[c] >> hb) & 0xFFFu), Nb - 1);
+        else return cl[c];
+    };
+    auto marks_of = [&](int c) __attribute__((always_inline)) {
+        if constexpr (SLOTS) return (sl[c] >> (hb + 12)) & 0xFu;
+        else return 0u;
+    };
+    const int qpart = (MARKS && fp > 0 && 32 * qh + l32 >= frame_split(i, fp)) ? 1 : 0;
     const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * N * (long)D, head_bytes);
@@ -115,19 +142,19 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // the tile offset goes into the per-lane offset, which the buffer's bounds
     // check covers (a ragged last tile reads zeros)
     auto load_k = [&](int c, int slot) __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)(64L * cl[c] * D * sizeof(T));
+        const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) dma16(rk, &Kk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
     };
     auto load_v = [&](int c) __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)(64L * cl[c] * D * sizeof(T));
+        const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov_[u] + off, 0);
     };
     v8<T> pb[2];
     // S^T = K Q^T of block c and its softmax: P^T in pb
     auto score = [&](int c, int slot) __attribute__((always_inline)) {
-        const int j = cl[c];
+        const int j = blk_of(c);
         v8<T> ak[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) ak[s] = ld8<T>(&Kk[slot][koff[s]]);
@@ -136,6 +163,21 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16(sacc, ak[s], qf[s]);
+        if constexpr (SLOTS) {
+            const uint32_t marks = marks_of(c);
+            if (marks == 0xFu) [[unlikely]] {           // padding: no key of the slot for this row
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[r] = NEG_INF;
+            } else if (MARKS && marks != 0u) {           // a frame boundary hides some keys
+                const int ks = fp > 0 ? frame_split(j, fp) : 64;
+                const uint32_t hide = marks >> (2 * qpart);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if ((hide >> (key >= ks ? 1 : 0)) & 1u) sacc[r] = NEG_INF;
+                }
+            }
+        }
         if (64 * j + 64 > N) {                           // ragged last block: keys past N score -inf
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -308,20 +350,30 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     }
 }
 
-template <int D, typename TO>
+template <int D, typename TO, bool SLOTS, bool MARKS>
 static hipError_t launch_fused16s_t(const FusedArgs &a, hipStream_t st) {
     const long G = a.BH * a.Nb;
     const int per = (int)((G + 7) / 8);
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-    fused16s_kernel<bf16, f16, D, TO><<<(unsigned)(8L * per), 256, 0, st>>>(
-        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.crit, a.kc, (const f16 *)a.hhat, a.mcount, a.Lp,
-        (TO *)a.out, a.lse, G, per, a.N, a.Nb, sl2);
+    fused16s_kernel<bf16, f16, D, TO, SLOTS, MARKS><<<(unsigned)(8L * per), 256, 0, st>>>(
+        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.crit, a.kc, a.slots, a.pcount, a.bcast ? 1 : 0,
+        a.fp, (const f16 *)a.hhat, a.mcount, a.Lp, (TO *)a.out, a.lse, G, per, a.N, a.Nb, sl2);
     return hipGetLastError();
 }
 
+template <bool SLOTS, bool MARKS>
+static hipError_t launch_fused16s_m(const FusedArgs &a, hipStream_t st) {
+    if (a.bf16_out)
+        return a.D == 64 ? launch_fused16s_t<64, bf16, SLOTS, MARKS>(a, st)
+                         : launch_fused16s_t<128, bf16, SLOTS, MARKS>(a, st);
+    return a.D == 64 ? launch_fused16s_t<64, float, SLOTS, MARKS>(a, st)
+                     : launch_fused16s_t<128, float, SLOTS, MARKS>(a, st);
+}
+
+// critical lists (crit), or the slot schedule (slots) when crit is null
 hipError_t launch_fused16s(const FusedArgs &a, hipStream_t st) {
-    if (a.bf16_out) return a.D == 64 ? launch_fused16s_t<64, bf16>(a, st) : launch_fused16s_t<128, bf16>(a, st);
-    return a.D == 64 ? launch_fused16s_t<64, float>(a, st) : launch_fused16s_t<128, float>(a, st);
+    if (a.crit) return launch_fused16s_m<false, false>(a, st);
+    return a.fp > 0 ? launch_fused16s_m<true, true>(a, st) : launch_fused16s_m<true, false>(a, st);
 }
 
 }  // namespace sla

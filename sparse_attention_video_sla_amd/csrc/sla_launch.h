@@ -51,7 +51,7 @@ struct FusedArgs {
     const uint32_t *ulist;   // [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
     const int32_t *ucount;   // [BH][ceil(Nb/2)]
     const uint32_t *slots;   // [BH][ceil(Nb/2)][kc] slot schedule (16-bit inputs), [ceil(Nb/2)][kc] with bcast
-    const int32_t *crit;     // [BH][Nb][kc] critical lists (the one-block-per-workgroup kernel)
+    const int32_t *crit;     // [BH][Nb][kc] critical lists (null: the slot schedule gives the blocks)
     int kc;
     const int32_t *pcount;   // nullable: slots used per pair ([BH][ceil(Nb/2)], or [ceil(Nb/2)] with bcast)
     bool bcast;              // one schedule shared by every head
@@ -81,8 +81,7 @@ hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st);
 hipError_t launch_state(const StateArgs &a, hipStream_t st);
 hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t st);     // float inputs
-hipError_t launch_fused16(const FusedArgs &a, hipStream_t st);   // bf16 inputs, pairs of query blocks on slots
-hipError_t launch_fused16s(const FusedArgs &a, hipStream_t st);  // bf16 inputs, one query block per workgroup
+hipError_t launch_fused16s(const FusedArgs &a, hipStream_t st);  // bf16 inputs: critical lists, or a slot schedule
 hipError_t launch_block_mass(const MassArgs &a, hipStream_t st);
 hipError_t launch_lists_to_slots(const int32_t *lists, const int32_t *counts, int kmax, long BH, int Nb,
                                  uint32_t *slots, int32_t *pcount, hipStream_t st);

@@ -41,6 +41,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds,
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 
+// offset of the first token of the block's part 1 (a frame boundary inside
+// the block), 64 when the block lies in one frame; frames of fp >= 64 tokens
+__device__ __forceinline__ int frame_split(int blk, int fp) {
+    const int start = 64 * blk;
+    const int bnd = (start / fp + 1) * fp - start;
+    return bnd < 64 ? bnd : 64;
+}
+
 // swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
 template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 

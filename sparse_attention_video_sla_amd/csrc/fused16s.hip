@@ -132,12 +132,13 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     }
     int toff[NCT][2];                                    // V transposing reads (V-swizzled rows)
     tr_offsets<D, true>(lane, toff);
-    uint32_t ok_[NBW], ov_[NBW];
+    uint32_t ok_[NBW];
 #pragma unroll
-    for (int u = 0; u < NBW; ++u) {
-        ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
-        ov_[u] = off_klayout<D, true>((wave * NBW + u) * 1024 + 16 * lane);
-    }
+    for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
+    // V: the swizzle only depends on the row modulo 4 (d = 128) or 8 (d = 64),
+    // which a 1 KB piece (4 or 8 rows) does not change: piece u is piece 0
+    // plus u KB
+    const uint32_t ov0 = off_klayout<D, true>(wave * NBW * 1024 + 16 * lane);
     // this wave's NBW 1 KB pieces of the K or V tile of block c of the list;
     // the tile offset goes into the per-lane offset, which the buffer's bounds
     // check covers (a ragged last tile reads zeros)
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     auto load_v = [&](int c) __attribute__((always_inline)) {
         const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
 #pragma unroll
-        for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov_[u] + off, 0);
+        for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov0 + off + 1024 * u, 0);
     };
     v8<T> pb[2];
     // S^T = K Q^T of block c and its softmax: P^T in pb

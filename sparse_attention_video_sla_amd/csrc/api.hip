@@ -69,7 +69,7 @@ sla_status check_shape(int B, int H, int N, int d, int block, int max_nb = MAX_N
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, marg, mbits, mcount, ulist, ucount, slots, wst, hs, hhat, total;
+    size_t qp, kp, mask, crit, marg, mbits, mcount, ulist, ucount, wst, hs, hhat, total;
     int Nb, Nbc, Nbp, Lp, kc, kn;
 };
 
@@ -91,10 +91,9 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     L.crit = take(sizeof(int32_t) * BH * L.Nb * (kc > 0 ? kc : 1));
     L.mcount = take(sizeof(int32_t) * BH * L.Nb);
     const long Np = (L.Nb + 1) / 2;
-    // float inputs: union of each row pair's critical lists; 16-bit inputs: slot schedule
+    // float inputs: union of each row pair's critical lists (16-bit inputs read the critical lists)
     L.ulist = take(f32 ? sizeof(uint32_t) * BH * Np * 2 * (kc > 0 ? kc : 1) : 0);
     L.ucount = take(f32 ? sizeof(int32_t) * BH * Np : 0);
-    L.slots = take(f32 ? 0 : sizeof(uint32_t) * BH * Np * (kc > 0 ? kc : 1));
     const bool states = kc + kn < L.Nb;
     // marginal indicator: float rows for float inputs, bits for 16-bit inputs
     L.marg = take(states && f32 ? sizeof(float) * BH * L.Nb * L.Nbc : 0);
@@ -534,7 +533,7 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
     a.qp = q_pool; a.kp = k_pool; a.BH = (long)B * H; a.Nb = Nb; a.D = d; a.kc = kc; a.kn = kn;
     a.mask = mask; a.crit = crit_idx; a.excl = excl_idx; a.pc = p_c;
     a.marg = nullptr; a.mbits = nullptr; a.Nbc = 0; a.Nbp = 0; a.mcount = nullptr; a.n_last = 64;
-    a.ulist = nullptr; a.ucount = nullptr; a.slots = nullptr;
+    a.ulist = nullptr; a.ucount = nullptr;
     a.inv_sqrt_d = 1.0 / sqrt((double)d);
     return device_status(sla::launch_classify(a, (hipStream_t)stream), "classify launch");
 }
@@ -616,7 +615,6 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     ca.mcount = mcount; ca.n_last = N - 64 * (Nb - 1);
     ca.ulist = f32 ? (uint32_t *)(ws + L.ulist) : nullptr;
     ca.ucount = f32 ? (int32_t *)(ws + L.ucount) : nullptr;
-    ca.slots = f32 ? nullptr : (uint32_t *)(ws + L.slots);
     ca.inv_sqrt_d = 1.0 / sqrt((double)d);
     mark_stage(ev, 1, 0, s);
     st = device_status(sla::launch_classify(ca, s), "classify launch");
@@ -640,7 +638,7 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     mark_stage(ev, 4, 0, s);
     sla::FusedArgs fa{};
     fa.q = q; fa.k = k; fa.v = v; fa.ulist = (const uint32_t *)(ws + L.ulist);
-    fa.ucount = (const int32_t *)(ws + L.ucount); fa.slots = (const uint32_t *)(ws + L.slots); fa.kc = kc;
+    fa.ucount = (const int32_t *)(ws + L.ucount); fa.kc = kc;
     fa.hhat = ws + L.hhat; fa.mcount = states && !linear_off ? mcount : nullptr; fa.Lp = L.Lp;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d; fa.lse = lse_out;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;

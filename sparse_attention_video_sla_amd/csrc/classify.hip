@@ -24,12 +24,6 @@
 //      of their critical lists, each entry j | in_row_2p << 16 | in_row_2p+1 << 17
 //      (32-bit, so that the fused kernel reads it with scalar loads), and its
 //      length.  The float fused kernel streams a pair's union once.
-//   5. For the 16-bit fused kernel, per row pair a schedule of k_c slots, each
-//      one 32-bit entry (tile of row 2p) | (tile of row 2p+1) << 16: first the
-//      blocks both rows selected (one tile serves both), ascending, then the
-//      i-th block only row 2p selected beside the i-th only row 2p+1 selected
-//      (both rows select exactly k_c blocks, so these two lists have equal
-//      length).  A pair without a second row (odd Nb) has 0xFFFF there.
 #include "sla_device.h"
 #include "sla_launch.h"
 
@@ -108,7 +102,7 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
     int8_t *__restrict__ mask, int32_t *__restrict__ crit, int32_t *__restrict__ excl,
     float *__restrict__ pc, float *__restrict__ marg, uint32_t *__restrict__ mbits, int Nbc, int Nbp,
     int32_t *__restrict__ mcount, int n_last,
-    uint32_t *__restrict__ ulist, int32_t *__restrict__ ucount, uint32_t *__restrict__ slots,
+    uint32_t *__restrict__ ulist, int32_t *__restrict__ ucount,
     double inv_sqrt_d) {
     extern __shared__ double smem[];
     double *qd = smem;                                        // [R][D]
@@ -200,7 +194,7 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
             for (int j = lane; j < Nb; j += 64) pc[row * Nb + j] = (float)(exp((s[j] - m) * inv_sqrt_d) / z);
         }
     }
-    if (ulist == nullptr && slots == nullptr) return;
+    if (ulist == nullptr) return;
     __syncthreads();
     // union of the critical lists of each row pair (R is even, i0 is even)
     const int Np = (Nb + 1) / 2;
@@ -221,38 +215,6 @@ __global__ __launch_bounds__(CL_THREADS) void classify_kernel(
         }
         if (lane == 0) ucount[pair] = run;
     }
-    // slot schedule of each row pair
-    for (int pr = wave; slots != nullptr && kc > 0 && 2 * pr < nr; pr += CL_THREADS / 64) {
-        const long pair = bh * Np + (i0 / 2 + pr);
-        const int8_t *la = labs + (2 * pr) * Nb;
-        const int8_t *lb = (2 * pr + 1 < nr) ? labs + (2 * pr + 1) * Nb : nullptr;
-        uint16_t *sl = reinterpret_cast<uint16_t *>(slots + pair * kc);   // (row 2p, row 2p+1) halves
-        int ns = 0;
-        for (int e = 0; e < ne && lb != nullptr; ++e) {
-            const int j = lane + 64 * e;
-            ns += __popcll(__ballot(j < Nb && la[j] == 1 && lb[j] == 1));
-        }
-        int rs = 0, ra = 0, rb = 0;
-        for (int e = 0; e < ne; ++e) {
-            const int j = lane + 64 * e;
-            const bool a = j < Nb && la[j] == 1;
-            const bool b = j < Nb && lb != nullptr && lb[j] == 1;
-            const uint64_t bs = __ballot(a && b), ba = __ballot(a && !b), bb = __ballot(b && !a);
-            if (a && b) {
-                const int p = rs + __popcll(bs & lt);
-                if (p < kc) { sl[2 * p] = (uint16_t)j; sl[2 * p + 1] = (uint16_t)j; }
-            } else if (a) {
-                const int p = ns + ra + __popcll(ba & lt);
-                if (p < kc) sl[2 * p] = (uint16_t)j;
-            } else if (b) {
-                const int p = ns + rb + __popcll(bb & lt);
-                if (p < kc) sl[2 * p + 1] = (uint16_t)j;
-            }
-            rs += __popcll(bs); ra += __popcll(ba); rb += __popcll(bb);
-        }
-        if (lb == nullptr)
-            for (int p = lane; p < kc; p += 64) sl[2 * p + 1] = (uint16_t)0xFFFFu;
-    }
 }
 
 template <int D, int R, int KM>
@@ -264,7 +226,7 @@ static hipError_t launch_cls_k(const ClassifyArgs &a, hipStream_t st) {
     const long tiles = (a.Nb + R - 1) / R;
     const unsigned grid = (unsigned)(a.BH * tiles);
     kern<<<grid, CL_THREADS, lds, st>>>(a.qp, a.kp, a.Nb, a.kc, a.kn, a.mask, a.crit, a.excl, a.pc,
-                                        a.marg, a.mbits, a.Nbc, a.Nbp, a.mcount, a.n_last, a.ulist, a.ucount, a.slots,
+                                        a.marg, a.mbits, a.Nbc, a.Nbp, a.mcount, a.n_last, a.ulist, a.ucount,
                                         a.inv_sqrt_d);
     return hipGetLastError();
 }

@@ -19,7 +19,6 @@ struct ClassifyArgs {
     int n_last;       // valid tokens of the last block
     uint32_t *ulist;  // nullable [BH][ceil(Nb/2)][2*kc] union of each row pair's critical lists
     int32_t *ucount;  // [BH][ceil(Nb/2)] union lengths
-    uint32_t *slots;  // nullable [BH][ceil(Nb/2)][kc] slot schedule of each row pair (16-bit path)
     double inv_sqrt_d;
 };
 

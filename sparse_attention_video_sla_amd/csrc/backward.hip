@@ -21,6 +21,10 @@
 //   keys:  v'_u = W v_u, dphi(k_u) = dh'_j v'_u + dz_j, dv'_u = dh'_j^T phi(k_u),
 //          dv_u += W^T dv'_u, dW += sum_u dv'_u v_u^T;
 //   phi = softmax over channels: dx = phi * (dphi - phi . dphi).
+// Every product of the linear part runs on fp16 MFMA with fp32 accumulation;
+// operands derived from dO (dO, dh'_j, dv') carry a power of two per block
+// that puts the block's largest magnitude in [0.5, 1), and the per-row state
+// gradients are summed over the rows as bf16 pairs hi + lo.
 #include "sla_device.h"
 #include "sla_launch.h"
 #include "tile_common.h"

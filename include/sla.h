@@ -145,8 +145,9 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
  *   gives zeros.  kmax in [1, Nb]; Nb = ceil(N/64) <= 4095.
  * q, k, v: [B,H,N,d] bf16 (float32: SLA_ERR_UNSUPPORTED); out: [B,H,N,d] of
  *   out_dtype (F32 or BF16).  workspace: sla_lists_workspace_size() bytes,
- *   256-byte aligned.  The cost of a pair of rows follows the number of
- *   distinct blocks the two rows list (a block both list counts once). */
+ *   256-byte aligned.  Rows 2p and 2p+1 share a schedule of slots (blocks
+ *   both list, then their other blocks side by side); each row's cost
+ *   follows the number of slots of its pair. */
 sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes);
 sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
                              int B, int H, int N, int d, int block, const int32_t *lists, const int32_t *counts,

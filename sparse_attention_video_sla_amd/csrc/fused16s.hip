@@ -55,7 +55,8 @@ template <> __device__ __forceinline__ void store4s<bf16>(bf16 *p, float a, floa
 
 // SLOTS: the blocks come from a slot schedule of row pairs (the workgroup
 // takes its row's half of each slot: a key block index in the low 12 bits,
-// frame marks or 0xF for padding in the top 4) instead of critical lists;
+// frame marks or 0xF for padding in the top 4; a padding half costs two
+// barriers and nothing else) instead of critical lists;
 // MARKS: those halves may carry frame marks (bit 2a + c set: query part a
 // does not see key part c, part 1 being what follows a frame boundary inside
 // the block).
@@ -120,6 +121,8 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         if constexpr (SLOTS) return (sl[c] >> (hb + 12)) & 0xFu;
         else return 0u;
     };
+    // a padding half: this row has no block in the slot (no load, no work)
+    auto pad = [&](int c) __attribute__((always_inline)) { return SLOTS && marks_of(c) == 0xFu; };
     const int qpart = (MARKS && fp > 0 && 32 * qh + l32 >= frame_split(i, fp)) ? 1 : 0;
     const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, head_bytes);
@@ -143,11 +146,13 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // the tile offset goes into the per-lane offset, which the buffer's bounds
     // check covers (a ragged last tile reads zeros)
     auto load_k = [&](int c, int slot) __attribute__((always_inline)) {
+        if (pad(c)) return;
         const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) dma16(rk, &Kk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
     };
     auto load_v = [&](int c) __attribute__((always_inline)) {
+        if (pad(c)) return;
         const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov0 + off + 1024 * u, 0);
@@ -164,12 +169,9 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16(sacc, ak[s], qf[s]);
-        if constexpr (SLOTS) {
+        if constexpr (MARKS) {
             const uint32_t marks = marks_of(c);
-            if (marks == 0xFu) [[unlikely]] {           // padding: no key of the slot for this row
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = NEG_INF;
-            } else if (MARKS && marks != 0u) {           // a frame boundary hides some keys
+            if (marks != 0u) {                           // a frame boundary hides some keys
                 const int ks = fp > 0 ? frame_split(j, fp) : 64;
                 const uint32_t hide = marks >> (2 * qpart);
 #pragma unroll
@@ -223,11 +225,12 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // into it, accumulate, barrier (the V tile free), load V(c+1).  Each
     // load has a whole phase or two to land.
     auto block = [&](int c, int slot) __attribute__((always_inline)) {
-        score(c, slot);
+        const bool work = !pad(c);                       // uniform across the workgroup
+        if (work) score(c, slot);
         wait_vm0();
         lds_barrier();
         if (c + 2 < kc) load_k(c + 2, slot);
-        accumulate();
+        if (work) accumulate();
         lds_barrier();
         if (c + 1 < kc) load_v(c + 1);
     };

@@ -675,8 +675,8 @@ static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_
     auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
     o->fwd = 0;
     o->o_s = take(sizeof(float) * BH * N * d);
-    o->lse = take(sizeof(float) * BH * N);
-    o->dbuf = take(sizeof(float) * BH * N);
+    o->lse = take(sizeof(float) * BH * 64 * Nb);       // rows padded to whole blocks (aligned runs)
+    o->dbuf = take(sizeof(float) * BH * 64 * Nb);
     o->tlist = take(sizeof(uint16_t) * BH * Nb * Nb);
     o->tcnt = take(sizeof(int32_t) * BH * Nb);
     o->mbitsT = take(sizeof(uint32_t) * BH * (2 * L->Nbc / 32) * L->Nbp);

@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
         }
     }
     Dr = half_swap_sum(Dr);
-    if (kh == 0 && hh == 0 && qvalid) dbuf[bh * N + qrow] = Dr;
-    const float lse2 = qvalid ? lse[bh * N + qrow] : __builtin_inff();
+    if (kh == 0 && hh == 0 && qvalid) dbuf[bh * (64L * Nb) + qrow] = Dr;
+    const float lse2 = qvalid ? lse[bh * (64L * Nb) + qrow] : __builtin_inff();
 
     int koff[NS];
 #pragma unroll
@@ -325,13 +325,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict_
         for (int r = 0; r < 16; ++r) dvt[ct][r] = dkt[ct][r] = 0.f;
     auto produce = [&](int c, int slot) __attribute__((always_inline)) {
         const int i = tl[c];
-        // the rows of the accumulator this lane holds, their lse and D
+        // the rows of the accumulator this lane holds (four runs of four,
+        // 16-byte aligned in the per-head rows of 64 Nb), their lse and D
         float lr[16], dr[16];
+        const long rb = bh * (64L * Nb) + 64 * i + 32 * rh + 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 64 * i + 32 * rh + 8 * (r >> 2) + 4 * hh + (r & 3);
-            lr[r] = row < N ? lse[bh * N + row] : __builtin_inff();
-            dr[r] = row < N ? dbuf[bh * N + row] : 0.f;
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 lv = *reinterpret_cast<const f32x4 *>(lse + rb + 8 * g);
+            const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dbuf + rb + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = 64 * i + 32 * rh + 8 * g + 4 * hh + e < N;
+                lr[4 * g + e] = ok ? lv[e] : __builtin_inff();
+                dr[4 * g + e] = ok ? dv4[e] : 0.f;
+            }
         }
         f32x16 sacc, pacc;
 #pragma unroll

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
         // log-sum-exp of the row's sparse softmax in the kernel's log2 units
         // (P = exp2(s * log2(e) / sqrt(d) - lse)), +inf for a row with no key
-        if (lse && kh == 0 && hh == 0 && qvalid) lse[bh * N + qrow] = lt > 0.f ? mm + __log2f(lt) : __builtin_inff();
+        if (lse && kh == 0 && hh == 0 && qvalid) lse[bh * (64L * Nb) + qrow] = lt > 0.f ? mm + __log2f(lt) : __builtin_inff();
 #pragma unroll
         for (int t = 0; t < NCH; ++t)
 #pragma unroll
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
                 for (int e = 0; e < 4; ++e) mine[t][4 * g + e] = (mine[t][4 * g + e] * as + y[e] * ao) * inv;
             }
     }
-    if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * N + qrow] = __builtin_inff();
+    if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * (64L * Nb) + qrow] = __builtin_inff();
 
     if (lin) {
         constexpr float LOG2E = 1.4426950408889634f;

@@ -55,7 +55,7 @@ struct FusedArgs {
     const int32_t *pcount;   // nullable: slots used per pair ([BH][ceil(Nb/2)], or [ceil(Nb/2)] with bcast)
     bool bcast;              // one schedule shared by every head
     int fp;                  // tokens per frame for the frame marks in the slots (0: no marks)
-    float *lse;              // nullable: [BH][N] log-sum-exp of each row's sparse softmax (log2 units)
+    float *lse;              // nullable: [BH][64 Nb] log-sum-exp of each row's sparse softmax (log2 units)
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere
     int Lp;
@@ -95,14 +95,14 @@ hipError_t launch_lvsa_frames(const LvsaParams &p, int32_t *lohi, int32_t *sets,
 struct BackwardArgs {
     const void *q, *k, *v, *dout;     // [BH][N][D] bf16
     const float *w;                   // [D][D]
-    const float *o_s, *lse;           // sparse output and its log-sum-exp (log2 units)
+    const float *o_s, *lse;           // sparse output [BH][N][D] and its log-sum-exp [BH][64 Nb] (log2 units)
     const int32_t *crit;              // [BH][Nb][kc]
     int kc;
     const int8_t *mask;               // [BH][Nb][Nb] labels
     const void *hhat;                 // [BH][Nb][Lp] f16 marginal states (Ĥ'^T, Ẑ; / m_i)
     const int32_t *mcount;            // [BH][Nb] marginal tokens per row
     float *dq, *dk, *dv, *dw;         // gradients
-    float *dbuf;                      // [BH][N] D_r = dO_r . O_s,r
+    float *dbuf;                      // [BH][64 Nb] D_r = dO_r . O_s,r
     uint16_t *tlist;                  // [BH][Nb][Nb] transposed critical lists
     int32_t *tcnt;                    // [BH][Nb]
     uint32_t *mbitsT;                 // [BH][2 Nbc / 32][Nbp] transposed marginal indicator bits

@@ -95,3 +95,26 @@ def test_forward_lists_bf16_output(sla):
     ref = ol.attention_lists(inp.q, inp.k, inp.v, lists, counts)
     got = out.double().cpu().numpy()
     assert np.abs(got - ref).max() <= 1e-2 + 2.0 ** -8 * np.abs(ref).max()
+
+
+def test_forward_lists_full_size_sampled(sla):
+    """The Wan2.1 480p shape (B=1, H=12, N=32760, d=128) with random lists of
+    up to 26 blocks per row (empty rows and junk entries included) in one
+    call; sampled query blocks of two heads (first, ragged last, random)
+    against the oracle row by row."""
+    from sparse_attention_video_sla_amd.inputs import make_workload
+    inp = make_workload(1)
+    B, H, N, d = inp.q.shape
+    Nb = -(-N // 64)
+    lists, counts = random_lists(B, H, Nb, 26, seed=11, extra_junk=True)
+    say("lists full size", B, H, N, d)
+    out = sla.forward_lists(dev(inp.q), dev(inp.k), dev(inp.v), torch.from_numpy(lists).cuda(),
+                            torch.from_numpy(counts).cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = [(bh, i) for bh in (0, 7) for i in sorted({0, Nb - 1, *rng.integers(1, Nb - 1, size=3).tolist()})]
+    ref = ol.attention_lists(inp.q, inp.k, inp.v, lists, counts, rows=rows)
+    got = out.reshape(B * H, N, d)
+    for x, (bh, i) in enumerate(rows):
+        r0, r1 = 64 * i, min(N, 64 * (i + 1))
+        check(got[bh, r0:r1], ref[x, :r1 - r0])

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     constexpr float TAU = 64.f;
     __shared__ __attribute__((aligned(1024))) T Kk[2][TILE];
     __shared__ __attribute__((aligned(1024))) T Vk[TILE];
+    __shared__ __attribute__((aligned(16))) S Zl[D];        // the row's Ẑ_i
 
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
@@ -156,6 +157,20 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov0 + off + 1024 * u, 0);
+    };
+    // the row's marginal state Ĥ_i^T ([c][a], D rows of 2D bytes, stored in
+    // the K ring with the K layout's chunk swizzle once the loop is done) and
+    // Ẑ_i, straight into LDS: one round trip for the whole read-out (issuing
+    // it inside the last block instead spills registers in the loop)
+    const S *hr = hhat + rid * (long)Lp;
+    auto load_hhat = [&]() __attribute__((always_inline)) {
+        constexpr int NBH = D * D * 2 / 1024 / 4;        // 1 KB pieces per wave
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(hr, (uint32_t)((D * D + D) * sizeof(S)));
+        T *dst = &Kk[0][0];
+#pragma unroll
+        for (int u = 0; u < NBH; ++u)
+            dma16(rh, dst + (wave * NBH + u) * 512, off_klayout<D>((wave * NBH + u) * 1024 + 16 * lane), 0);
+        if (wave == 0 && lane < D / 8) dma16(rh, Zl, (uint32_t)(D * D * sizeof(S)) + 16 * lane, 0);
     };
     v8<T> pb[2];
     // S^T = K Q^T of block c and its softmax: P^T in pb
@@ -247,7 +262,57 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         }
         if (c < kc) block(c, 0);
     }
+    if (lin) load_hhat();                                // the K ring is free once the loop is done
     wait_vm0();                                          // no load into LDS outlives the loop
+    lds_barrier();                                       // Ĥ_i and Ẑ_i visible
+
+    // linear read-out for this wave's output channels (tiles NCH*kh ..):
+    // y = Ĥ_i phi(q) / (phi(q).Ẑ_i), Ĥ_i rows from LDS
+    f32x16 yl[NCH];
+    float rden = 0.f;
+    if (lin) {
+        constexpr float LOG2E = 1.4426950408889634f;
+        float mq = NEG_INF;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mq = fmaxf(mq, to_f32<T>(qf[s][e]));
+        mq = half_swap_max(mq);
+        v8<S> ph[NS];                                    // exp(q - max), then phi(q)
+        float se = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = fast_exp2((to_f32<T>(qf[s][e]) - mq) * LOG2E);
+                se += x;
+                ph[s][e] = from_f32<S>(x);
+            }
+        se = half_swap_sum(se);
+        const float inv_se = 1.f / se;
+        float den = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const v8<S> hz = ld8<S>(&Zl[16 * s + 8 * hh]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ph[s][e] = from_f32<S>(to_f32<S>(ph[s][e]) * inv_se);
+                den += to_f32<S>(ph[s][e]) * to_f32<S>(hz[e]);
+            }
+        }
+        den = half_swap_sum(den);
+        rden = 1.f / den;
+        const S *Hs = reinterpret_cast<const S *>(&Kk[0][0]);
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const int c = 32 * (NCH * kh + t) + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yl[t][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) mma16(yl[t], ld8<S>(&Hs[c * D + ((2 * s + hh) ^ kswz<D>(c)) * 8]), ph[s]);
+        }
+    }
+    lds_barrier();                                       // the ring is free for the exchange
 
     // merge the two key halves: wave kh keeps channel tiles NCH*kh .. +NCH-1.
     // Exchange area: 4*NCH f32x4 per lane and wave in Kk, m and l in Vk.
@@ -274,7 +339,6 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         xl[wave * 64 + lane] = l;
     }
 
-    const S *hr = hhat + rid * (long)Lp;
     if (kc > 0) {
         lds_barrier();
         const float mo = xm[partner * 64 + lane], lo = xl[partner * 64 + lane];
@@ -298,47 +362,10 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * (64L * Nb) + qrow] = __builtin_inff();
 
     if (lin) {
-        constexpr float LOG2E = 1.4426950408889634f;
-        float mq = NEG_INF;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int t = 0; t < NCH; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mq = fmaxf(mq, to_f32<T>(qf[s][e]));
-        mq = half_swap_max(mq);
-        float ex[NS][8];
-        float se = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                ex[s][e] = fast_exp2((to_f32<T>(qf[s][e]) - mq) * LOG2E);
-                se += ex[s][e];
-            }
-        se = half_swap_sum(se);
-        const float inv_se = 1.f / se;
-        v8<S> ph[NS];
-        float den = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const v8<S> hz = ld8<S>(hr + D * D + 16 * s + 8 * hh);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                ph[s][e] = from_f32<S>(ex[s][e] * inv_se);
-                den += to_f32<S>(ph[s][e]) * to_f32<S>(hz[e]);
-            }
-        }
-        den = half_swap_sum(den);
-        const float rden = 1.f / den;
-#pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            f32x16 y;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) mma16(y, ld8<S>(hr + (32 * (NCH * kh + t) + l32) * D + 16 * s + 8 * hh), ph[s]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mine[t][r] += y[r] * rden;
-        }
+            for (int r = 0; r < 16; ++r) mine[t][r] += yl[t][r] * rden;
     }
 
     if (qvalid) {

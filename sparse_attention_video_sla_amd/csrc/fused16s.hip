@@ -134,8 +134,13 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const int r = 32 * kh + l32;
         koff[s] = r * D + ((2 * s + hh) ^ kswz<D>(r)) * 8;
     }
-    int toff[NCT][2];                                    // V transposing reads (V-swizzled rows)
+    // V transposing reads (V-swizzled rows): the second run of a step lies
+    // 8 rows below the first at the same swizzle, 8D elements further on
+    int toff[NCT][2];
     tr_offsets<D, true>(lane, toff);
+    int tv[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) tv[ct] = toff[ct][0];
     uint32_t ok_[NBW];
 #pragma unroll
     for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const T *base = &Vk[(32 * kh + 16 * ks) * D];
-                mma16(o[ct], cat8<T>(lds_tr_raw<T>(base + toff[ct][0]), lds_tr_raw<T>(base + toff[ct][1])), pb[ks]);
+                mma16(o[ct], cat8<T>(lds_tr_raw<T>(base + tv[ct]), lds_tr_raw<T>(base + tv[ct] + 8 * D)), pb[ks]);
             }
     };
     // Block c: score (K(c) visible; V(c) and K(c+1) in flight), wait for

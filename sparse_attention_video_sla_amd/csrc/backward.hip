@@ -563,6 +563,17 @@ __global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restr
     // 2. y^T and s X^T for the wave's channel half and token half
     const int rh = wave & 1, chh = wave >> 1;
     const int r = 32 * rh + l32;                         // this lane's token
+    const int row = 64 * i + r;
+    float *qg = dq + (bh * N + row) * (long)D;
+    // this lane's dQ values, read now so that the load overlaps the products
+    f32x4 dqv[NCT][4];
+#pragma unroll
+    for (int mt = 0; mt < NCT; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int a0 = (D / 2) * chh + 32 * mt + 8 * g + 4 * hh;
+            dqv[mt][g] = row < N ? *reinterpret_cast<const f32x4 *>(qg + a0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     f32x16 yt[NCT], xt[NCT];
 #pragma unroll
     for (int mt = 0; mt < NCT; ++mt)
@@ -615,15 +626,13 @@ __global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restr
     }
     __syncthreads();
     const float dts = Dn[r] * (Tx[0][r] + Tx[1][r]), isc = 1.f / sc;
-    const int row = 64 * i + r;
     if (row < N) {
-        float *qg = dq + (bh * N + row) * (long)D;
 #pragma unroll
         for (int mt = 0; mt < NCT; ++mt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int a0 = (D / 2) * chh + 32 * mt + 8 * g + 4 * hh;
-                f32x4 cur = *reinterpret_cast<const f32x4 *>(qg + a0);
+                f32x4 cur = dqv[mt][g];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) cur[e] += (float)pn4[mt][g][e] * (xt[mt][4 * g + e] - dts) * isc;
                 *reinterpret_cast<f32x4 *>(qg + a0) = cur;

@@ -152,3 +152,58 @@ def test_sta_tile_order_matches_oracle_and_shapes_are_checked(lib):
     assert lib.sla_sta_workspace_size(1, 1, 30, 48, 80, 6, 8, 5, 18, 27, 24, ctypes.byref(n)) != 0   # 5 does not divide 80
     assert lib.sla_sta_workspace_size(1, 1, 6, 6, 6, 3, 3, 3, 18, 27, 24, ctypes.byref(n)) != 0      # 27-token tiles
     assert lib.sla_sta_workspace_size(1, 1, 30, 48, 80, 6, 8, 8, 0, 27, 24, ctypes.byref(n)) != 0    # empty window
+
+
+def bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, do=FAKE, ind=_lib.SLA_BF16, B=1, H=1, N=128, d=128, block=64,
+             rc=0.05, rn=0.10, phi=0, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.sla_backward(a["q"], a["k"], a["v"], a["w"], a["do"], a["ind"], a["B"], a["H"], a["N"], a["d"],
+                            a["block"], a["rc"], a["rn"], a["phi"], a["dq"], a["dk"], a["dv"], a["dw"], a["ws"],
+                            a["wsb"], a["stream"])
+
+
+def test_backward_rejects_before_launch(lib):
+    """sla_backward validates everything on the host before any launch."""
+    assert bwd(lib, do=None) == _lib.SLA_ERR_INVALID_ARG
+    assert bwd(lib, dw=None) == _lib.SLA_ERR_INVALID_ARG
+    assert bwd(lib, ind=_lib.SLA_F32) == _lib.SLA_ERR_UNSUPPORTED
+    assert bwd(lib, phi=1) == _lib.SLA_ERR_UNSUPPORTED
+    assert bwd(lib, d=96) == _lib.SLA_ERR_UNSUPPORTED
+    assert bwd(lib, N=0) == _lib.SLA_ERR_INVALID_ARG
+    assert bwd(lib, rc=0.7, rn=0.4) == _lib.SLA_ERR_INVALID_ARG
+    assert bwd(lib, ws=None) == _lib.SLA_ERR_INVALID_ARG
+    assert bwd(lib, wsb=16) == _lib.SLA_ERR_WORKSPACE
+    n = ctypes.c_size_t()
+    assert lib.sla_backward_workspace_size(1, 1, 128, 128, 64, 0.05, 0.10, ctypes.byref(n)) == 0
+    assert bwd(lib, ws=FAKE + 8, wsb=n.value) == _lib.SLA_ERR_INVALID_ARG   # misaligned workspace
+
+
+def test_backward_workspace_size(lib):
+    """The backward workspace holds the forward's and grows with the sequence."""
+    nf, nb, nb2 = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sla_workspace_size(1, 12, 32760, 128, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(nf)) == 0
+    assert lib.sla_backward_workspace_size(1, 12, 32760, 128, 64, 0.05, 0.10, ctypes.byref(nb)) == 0
+    assert nb.value > nf.value
+    assert lib.sla_backward_workspace_size(1, 12, 2 * 32760, 128, 64, 0.05, 0.10, ctypes.byref(nb2)) == 0
+    assert nb2.value > nb.value
+    assert lib.sla_backward_workspace_size(1, 12, 32760, 128, 64, 0.05, 0.10, None) == _lib.SLA_ERR_INVALID_ARG
+    assert lib.sla_backward_workspace_size(1, 12, 32760, 64, 32, 0.05, 0.10, ctypes.byref(nb)) == _lib.SLA_ERR_UNSUPPORTED
+
+
+def test_lists_entry_points_reject(lib):
+    n = ctypes.c_size_t()
+    assert lib.sla_lists_workspace_size(1, 2, 1000, 0, ctypes.byref(n)) == _lib.SLA_ERR_INVALID_ARG    # kmax < 1
+    assert lib.sla_lists_workspace_size(1, 2, 1000, 17, ctypes.byref(n)) == _lib.SLA_ERR_INVALID_ARG   # kmax > Nb = 16
+    assert lib.sla_lists_workspace_size(1, 2, 64 * 4096, 8, ctypes.byref(n)) == _lib.SLA_ERR_UNSUPPORTED   # 4096 blocks
+    assert lib.sla_lists_workspace_size(1, 2, 1000, 16, ctypes.byref(n)) == 0 and n.value > 0
+    args = [FAKE, FAKE, FAKE, _lib.SLA_BF16, _lib.SLA_F32, 1, 2, 1000, 128, 64, FAKE, FAKE, 8, FAKE, FAKE, 0, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.sla_forward_lists(*a)
+    assert call(a10=None) == _lib.SLA_ERR_INVALID_ARG            # no lists
+    assert call(a3=_lib.SLA_F32) == _lib.SLA_ERR_UNSUPPORTED      # float inputs
+    assert call(a12=40) == _lib.SLA_ERR_INVALID_ARG              # kmax > Nb
+    assert call() == _lib.SLA_ERR_WORKSPACE                      # no room for the schedule

@@ -41,6 +41,7 @@ def dev(x):
     (2, 1, 640, 128, 1.0, 0.0),     # dense: no linear branch
     (1, 1, 600, 64, 0.0, 0.5),      # no critical block: linear branch only
     (1, 1, 2048, 128, 0.05, 0.10),  # the default fractions
+    (2, 2, 700, 64, 0.2, 0.3),      # dW summed over batch and heads, ragged
 ])
 def test_backward_matches_oracle(sla, B, H, N, d, rc, rn):
     say("backward", B, H, N, d, rc, rn)

@@ -79,17 +79,36 @@ def fused_traffic(path=TRAFFIC_FILE, kernel="fused16s_kernel", source="fused16s.
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
     calibration), or None when the kernel source has changed since the
     counters were taken."""
-    import hashlib
     import re
     try:
         text = open(path).read()
-        src = open(os.path.join(CSRC, source), "rb").read()
+        sha = source_sha(source)
     except OSError:
         return None
     m = re.search(kernel + r" HBM bytes per launch: (\d+) \(source sha256 ([0-9a-f]{16})\)", text)
-    if not m or hashlib.sha256(src).hexdigest()[:16] != m.group(2):
+    if not m or sha != m.group(2):
         return None
     return int(m.group(1))
+
+
+def source_sha(source):
+    """First 16 hex digits of the sha256 over a kernel source and, depth
+    first, every header of the package it includes with quotes (each once),
+    so that a change to a shared header also voids stored counters."""
+    import hashlib
+    import re
+    h, seen = hashlib.sha256(), set()
+
+    def add(name):
+        if name in seen:
+            return
+        seen.add(name)
+        src = open(os.path.join(CSRC, name), "rb").read()
+        h.update(src)
+        for inc in re.findall(rb'^#include "([^"]+)"', src, re.M):
+            add(inc.decode())
+    add(source)
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(inp, wl, rc, rn, heads):

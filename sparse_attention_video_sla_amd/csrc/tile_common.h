@@ -49,8 +49,14 @@ __device__ __forceinline__ int frame_split(int blk, int fp) {
     return bnd < 64 ? bnd : 64;
 }
 
-// swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r)
-template <int D> __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+// swizzle of the K tile: chunk c of row r sits at chunk c ^ kswz(r). Row
+// reads (a lane per row, 16 bytes each) touch every bank once per 16 lanes,
+// and the transposing reads of tr_offsets every bank exactly twice: the two
+// low row bits pick the high chunk bits and the next two the low ones
+template <int D> __device__ __forceinline__ int kswz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                    : (((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2));
+}
 
 // swizzle of a tile that is only read transposed (V): chunk c of row r sits
 // at chunk c ^ vswz(r), so that the 8 rows x 4 chunks of one transposing read

@@ -13,7 +13,8 @@ kernel, timed live with HIP events recorded on its stream; its algorithmic
 flops are the critical pairs plus 2*64*d*d per query block (phi(Q) times the
 marginal state; the projection is folded into the state kernel).
 `roofline.traffic` is the kernel's HBM bytes per launch from the committed
-rocprofv3 counter summary, reported only while the kernel source matches.
+rocprofv3 counter summary, reported only while the kernel source and the
+package headers it includes match the ones the counters were taken with.
 `cpu_baseline` times the CPU oracle on whole heads (by default all of them).
 
 With --lvsa it prints instead one JSON line for LVSA frame-level sparse
@@ -34,7 +35,9 @@ With --backward it prints instead one JSON line for the SLA backward pass
 same Wan2.1 480p workload; `value` counts the forward's F plus 10*64*64*d per
 critical pair (five products), 6*64*d*d per query block and 10*64*d*d per
 key block of the linear branch, and (d*d + d) per marginal pair (the
-transposed sums).
+transposed sums).  Its `roofline` is for the slowest stage; `traffic` is
+filled from the backward's counter summary when that stage is one kernel
+(dQ, dK/dV or the linear keys).
 
 With --quality it prints instead one JSON line for the mask-quality
 diagnostics (sla_block_mass + sla_mask_stats) on the same workload: the
@@ -61,6 +64,9 @@ CSRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
 LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16s_lvsa_wan6x_stats.md")
 STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16s_sta_hunyuan_stats.md")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_backward_wan480p_stats.md")
+# backward stages that are one kernel each (the others span several)
+BWD_STAGE_KERNEL = {"dq": "bwd_dq_kernel", "dkv": "bwd_dkv_kernel", "linear_keys": "bwd_lin_key_kernel"}
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -463,7 +469,10 @@ def run_backward(args, wl):
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64, "crit_frac": rc,
                    "negl_frac": rn, "k_c": kc, "k_n": kn, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "backward stage " + dom,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": (fused_traffic(BWD_TRAFFIC_FILE, BWD_STAGE_KERNEL[dom], "backward.hip")
+                                 if dom in BWD_STAGE_KERNEL else None),
+                     "kernel": "backward stage " + dom,
                      "flops_per_launch": fl, "avg_launch_ms": round(st_ms[dom], 4)},
         "stages": stages,
     }

@@ -41,7 +41,11 @@
  *     process ends.  sla_forward runs its block-state kernel on that side
  *     stream, forked from and joined back to the caller's stream, so all of
  *     its work is still ordered on the caller's stream.  Results are
- *     deterministic run to run (no atomics).
+ *     bitwise deterministic run to run: no kernel adds floating-point values
+ *     with atomics (the only atomics are ORs into bit sets, whose result
+ *     does not depend on their order), and every sum over workgroups (dW in
+ *     sla_backward) adds per-workgroup partials in a fixed order over a
+ *     fixed number of workgroups.
  */
 #ifndef SLA_H
 #define SLA_H
@@ -61,11 +65,24 @@ typedef enum {
     SLA_ERR_DEVICE = 4         /* HIP launch / runtime failure */
 } sla_status;
 
+/* Element types.  A C caller may pass any int for an enum argument; C++
+ * gives these enums int as their underlying type so that the library can
+ * read such a value and reject it (SLA_ERR_UNSUPPORTED) instead of holding
+ * an enum value outside its range.  Both spellings have the size and the
+ * calling convention of int. */
+#ifdef __cplusplus
+typedef enum : int { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
+#else
 typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
+#endif
 
 /* Feature map of the linear branch: softmax over the d channels of each token
  * (the SLA article, section 5, reports softmax beating ELU+1 and ReLU). */
+#ifdef __cplusplus
+typedef enum : int { SLA_PHI_SOFTMAX = 0 } sla_phi;
+#else
 typedef enum { SLA_PHI_SOFTMAX = 0 } sla_phi;
+#endif
 
 /* Library version (major*10000 + minor*100 + patch). */
 int sla_version(void);
@@ -226,7 +243,10 @@ sla_status sla_forward_sta(const void *q, const void *k, const void *v, sla_dtyp
  *   stats [rows][4] float32 = mass on the critical, marginal and negligible
  *   blocks, and the 95 % block density: the smallest number of key blocks,
  *   taken by decreasing mass, whose mass reaches 0.95 of the row's total,
- *   divided by Nb.  Nb <= 2432. */
+ *   divided by Nb.  Sums in fp64 (class masses rounded once to float32), so
+ *   the count equals that of an fp64 cumulative sum over the sorted masses
+ *   unless a row's cumulative mass lies within fp64 rounding of 0.95 of its
+ *   total.  Nb <= 2432. */
 sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,
                           float *mass, void *stream);
 sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int Nb, float *stats, void *stream);

@@ -127,7 +127,7 @@ thread_local StageTimer g_timer;
 
 // Records the start (end = 0) or the end (end = 1) of stage `i` of the current call.
 void mark_stage(StageEvents *ev, int i, int end, hipStream_t s) {
-    if (ev && (*ev)[2 * i + end]) hipEventRecord((*ev)[2 * i + end], s);
+    if (ev && (*ev)[2 * i + end]) (void)hipEventRecord((*ev)[2 * i + end], s);   // timing only: a failed record is not an error of the call
 }
 
 // The event set of a new call while timing is on, else nullptr.
@@ -579,7 +579,7 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     struct JoinOnExit {
         hipStream_t s;
         SideStream *ss = nullptr;
-        ~JoinOnExit() { if (ss) hipStreamWaitEvent(s, ss->join, 0); }
+        ~JoinOnExit() { if (ss) (void)hipStreamWaitEvent(s, ss->join, 0); }   // on an error return already being reported
     } guard{s};
     if (states) {
         st = device_status(side_stream(&ss), "side stream");
@@ -659,7 +659,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
 // ---- backward ----------------------------------------------------------------
 
 struct BwdLayout {
-    size_t fwd, o_s, lse, dbuf, tlist, tcnt, mbitsT, unit, dh2, dhs, total;
+    size_t fwd, o_s, lse, dbuf, tlist, tcnt, mbitsT, unit, dh2, dhs, dwp, total;
 };
 
 static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_frac, double negl_frac,
@@ -683,6 +683,7 @@ static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_
     o->unit = take(sizeof(int32_t) * BH * Nb);
     o->dh2 = take(sizeof(uint16_t) * BH * 2 * L->Nbc * L->Lp);
     o->dhs = take(sizeof(float) * BH * Nb * L->Lp);
+    o->dwp = take(sizeof(float) * sla::backward_key_groups((long)BH, Nb, d) * d * d);
     o->total = off;
     return SLA_OK;
 }
@@ -735,7 +736,7 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
     a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbuf = (float *)(ws + o.dbuf);
     a.tlist = (uint16_t *)(ws + o.tlist); a.tcnt = (int32_t *)(ws + o.tcnt);
     a.mbitsT = (uint32_t *)(ws + o.mbitsT); a.unit = (int32_t *)(ws + o.unit);
-    a.dh2 = ws + o.dh2; a.dhs = (float *)(ws + o.dhs);
+    a.dh2 = ws + o.dh2; a.dhs = (float *)(ws + o.dhs); a.dwp = (float *)(ws + o.dwp);
     a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Nbp = L.Nbp; a.Lp = L.Lp; a.D = d;
     mark_stage(ev, 1, 0, s);
     st = device_status(sla::launch_backward_dq(a, s), "backward dq launch");

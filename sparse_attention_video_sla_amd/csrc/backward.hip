@@ -683,7 +683,7 @@ template <int D>
 __global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
                                                             const float *__restrict__ w, const float *__restrict__ dhs,
                                                             int Lp, float *__restrict__ dk, float *__restrict__ dv,
-                                                            float *__restrict__ dw, long BH, int N, int Nb) {
+                                                            float *__restrict__ dwp, long BH, int N, int Nb) {
     constexpr int NT = 4 * D, NW = NT / 64;              // threads, waves (2 tiles of tokens x D/32 of channels)
     constexpr int STR = D + 8;
     constexpr int CPR = D / 8, RPP = NT / CPR, NP = 64 / RPP;
@@ -868,13 +868,26 @@ __global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restri
             }
         }
     }
+    // this workgroup's partial dW, summed over the workgroups in a fixed order
+    // by bwd_dw_reduce_kernel
+    float *part = dwp + (long)blockIdx.x * D * D;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int x = wave * TPW + t, ct = x / (D / 32), et = x % (D / 32);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            atomicAdd(&dw[(32 * ct + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + 32 * et + l32], wacc[t][e]);
+        for (int e = 0; e < 16; ++e) part[(32 * ct + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + 32 * et + l32] = wacc[t][e];
     }
+}
+
+// dW = the sum of the linear-keys workgroups' partials, in ascending
+// workgroup order (the same bits on every run)
+__global__ __launch_bounds__(256) void bwd_dw_reduce_kernel(const float *__restrict__ part, int groups, long n,
+                                                            float *__restrict__ dw) {
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n) return;
+    float s = 0.f;
+    for (int g = 0; g < groups; ++g) s += part[(long)g * n + t];
+    dw[t] = s;
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -912,8 +925,7 @@ hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st) {
-    // zero dW; the transposed indicator bits and unit counts
-    bwd_zero_kernel<<<(unsigned)((a.D * a.D + 255) / 256), 256, 0, st>>>(a.dw, (long)a.D * a.D);
+    // the transposed indicator bits and unit counts
     const long nt = a.BH * (2 * a.Nbc / 32) * (long)a.Nbp;
     bwd_mbitsT_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, st>>>(a.mask, a.BH, a.Nb, a.Nbc, a.Nbp, a.mbitsT, a.unit);
     const unsigned rows = (unsigned)(a.BH * a.Nbc);
@@ -933,18 +945,25 @@ hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st) {
     return launch_assemble(as, st);
 }
 
+// one workgroup per compute unit of an MI355X (256), two for d = 64 (they
+// fit a compute unit's LDS twice); a fixed number, not the device's
+long backward_key_groups(long BH, int Nb, int D) {
+    const long per_cu = D == 64 ? 2 : 1;
+    return std::min<long>(BH * Nb, per_cu * 256);
+}
+
 hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st) {
-    int dev = 0, cus = 0;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const long per_cu = a.D == 64 ? 2 : 1;               // workgroups that fit a compute unit's LDS
-    const unsigned gk = (unsigned)std::min<long>(a.BH * a.Nb, per_cu * std::max(cus, 1));
+    const unsigned gk = (unsigned)backward_key_groups(a.BH, a.Nb, a.D);
     if (a.D == 64)
         bwd_lin_key_kernel<64><<<gk, 256, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk, a.dv,
-                                                   a.dw, a.BH, a.N, a.Nb);
+                                                   a.dwp, a.BH, a.N, a.Nb);
     else
         bwd_lin_key_kernel<128><<<gk, 512, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk,
-                                                    a.dv, a.dw, a.BH, a.N, a.Nb);
+                                                    a.dv, a.dwp, a.BH, a.N, a.Nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long n = (long)a.D * a.D;
+    bwd_dw_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.dwp, (int)gk, n, a.dw);
     return hipGetLastError();
 }
 

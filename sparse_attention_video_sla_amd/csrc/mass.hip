@@ -165,9 +165,18 @@ __global__ __launch_bounds__(512) void block_mass16_kernel(const bf16 *__restric
 // by decreasing mass, whose mass reaches 0.95 of the row's total, over Nb.
 // The count comes from a bitwise search for the threshold t (masses are >= 0,
 // so their bit patterns order like their values): the largest t with
-// sum{mass >= t} >= target; then #{mass > t} plus as many of the blocks equal
-// to t as the remaining mass needs.  Sums are per-lane partials in block
-// order, then a fixed wave reduction.
+// sum{mass >= t} >= target; then #{mass > t} plus the blocks equal to t
+// added one at a time until the target is reached.  Every sum is in fp64
+// (per-lane partials in block order, then a fixed wave reduction), so the
+// count is the one an fp64 cumulative sum over the sorted masses gives,
+// except for a row whose cumulative mass lies within fp64 rounding of the
+// target.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
 template <int KM>
 __global__ __launch_bounds__(256) void mask_stats_kernel(const float *__restrict__ mass, const int8_t *__restrict__ mask,
                                                          long rows, int Nb, float *__restrict__ stats) {
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const float *__restrict
     const float *mr = mass + row * Nb;
     const int8_t *lr = mask + row * Nb;
     uint32_t key[KM];
-    float cls[3] = {0.f, 0.f, 0.f};                      // negligible, marginal, critical
-    float tot = 0.f;
+    double cls[3] = {0.0, 0.0, 0.0};                     // negligible, marginal, critical
+    double tot = 0.0;
 #pragma unroll
     for (int e = 0; e < KM; ++e) {
         const int j = lane + 64 * e;
@@ -186,19 +195,19 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const float *__restrict
         key[e] = __float_as_uint(x);
         if (j < Nb) {
             const int lb = lr[j];
-            cls[lb + 1] += x;
-            tot += x;
+            cls[lb + 1] += (double)x;
+            tot += (double)x;
         }
     }
 #pragma unroll
-    for (int c = 0; c < 3; ++c) cls[c] = wave_sum(cls[c]);
-    tot = wave_sum(tot);
-    const float target = 0.95f * tot;
+    for (int c = 0; c < 3; ++c) cls[c] = wave_sum_f64(cls[c]);
+    tot = wave_sum_f64(tot);
+    const double target = 0.95 * tot;
     auto sum_ge = [&](uint32_t t) {
-        float s = 0.f;
+        double s = 0.0;
 #pragma unroll
-        for (int e = 0; e < KM; ++e) s += key[e] >= t ? __uint_as_float(key[e]) : 0.f;
-        return wave_sum(s);
+        for (int e = 0; e < KM; ++e) s += key[e] >= t ? (double)__uint_as_float(key[e]) : 0.0;
+        return wave_sum_f64(s);
     };
     uint32_t lo = 0;
     for (int bit = 30; bit >= 0; --bit) {               // bit 31 (sign) is 0 for every mass
@@ -206,25 +215,25 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const float *__restrict
         if (sum_ge(cand) >= target) lo = cand;
     }
     int gt = 0, eq = 0;
-    float sgt = 0.f;
+    double sgt = 0.0;
 #pragma unroll
     for (int e = 0; e < KM; ++e) {
         const bool ok = lane + 64 * e < Nb;
         gt += (ok && key[e] > lo) ? 1 : 0;
         eq += (ok && key[e] == lo) ? 1 : 0;
-        sgt += (ok && key[e] > lo) ? __uint_as_float(key[e]) : 0.f;
+        sgt += (ok && key[e] > lo) ? (double)__uint_as_float(key[e]) : 0.0;
     }
-    gt = (int)wave_sum((float)gt);
-    eq = (int)wave_sum((float)eq);
-    sgt = wave_sum(sgt);
-    const float t = __uint_as_float(lo);
+    gt = (int)wave_sum_f64((double)gt);
+    eq = (int)wave_sum_f64((double)eq);
+    sgt = wave_sum_f64(sgt);
+    const double t = (double)__uint_as_float(lo);
     int need = gt;
-    if (sgt < target) need += t > 0.f ? min(eq, (int)ceilf((target - sgt) / t)) : eq;
+    for (double s = sgt; need < gt + eq && s < target; ++need) s += t;
     if (lane == 0) {
         float *o = stats + row * 4;
-        o[0] = cls[2];
-        o[1] = cls[1];
-        o[2] = cls[0];
+        o[0] = (float)cls[2];
+        o[1] = (float)cls[1];
+        o[2] = (float)cls[0];
         o[3] = (float)need / (float)Nb;
     }
 }

@@ -109,9 +109,13 @@ struct BackwardArgs {
     int32_t *unit;                    // [BH][Nb] = 64
     void *dh2;                        // [BH][2 Nbc][Lp] bf16 per-row state gradients (hi rows, then lo rows)
     float *dhs;                       // [BH][Nb][Lp] per-key-block state gradients
+    float *dwp;                       // [backward_key_groups][D][D] per-workgroup partial sums of dW
     long BH;
     int N, Nb, Nbc, Nbp, Lp, D;
 };
+// workgroups of the linear-keys kernel (a fixed count, so that dW sums its
+// per-workgroup partials in the same order on every device and every run)
+long backward_key_groups(long BH, int Nb, int D);
 hipError_t launch_backward_dq(const BackwardArgs &a, hipStream_t st);        // transposed lists + dQ (sparse)
 hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st);       // dK, dV (sparse)
 hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st);  // linear rows + transposed sums

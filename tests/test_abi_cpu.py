@@ -15,10 +15,13 @@ HEADER = os.path.join(ROOT, "include", "sla.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_lib.LIB_PATH):
+    # SLA_TEST_LIB: another build of the same sources (the sanitizer test
+    # runs this file against a host-sanitized copy)
+    path = os.environ.get("SLA_TEST_LIB") or _lib.LIB_PATH
+    if not os.path.exists(path):
         from sparse_attention_video_sla_amd import build
         build.build()
-    return _lib.load()
+    return _lib.load(path)
 
 
 def declared_functions():

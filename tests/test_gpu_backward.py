@@ -1,8 +1,10 @@
 """GPU parity of the SLA backward pass (sla_backward) against the fp64
 autograd oracle (oracle/backward.py), with the block labels from the C
-oracle's classification (bit-identical to the GPU's).  Bar: relative L2
-error <= 1e-2 for each of dq, dk, dv, dw (bf16 inputs; P and dS go to the
-matrix cores in bf16, 2^-9 relative rounding, accumulated in fp32)."""
+oracle's classification (bit-identical to the GPU's).  Bar, for each of dq,
+dk, dv and dw: relative L2 error <= 1e-2 and every element within 2e-2 of
+the largest magnitude of that gradient's reference (bf16 inputs; P and dS
+go to the matrix cores in bf16, 2^-9 relative rounding, accumulated in
+fp32; the linear branch in fp16 with a power-of-two scale per block)."""
 import sys
 
 import numpy as np
@@ -35,6 +37,26 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(torch.bfloat16)
 
 
+REL_L2, REL_ELEM = 1e-2, 2e-2
+
+
+def check(name, g, ref):
+    """Relative L2 and a per-element bound scaled by the reference's largest
+    magnitude (an all-zero reference must give all zeros)."""
+    assert np.isfinite(g).all(), name
+    d = np.abs(g - ref)
+    mref = np.abs(ref).max()
+    nr = np.linalg.norm(ref)
+    rel = np.linalg.norm(g - ref) / nr if nr > 0 else np.linalg.norm(g)
+    say("  %s rel %.3g max|d| %.3g max|ref| %.3g (max|d| / max|ref| %.3g)"
+        % (name, rel, d.max(), mref, d.max() / mref if mref > 0 else d.max()))
+    assert rel <= REL_L2, (name, rel)
+    if mref > 0:
+        assert d.max() <= REL_ELEM * mref, (name, np.unravel_index(d.argmax(), d.shape), d.max(), mref)
+    else:
+        assert d.max() == 0.0, name
+
+
 @pytest.mark.parametrize("B,H,N,d,rc,rn", [
     (1, 2, 1000, 128, 0.25, 0.25),
     (1, 1, 777, 64, 0.1, 0.2),      # ragged last block
@@ -54,15 +76,8 @@ def test_backward_matches_oracle(sla, B, H, N, d, rc, rn):
     w = torch.from_numpy(inp.w).cuda()
     dq, dk, dv, dw = sla.backward(dev(inp.q), dev(inp.k), dev(inp.v), w, dev(dout), rc, rn)
     torch.cuda.synchronize()
-    worst = 0.0
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)):
-        g = got.double().cpu().numpy()
-        nr = np.linalg.norm(ref)
-        rel = np.linalg.norm(g - ref) / nr if nr > 0 else np.linalg.norm(g)
-        say("  %s rel %.3g max|d| %.3g max|ref| %.3g" % (name, rel, np.abs(g - ref).max(), np.abs(ref).max()))
-        assert np.isfinite(g).all()
-        worst = max(worst, rel)
-    assert worst <= 1e-2
+        check(name, got.double().cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("gscale", [2.0 ** -40, 2.0 ** 20])
@@ -81,18 +96,16 @@ def test_backward_gradient_scale(sla, gscale):
     dq, dk, dv, dw = sla.backward(dev(inp.q), dev(inp.k), dev(inp.v), w, dev(dout), rc, rn)
     torch.cuda.synchronize()
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)):
-        g = got.double().cpu().numpy()
-        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
-        say("  %s rel %.3g" % (name, rel))
-        assert np.isfinite(g).all() and rel <= 1e-2
+        check(name, got.double().cpu().numpy(), ref)
 
 
-def test_backward_full_size_sampled_blocks(sla):
+@pytest.mark.timeout(900)
+def test_backward_full_size(sla):
     """The Wan2.1 480p workload (B=1, H=12, N=32760, d=128, 5 % / 10 %) in one
-    call, as the backward bench runs it; the oracle computes one head's
-    gradients on sampled blocks exactly (gradients_blocks): dq of the first,
-    an interior and the ragged last query block, dk and dv of three key
-    blocks.  Same bar per gradient over the sampled rows."""
+    call, as the backward bench runs it.  The oracle computes, exactly on
+    selected blocks (gradients_blocks): dq of the first, two interior and the
+    ragged last query block and dk, dv of four key blocks, on three heads; and
+    every head's dW, summed over the twelve heads as the GPU's dw is."""
     from sparse_attention_video_sla_amd.inputs import make_workload
     inp = make_workload(1)
     B, H, N, d = inp.q.shape
@@ -103,13 +116,35 @@ def test_backward_full_size_sampled_blocks(sla):
     w = torch.from_numpy(inp.w).cuda()
     dq, dk, dv, dw = sla.backward(dev(inp.q), dev(inp.k), dev(inp.v), w, dev(dout), rc, rn)
     torch.cuda.synchronize()
+    dq, dk, dv, dw = (x.double().cpu().numpy() for x in (dq, dk, dv, dw))
     mask = orc.classify(orc.pool(inp.q), orc.pool(inp.k), rc, rn)["mask"]
     Nb = -(-N // 64)
-    h, qb, kb = 5, [0, 137, Nb - 1], [0, 300, Nb - 1]
-    gq, gk, gv, _ = ob.gradients_blocks(inp.q[0, h], inp.k[0, h], inp.v[0, h], inp.w, mask[0, h], dout[0, h], qb, kb)
+    qb, kb = [0, 137, 301, Nb - 1], [0, 55, 300, Nb - 1]
     rows = lambda blocks: np.concatenate([np.arange(b * 64, min(N, (b + 1) * 64)) for b in blocks])
-    for name, got, ref, blocks in (("dq", dq, gq, qb), ("dk", dk, gk, kb), ("dv", dv, gv, kb)):
-        g = got[0, h].double().cpu().numpy()[rows(blocks)]
-        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
-        say("  %s rel %.3g max|d| %.3g max|ref| %.3g" % (name, rel, np.abs(g - ref).max(), np.abs(ref).max()))
-        assert np.isfinite(g).all() and rel <= 1e-2
+    dw_ref = np.zeros((d, d))
+    for h in range(H):
+        sampled = h in (0, 5, 11)
+        gq, gk, gv, gw = ob.gradients_blocks(inp.q[0, h], inp.k[0, h], inp.v[0, h], inp.w, mask[0, h], dout[0, h],
+                                             qb if sampled else [0], kb if sampled else [0])
+        dw_ref += gw
+        if sampled:
+            say(" head", h)
+            for name, got, ref, blocks in (("dq", dq, gq, qb), ("dk", dk, gk, kb), ("dv", dv, gv, kb)):
+                check(name, got[0, h][rows(blocks)], ref)
+    check("dw (12 heads)", dw, dw_ref)
+
+
+def test_backward_deterministic(sla):
+    """Two calls on the same inputs give the same bits in every gradient,
+    dW (a sum over workgroups) included."""
+    B, H, N, d, rc, rn = 2, 3, 3000, 128, 0.05, 0.10
+    inp = make_inputs(B, H, (1, 1, N), d, "bf16", seed=5)
+    rng = np.random.default_rng(6)
+    dout = dev(round_bf16(rng.standard_normal((B, H, N, d)).astype(np.float32)))
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w = torch.from_numpy(inp.w).cuda()
+    a = sla.backward(q, k, v, w, dout, rc, rn)
+    b = sla.backward(q, k, v, w, dout, rc, rn)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv", "dw"), a, b):
+        assert torch.equal(x, y), name

@@ -315,3 +315,18 @@ def test_sampled_rows_match_full():
     for r, (bh, i) in enumerate(rows):
         idx = list(map(tuple, full["rows"])).index((bh, i))
         assert np.array_equal(part["o"][r], full["o"][idx])
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 1000, 128), (2, 1, 777, 64), (1, 1, 64, 16)])
+def test_dense_rows_equal_c_oracle_at_full_critical(B, H, N, d):
+    """oracle/dense.py (matrix products over all keys) against the C oracle's
+    sparse branch with every block critical, on ragged shapes and sampled
+    blocks: the same dense softmax attention from two independent codes."""
+    from oracle import dense
+    q, k, v, w = rand_qkv(B, H, N, d, seed=N + d)
+    Nb = -(-N // 64)
+    rows = np.array([(bh, i) for bh in range(B * H) for i in range(Nb) if (i * 7 + bh) % 3 != 1 or i == Nb - 1],
+                    np.int32)
+    ref = orc.forward(q, k, v, w, 64, 1.0, 0.0, rows=rows)["o"]
+    got = dense.attention_rows(q, k, v, rows)
+    assert np.abs(got - ref).max() <= 1e-12

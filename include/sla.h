@@ -36,11 +36,8 @@
  *   - Inputs must be finite.  BF16 inputs: the linear branch stages values in
  *     fp16, so |V| and |V W^T| must stay below 65504.
  *   - Reentrant.  Mutable state: per thread, the error message and the
- *     optional stage-timing events; per device, one side stream (default
- *     priority) and two events, created on first use and kept until the
- *     process ends.  sla_forward runs its block-state kernel on that side
- *     stream, forked from and joined back to the caller's stream, so all of
- *     its work is still ordered on the caller's stream.  Results are
+ *     optional stage-timing events.  Every kernel of a call runs on the
+ *     caller's stream, in order.  Results are
  *     bitwise deterministic run to run: no kernel adds floating-point values
  *     with atomics (the only atomics are ORs into bit sets, whose result
  *     does not depend on their order), and every sum over workgroups (dW in

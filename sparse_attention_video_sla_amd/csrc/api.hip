@@ -1,10 +1,8 @@
 // api.hip -- the extern "C" entry points of libsla (declared in include/sla.h).
 //
 // Host-side only: argument checks, per-row counts, workspace carving and the
-// launch sequence.  pool -> classify run on the caller's stream while the
-// block-state kernel, which needs only K, V and W, runs on a side stream of
-// the device; the caller's stream then waits for it and runs assemble ->
-// fused.  No host synchronisation.
+// launch sequence pool -> classify -> block states -> assemble -> fused, all
+// on the caller's stream.  No host synchronisation.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -12,7 +10,6 @@
 
 #include <algorithm>
 #include <array>
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -69,7 +66,7 @@ sla_status check_shape(int B, int H, int N, int d, int block, int max_nb = MAX_N
 }
 
 struct Layout {
-    size_t qp, kp, mask, crit, marg, mbits, mcount, ulist, ucount, wst, hs, hhat, total;
+    size_t qp, kp, kpack, mask, crit, marg, mbits, mcount, ulist, ucount, wst, hs, hhat, total;
     int Nb, Nbc, Nbp, Lp, kc, kn;
 };
 
@@ -87,6 +84,7 @@ Layout make_layout(int B, int H, int N, int d, bool f32, int kc, int kn) {
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     L.qp = take(sizeof(float) * BH * L.Nb * d);
     L.kp = take(sizeof(float) * BH * L.Nb * d);
+    L.kpack = take(sizeof(float) * BH * sla::classify_packed_keys(L.Nb) * d);
     L.mask = take((size_t)BH * L.Nb * L.Nb);
     L.crit = take(sizeof(int32_t) * BH * L.Nb * (kc > 0 ? kc : 1));
     L.mcount = take(sizeof(int32_t) * BH * L.Nb);
@@ -146,38 +144,6 @@ void mark_unused_stages(StageEvents *ev, hipStream_t s) {
         mark_stage(ev, i, 0, s);
         mark_stage(ev, i, 1, s);
     }
-}
-
-// The side stream of a device (default priority, non-blocking) and the two
-// events that fork it from and join it to the caller's stream.  Created on
-// first use and kept until the process ends.  The fork is recorded and waited
-// under the lock, so that a caller's side work never waits on another
-// caller's stream; the join may be re-recorded by a later caller, which only
-// makes a wait cover more of the side stream.
-struct SideStream {
-    std::mutex mu;
-    bool ready = false;
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int MAX_DEVICES = 64;
-SideStream g_side[MAX_DEVICES];
-
-hipError_t side_stream(SideStream **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
-    SideStream &ss = g_side[dev];
-    std::lock_guard<std::mutex> lock(ss.mu);
-    if (!ss.ready) {
-        if ((e = hipStreamCreateWithFlags(&ss.side, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
-        ss.ready = true;
-    }
-    *out = &ss;
-    return hipSuccess;
 }
 
 }  // namespace
@@ -513,7 +479,7 @@ sla_status sla_pool(const void *q, const void *k, sla_dtype in_dtype, int B, int
     if (st != SLA_OK) return st;
     if (in_dtype != SLA_F32 && in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "input dtype %d not supported", (int)in_dtype);
     const int Nb = (N + 63) / 64;
-    return device_status(sla::launch_pool(in_dtype == SLA_BF16, d, q, k, q_pool, k_pool, (long)B * H, N, Nb, 64,
+    return device_status(sla::launch_pool(in_dtype == SLA_BF16, d, q, k, q_pool, k_pool, nullptr, (long)B * H, N, Nb, 64,
                                           (hipStream_t)stream),
                          "pool launch");
 }
@@ -573,41 +539,14 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     int32_t *mcount = (int32_t *)(ws + L.mcount);
 
     StageEvents *ev = timed ? timed_call() : nullptr;
-    // block states on the side stream, concurrent with pool and classify; a
-    // return after the fork still makes the caller's stream wait for the join
-    SideStream *ss = nullptr;
-    struct JoinOnExit {
-        hipStream_t s;
-        SideStream *ss = nullptr;
-        ~JoinOnExit() { if (ss) (void)hipStreamWaitEvent(s, ss->join, 0); }   // on an error return already being reported
-    } guard{s};
-    if (states) {
-        st = device_status(side_stream(&ss), "side stream");
-        if (st != SLA_OK) return st;
-        std::lock_guard<std::mutex> lock(ss->mu);
-        st = device_status(hipEventRecord(ss->fork, s), "fork");
-        if (st == SLA_OK) st = device_status(hipStreamWaitEvent(ss->side, ss->fork, 0), "fork");
-        if (st != SLA_OK) return st;
-        sla::StateArgs sa{};
-        sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp; sa.Nbc = L.Nbc;
-        sa.hs = ws + L.hs; sa.wstate = ws + L.wst; sa.bf16_in = !f32;
-        mark_stage(ev, 2, 0, ss->side);
-        st = device_status(sla::launch_state(sa, ss->side), "state launch");
-        mark_stage(ev, 2, 1, ss->side);
-        if (st == SLA_OK) st = device_status(hipEventRecord(ss->join, ss->side), "join");
-        if (st != SLA_OK) return st;
-        guard.ss = ss;
-    } else {
-        mark_stage(ev, 2, 0, s);
-        mark_stage(ev, 2, 1, s);
-    }
     mark_stage(ev, 0, 0, s);
-    st = device_status(sla::launch_pool(!f32, d, q, k, qp, kp, BH, N, Nb, 64, s), "pool launch");
+    float *kpack = (float *)(ws + L.kpack);
+    st = device_status(sla::launch_pool(!f32, d, q, k, qp, kp, kpack, BH, N, Nb, 64, s), "pool launch");
     if (st != SLA_OK) return st;
     mark_stage(ev, 0, 1, s);
 
     sla::ClassifyArgs ca{};
-    ca.qp = qp; ca.kp = kp; ca.BH = BH; ca.Nb = Nb; ca.D = d; ca.kc = kc; ca.kn = kn;
+    ca.qp = qp; ca.kp = kp; ca.kpack = kpack; ca.BH = BH; ca.Nb = Nb; ca.D = d; ca.kc = kc; ca.kn = kn;
     ca.mask = mask; ca.crit = crit; ca.excl = nullptr; ca.pc = nullptr;
     ca.marg = states && f32 ? (float *)(ws + L.marg) : nullptr;
     ca.mbits = states && !f32 ? (uint32_t *)(ws + L.mbits) : nullptr;
@@ -621,10 +560,21 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     if (st != SLA_OK) return st;
     mark_stage(ev, 1, 1, s);
 
+    // block states (they need only K, V and W).  They run after pool and
+    // classify rather than beside them: the state kernel's persistent
+    // workgroups fill every compute unit's registers, so nothing would run
+    // next to them anyway.
     if (states) {
-        guard.ss = nullptr;
-        st = device_status(hipStreamWaitEvent(s, ss->join, 0), "join");
+        sla::StateArgs sa{};
+        sa.k = k; sa.v = v; sa.w = w_proj; sa.BH = BH; sa.N = N; sa.Nb = Nb; sa.D = d; sa.Lp = L.Lp; sa.Nbc = L.Nbc;
+        sa.hs = ws + L.hs; sa.wstate = ws + L.wst; sa.bf16_in = !f32;
+        mark_stage(ev, 2, 0, s);
+        st = device_status(sla::launch_state(sa, s), "state launch");
+        mark_stage(ev, 2, 1, s);
         if (st != SLA_OK) return st;
+    } else {
+        mark_stage(ev, 2, 0, s);
+        mark_stage(ev, 2, 1, s);
     }
     mark_stage(ev, 3, 0, s);
     if (states) {

@@ -15,7 +15,8 @@ namespace sla {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                    float *__restrict__ qp, float *__restrict__ kp,
-                                                   long BH, int N, int Nb, int blk) {
+                                                   float *__restrict__ kpack, int Nb2, long BH, int N, int Nb,
+                                                   int blk) {
     constexpr int CG = 16 / sizeof(T);   // channels per thread
     constexpr int TPB = D / CG;          // threads per (tensor, head, block)
     constexpr int BATCH = 16;            // rows loaded before they are summed
@@ -53,26 +54,34 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
     float *o = (which ? kp : qp) + (bh * Nb + i) * D + cg * CG;
 #pragma unroll
     for (int e = 0; e < CG; e += 4) st_chunk(o + e, *reinterpret_cast<const Chunk *>(&res[e]));
+    if (which && kpack) {   // channels 4 c4 .. +3 of key block i at [bh][c4][i][0..3]
+#pragma unroll
+        for (int e = 0; e < CG; e += 4) {
+            const long c4 = (cg * CG + e) / 4;
+            st_chunk(kpack + ((bh * (D / 4) + c4) * Nb2 + i) * 4, *reinterpret_cast<const Chunk *>(&res[e]));
+        }
+    }
 }
 
 template <typename T, int D>
-hipError_t launch_pool_t(const void *q, const void *k, float *qp, float *kp, long BH, int N, int Nb,
-                         int blk, hipStream_t st) {
+hipError_t launch_pool_t(const void *q, const void *k, float *qp, float *kp, float *kpack, long BH, int N,
+                         int Nb, int blk, hipStream_t st) {
     constexpr int TPB = D / (16 / sizeof(T));
     const long threads = 2 * BH * (long)Nb * TPB;
     const unsigned grid = (unsigned)((threads + 255) / 256);
-    pool_kernel<T, D><<<grid, 256, 0, st>>>((const T *)q, (const T *)k, qp, kp, BH, N, Nb, blk);
+    pool_kernel<T, D><<<grid, 256, 0, st>>>((const T *)q, (const T *)k, qp, kp, kpack, classify_packed_keys(Nb), BH,
+                                            N, Nb, blk);
     return hipGetLastError();
 }
 
-hipError_t launch_pool(bool bf16_in, int D, const void *q, const void *k, float *qp, float *kp,
+hipError_t launch_pool(bool bf16_in, int D, const void *q, const void *k, float *qp, float *kp, float *kpack,
                        long BH, int N, int Nb, int blk, hipStream_t st) {
     if (bf16_in) {
-        return D == 64 ? launch_pool_t<bf16, 64>(q, k, qp, kp, BH, N, Nb, blk, st)
-                       : launch_pool_t<bf16, 128>(q, k, qp, kp, BH, N, Nb, blk, st);
+        return D == 64 ? launch_pool_t<bf16, 64>(q, k, qp, kp, kpack, BH, N, Nb, blk, st)
+                       : launch_pool_t<bf16, 128>(q, k, qp, kp, kpack, BH, N, Nb, blk, st);
     }
-    return D == 64 ? launch_pool_t<float, 64>(q, k, qp, kp, BH, N, Nb, blk, st)
-                   : launch_pool_t<float, 128>(q, k, qp, kp, BH, N, Nb, blk, st);
+    return D == 64 ? launch_pool_t<float, 64>(q, k, qp, kp, kpack, BH, N, Nb, blk, st)
+                   : launch_pool_t<float, 128>(q, k, qp, kp, kpack, BH, N, Nb, blk, st);
 }
 
 }  // namespace sla

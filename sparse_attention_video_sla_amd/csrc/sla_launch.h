@@ -7,6 +7,7 @@ namespace sla {
 
 struct ClassifyArgs {
     const float *qp, *kp;
+    const float *kpack; // nullable: the key means packed by channel quads, [BH][D/4][classify_packed_keys(Nb)][4]
     long BH;
     int Nb, D, kc, kn;
     int8_t *mask;
@@ -72,8 +73,11 @@ struct MassArgs {
     float *mass;             // [BH][Nb][Nb]
 };
 
-hipError_t launch_pool(bool bf16_in, int D, const void *q, const void *k, float *qp, float *kp,
+// kpack (nullable): the key means also packed as classify reads them in the
+// forward pass
+hipError_t launch_pool(bool bf16_in, int D, const void *q, const void *k, float *qp, float *kp, float *kpack,
                        long BH, int N, int Nb, int blk, hipStream_t st);
+int classify_packed_keys(int Nb);   // key blocks of the packed key means (Nb rounded up to even)
 int classify_rows_per_group(int Nb, int D);
 size_t classify_lds_bytes(int R, int D, int Nb);
 hipError_t launch_classify(const ClassifyArgs &a, hipStream_t st);

@@ -246,11 +246,11 @@ def test_ragged_tail_reads_nothing_past_the_tensors(sla, dtype):
 
 
 def test_stream_ordering(sla):
-    """The block-state kernel runs on a side stream forked from the caller's
-    stream.  It must see K and V written on the caller's stream just before
-    the call (behind other queued work), and a second call that reuses the
-    workspace must not overwrite the first call's states before they are
-    used.  Nothing is synchronised between the steps below."""
+    """Every kernel of a call runs on the caller's stream: a call must see K
+    and V written on that stream just before it (behind other queued work),
+    and a second call that reuses the workspace must not overwrite the first
+    call's states before they are used.  Nothing is synchronised between the
+    steps below."""
     say("stream ordering")
     N, d, rc, rn = 3000, 128, 0.05, 0.10
     a = make_inputs(1, 2, (1, 1, N), d, "bf16", seed=31)
@@ -279,8 +279,8 @@ def test_stream_ordering(sla):
 
 
 def test_stage_timing(sla):
-    """Stage timing records every stage of each call; the state stage runs
-    concurrently with pool and classify."""
+    """Stage timing records every stage of each call (pool, classify, block
+    states, marginal-state GEMM, fused kernel)."""
     import ctypes
     say("stage timing")
     inp = make_inputs(1, 2, (1, 1, 3000), 128, "bf16", seed=5)

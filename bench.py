@@ -2,20 +2,30 @@
 """Benchmark of the SLA sparse-linear attention forward on one MI355X.
 
 A step is one sla_forward call (pool -> classify -> linear states ->
-marginal-state GEMM -> fused sparse+linear kernel) over the Wan2.1-1.3B 480p
-shaped workload: B=1, H=12, N=32760 (21x30x52 latent grid), d=128, bf16,
-5% critical / 10% negligible, synthetic seeded inputs resident in HBM.
+marginal-state GEMM -> fused sparse+linear kernel) over one of the named
+synthetic workloads, inputs resident in HBM.  The default is the Wan2.1-1.3B
+480p shape: B=1, H=12, N=32760 (21x30x52 latent grid), d=128, bf16, 5%
+critical / 10% negligible.  --workload picks another (0 tiny fp32, 2 the
+same grid with RoPE and a batch of two, 3 720p, 4 HunyuanVideo), --crit /
+--negl override the shares, --all prints one line for every workload and
+setting: 0, 1, 2 at 2.5/5/10 % critical, 3, 4 and 4 at 100 % critical (dense
+attention in the same kernels).
 
-Printed: one JSON line.  `value` is effective TFLOP/s over the whole call,
-counting the method's work F = 4*64*64*d per critical block pair +
-4*64*d*d per query block with marginal blocks.  `roofline` is for the fused
-kernel, timed live with HIP events recorded on its stream; its algorithmic
-flops are the critical pairs plus 2*64*d*d per query block (phi(Q) times the
-marginal state; the projection is folded into the state kernel).
-`roofline.traffic` is the kernel's HBM bytes per launch from the committed
-rocprofv3 counter summary, reported only while the kernel source and the
-package headers it includes match the ones the counters were taken with.
-`cpu_baseline` times the CPU oracle on whole heads (by default all of them).
+Printed: one JSON line per setting.  `value` is effective TFLOP/s over the
+whole call, counting the method's work F = 4*64*64*d per critical block pair
++ 4*64*d*d per query block with marginal blocks, and `ms_per_step` the mean
+of the K timed steps.  `timing` gives the median, p10 and p90 of 100 calls
+timed one by one with HIP events on the call's stream, with the 256 MB
+last-level cache (MALL) warm and flushed before each call (a 512 MB fill),
+and the GPU clock sampled through amdsmi while calls run back to back.  `roofline`
+is for the fused kernel, timed with HIP events recorded on its stream; its
+algorithmic flops are the critical pairs plus 2*64*d*d per query block
+(phi(Q) times the marginal state; the projection is folded into the state
+kernel).  `roofline.traffic` is the kernel's HBM bytes per launch from a
+committed rocprofv3 counter summary for the same workload, reported only
+while the kernel source and the package headers it includes match the ones
+the counters were taken with.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same inputs.
 
 With --lvsa it prints instead one JSON line for LVSA frame-level sparse
 attention (the LVSA page's sets A(t) = G_s U W(t)) on a long-video workload:
@@ -61,13 +71,10 @@ if ROOT not in sys.path:
 
 METRIC = "effective TFLOP/s + ms/call of sparse-linear attn fwd at N=32760, %MFMA peak"
 CSRC = os.path.join(ROOT, "sparse_attention_video_sla_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_forward_wan480p_stats.md")
-LVSA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16s_lvsa_wan6x_stats.md")
-STA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused16s_sta_hunyuan_stats.md")
-BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sla_backward_wan480p_stats.md")
 # backward stages that are one kernel each (the others span several)
 BWD_STAGE_KERNEL = {"dq": "bwd_dq_kernel", "dkv": "bwd_dkv_kernel", "linear_keys": "bwd_lin_key_kernel"}
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -80,21 +87,24 @@ def work(B, H, N, d, kc, kn):
     return f_comp, f_fused, pairs, marg_rows
 
 
-def fused_traffic(path=TRAFFIC_FILE, kernel="fused16s_kernel", source="fused16s.hip"):
-    """HBM bytes per launch of a fused kernel from a committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
-    calibration), or None when the kernel source has changed since the
-    counters were taken."""
+def profile_traffic(kernel, workload, source):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 summaries (a line `traffic: kernel=K workload=W
+    bytes_per_launch=B source=F sha256=H`: FETCH_SIZE + WRITE_SIZE scaled by
+    the copy-kernel calibration), or None when no summary covers them or the
+    kernel source has changed since the counters were taken."""
+    import glob
     import re
     try:
-        text = open(path).read()
         sha = source_sha(source)
     except OSError:
         return None
-    m = re.search(kernel + r" HBM bytes per launch: (\d+) \(source sha256 ([0-9a-f]{16})\)", text)
-    if not m or sha != m.group(2):
-        return None
-    return int(m.group(1))
+    pat = re.compile(r"traffic: kernel=(\S+) workload=(\S+) bytes_per_launch=(\d+) source=(\S+) sha256=([0-9a-f]{16})")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for m in pat.finditer(open(path).read()):
+            if m.group(1) == kernel and m.group(2) == workload and m.group(4) == source and m.group(5) == sha:
+                return int(m.group(3))
+    return None
 
 
 def source_sha(source):
@@ -117,19 +127,38 @@ def source_sha(source):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(inp, wl, rc, rn, heads):
+def block_flops(d, kc, linear):
+    """The method's F for one query block of one head (as work() counts it)."""
+    return 4 * 64 * 64 * d * kc + (4 * 64 * d * d if linear else 0)
+
+
+def cpu_baseline(inp, wl, rc, rn, per_head=None, seed=5):
+    """The C oracle (as it stands) on the same inputs: every query block of
+    every head (per_head None), or a seeded sample of per_head query blocks
+    per head; F counted for the blocks evaluated."""
     import numpy as np
     from oracle import oracle as orc
-    q, k, v = inp.q[:, :heads], inp.k[:, :heads], inp.v[:, :heads]
+    from sparse_attention_video_sla_amd.inputs import sample_query_blocks
+    B, H, N, d = inp.q.shape
+    Nb = -(-N // 64)
     t0 = time.perf_counter()
-    res = orc.forward(q, k, v, inp.w, 64, rc, rn)
+    qp, kp = orc.pool(inp.q), orc.pool(inp.k)
+    cls = orc.classify(qp, kp, rc, rn)
+    rows = None if per_head is None else sample_query_blocks(B, H, Nb, per_head, seed)
+    res = orc.forward(inp.q, inp.k, inp.v, inp.w, 64, rc, rn, rows=rows, cls=cls)
     t = time.perf_counter() - t0
-    f_comp, _, _, _ = work(1, heads, wl.N, wl.d, res["k_c"], res["k_n"])
-    return {"value": round(f_comp / t / 1e12, 6), "unit": "TFLOP/s", "cores": orc.threads(),
-            "kind": "oracle", "seconds": round(t, 3),
-            "sample": "heads 0-%d of %d (every query block): pool, classify, sparse and linear "
-                      "branches in fp64; F counted as for the GPU line" % (heads - 1, wl.H),
-            "ms_per_call_extrapolated": round(t * 1e3 * wl.H / heads, 1)}
+    n_rows = len(res["rows"])
+    kc, kn = res["k_c"], res["k_n"]
+    f = n_rows * block_flops(d, kc, kc + kn < Nb)
+    total_rows = B * H * Nb
+    if per_head is None:
+        sample = "every query block of all %d heads: pool, classify, sparse and linear branches in fp64" % (B * H)
+    else:
+        sample = ("%d query blocks (%d per head, seeded) of %d, after pool and classify of every row; "
+                  "sparse and linear branches in fp64" % (n_rows, per_head, total_rows))
+    return {"value": round(f / t / 1e12, 6), "unit": "TFLOP/s", "cores": orc.threads(), "kind": "oracle",
+            "seconds": round(t, 3), "sample": sample,
+            "ms_per_call_extrapolated": round(t * 1e3 * total_rows / n_rows, 1)}
 
 
 def run_quality(args, wl):
@@ -264,7 +293,7 @@ def run_lvsa(args):
                    "density_vs_dense": round(flops / dense, 5), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": fused_traffic(LVSA_TRAFFIC_FILE),
+                     "traffic": profile_traffic("fused16s_kernel", wl.name, "fused16s.hip"),
                      "kernel": "fused16s_kernel<bf16,f16,128,float,slots,frame marks>", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
@@ -367,7 +396,7 @@ def run_sta(args):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": fused_traffic(STA_TRAFFIC_FILE),
+                     "traffic": profile_traffic("fused16s_kernel", wl["name"], "fused16s.hip"),
                      "kernel": "fused16s_kernel<bf16,f16,128,float,slots> (tile schedule)", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
@@ -470,7 +499,7 @@ def run_backward(args, wl):
                    "negl_frac": rn, "k_c": kc, "k_n": kn, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": (fused_traffic(BWD_TRAFFIC_FILE, BWD_STAGE_KERNEL[dom], "backward.hip")
+                     "traffic": (profile_traffic(BWD_STAGE_KERNEL[dom], wl.name, "backward.hip")
                                  if dom in BWD_STAGE_KERNEL else None),
                      "kernel": "backward stage " + dom,
                      "flops_per_launch": fl, "avg_launch_ms": round(st_ms[dom], 4)},
@@ -500,48 +529,91 @@ def run_backward(args, wl):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, help="named workload id (1 = Wan2.1 480p)")
-    ap.add_argument("--crit", type=float, default=None)
-    ap.add_argument("--negl", type=float, default=None)
-    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--quality", action="store_true", help="mask-quality diagnostics line instead of the forward line")
-    ap.add_argument("--lvsa", action="store_true", help="LVSA frame-level sparse attention line (long-video workload)")
-    ap.add_argument("--sta", action="store_true", help="sliding tile attention line (HunyuanVideo-sized latent)")
-    ap.add_argument("--backward", action="store_true", help="SLA backward line (same workload as the forward)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
-              "pipeline (heads would shard across GPUs with no exchange); use --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
+# fused kernel per input dtype: name, source, peak of its matrix-core type
+FUSED_KERNEL = {"bf16": ("fused16s_kernel", "fused16s.hip", PEAK_BF16_TFLOPS, "bf16"),
+                "f32": ("fused_kernel", "fused.hip", PEAK_FP32_TFLOPS, "fp32")}
 
+
+def clock_sampler():
+    """A background sampler of the GPU's current graphics clock (MHz)
+    through amdsmi, or None where amdsmi is missing."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def run():
+        while not stop.is_set():
+            try:
+                info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+                samples.append(float(info["clk"]))
+            except Exception:
+                pass
+            stop.wait(0.02)
+    th = threading.Thread(target=run, daemon=True)
+    th.start()
+
+    def finish():
+        stop.set()
+        th.join()
+        return samples
+    return finish
+
+
+def busy_clock(step, seconds=0.8):
+    """The graphics clock (MHz) sampled while the GPU runs `step` back to
+    back for about `seconds`; the first fifth of the samples (the clock
+    ramping up) is dropped."""
+    import torch
+    finish = clock_sampler()
+    if finish is None:
+        return []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    samples = finish()
+    return samples[len(samples) // 5:]
+
+
+def per_call_ms(step, n, flush=None):
+    """n calls timed one by one with HIP events on torch's current stream
+    (the stream the library enqueues on); with `flush` a fill kernel runs
+    before each call, outside its events."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        if flush is not None:
+            flush.zero_()
+        a.record(st)
+        step()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def spread(ms):
+    import numpy as np
+    x = np.asarray(ms)
+    return {"median": round(float(np.median(x)), 4), "p10": round(float(np.percentile(x, 10)), 4),
+            "p90": round(float(np.percentile(x, 90)), 4)}
+
+
+def run_forward(args, cid, rc, rn, flush, cpu=True):
+    """One JSON line for workload cid at shares (rc, rn)."""
     import torch
     import sparse_attention_video_sla_amd as sla
     from sparse_attention_video_sla_amd import _lib
     from sparse_attention_video_sla_amd.inputs import WORKLOADS, make_workload
 
-    if args.lvsa:
-        run_lvsa(args)
-        return
-    if args.sta:
-        run_sta(args)
-        return
-    wl = WORKLOADS[args.workload]
-    if args.backward:
-        run_backward(args, wl)
-        return
-    if args.quality:
-        run_quality(args, wl)
-        return
-    rc = args.crit if args.crit is not None else wl.fracs[0][0]
-    rn = args.negl if args.negl is not None else wl.fracs[0][1]
-    inp = make_workload(args.workload)
+    wl = WORKLOADS[cid]
+    inp = make_workload(cid)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     q, k, v = (torch.from_numpy(x).to(dev).to(tdt) for x in (inp.q, inp.k, inp.v))
@@ -563,8 +635,12 @@ def main():
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    warm = per_call_ms(step, args.calls)
+    flushed = per_call_ms(step, args.calls, flush)
+    clocks = busy_clock(step)
     # per-stage times (HIP events around each kernel, on the stream it runs
-    # on) in a second pass, so that the event records stay out of the timed steps
+    # on) in a separate pass, so that the event records stay out of the
+    # timed steps
     L = _lib.load()
     L.sla_set_stage_timing(1)
     ms_buf = (ctypes.c_float * 5)()
@@ -579,22 +655,26 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     f_comp, f_fused, pairs, marg_rows = work(B, H, N, d, kc, kn)
     value = f_comp / (ms * 1e-3) / 1e12
+    kname, ksrc, peak, mfma_type = FUSED_KERNEL[wl.dtype]
     t_fused = stage_ms["fused"] * 1e-3
     achieved = f_fused / t_fused / 1e12 if t_fused > 0 else 0.0
     Lp = -(-(d * d + d) // 256) * 256
     Nbc = -(-Nb // 64) * 64
+    es = 2 if wl.dtype == "bf16" else 4
     nbytes = {   # algorithmic bytes per launch
-        "pool": 2 * B * H * N * d * 2 + 2 * B * H * Nb * d * 4,
-        "state": 2 * B * H * N * d * 2 + B * H * Nbc * Lp * 2,
-        "assemble": B * H * Nb * Nbc // 8 + B * H * Nbc * Lp * 2 + B * H * Nb * Lp * 2,
+        "pool": 2 * B * H * N * d * es + 2 * B * H * Nb * d * 4,
+        "state": 2 * B * H * N * d * es + B * H * Nbc * Lp * es,
+        "assemble": B * H * Nb * Nbc // 8 + B * H * Nbc * Lp * es + B * H * Nb * Lp * es,
     }
     stages = {}
     for name in _lib.STAGES:
-        s = {"ms": round(stage_ms[name], 4)}
+        st_ = {"ms": round(stage_ms[name], 4)}
         if name in nbytes and stage_ms[name] > 0:
-            s["GB/s"] = round(nbytes[name] / (stage_ms[name] * 1e-3) / 1e9, 1)
-        stages[name] = s
-    stages["assemble"]["TFLOP/s"] = round(2 * B * H * Nb * Nbc * Lp / max(stage_ms["assemble"], 1e-9) / 1e9, 1)
+            st_["GB/s"] = round(nbytes[name] / (stage_ms[name] * 1e-3) / 1e9, 1)
+        stages[name] = st_
+    if marg_rows:
+        stages["assemble"]["TFLOP/s"] = round(2 * B * H * Nb * Nbc * Lp / max(stage_ms["assemble"], 1e-9) / 1e9, 1)
+    clk = {"median_mhz": round(float(sorted(clocks)[len(clocks) // 2]), 1), "samples": len(clocks)} if clocks else None
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -610,15 +690,88 @@ def main():
         "data": "synthetic (seeded; local sinusoid Q/K + noise, V ~ N(0,1))",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "d": d, "block": 64,
                    "crit_frac": rc, "negl_frac": rn, "k_c": kc, "k_n": kn, "parallelism": "none (1 GPU)"},
-        "mfma_frac_fused": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": fused_traffic(),
-                     "kernel": "fused16s_kernel<bf16,f16,128,float>",
+        "mfma_frac_fused": round(achieved / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": profile_traffic(kname, "%s:%g/%g" % (wl.name, rc, rn), ksrc),
+                     "kernel": kname, "mfma_type": mfma_type,
                      "flops_per_launch": f_fused, "avg_launch_ms": round(stage_ms["fused"], 4)},
+        "timing": {"calls": args.calls, "warm_ms": spread(warm), "mall_flushed_ms": spread(flushed),
+                   "flush": "512 MB fill before each call (MALL 256 MB)", "clock": clk},
+        "dense_equivalent_tflops": round(4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 3),
         "stages": stages,
     }
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(inp, wl, rc, rn, args.cpu_heads or wl.H)
+    if clk:
+        # the nominal peak is quoted at 2.4 GHz; the same peak at the sampled clock
+        line["roofline"]["frac_at_measured_clock"] = round(achieved / (peak * clk["median_mhz"] / 2400.0), 4)
+    if cpu and not args.no_cpu:
+        # bounded samples: whole heads for the small workloads, 64 query
+        # blocks per head at 720p and HunyuanVideo, one per head when dense
+        per_head = None if cid in (0, 1) else (1 if kc == Nb else 64)
+        line["cpu_baseline"] = cpu_baseline(inp, wl, rc, rn, per_head)
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return line, ms
+
+
+ALL_SETTINGS = [(0, 0.05, 0.10), (1, 0.05, 0.10), (2, 0.025, 0.10), (2, 0.05, 0.10), (2, 0.10, 0.10),
+                (3, 0.05, 0.10), (4, 0.05, 0.10), (4, 1.0, 0.0)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--calls", type=int, default=100, help="calls timed one by one for the median / p10 / p90")
+    ap.add_argument("--workload", type=int, default=1, help="named workload id (1 = Wan2.1 480p)")
+    ap.add_argument("--crit", type=float, default=None)
+    ap.add_argument("--negl", type=float, default=None)
+    ap.add_argument("--all", action="store_true", help="one line per workload and setting (0-4, 4 dense)")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quality", action="store_true", help="mask-quality diagnostics line instead of the forward line")
+    ap.add_argument("--lvsa", action="store_true", help="LVSA frame-level sparse attention line (long-video workload)")
+    ap.add_argument("--sta", action="store_true", help="sliding tile attention line (HunyuanVideo-sized latent)")
+    ap.add_argument("--backward", action="store_true", help="SLA backward line (same workload as the forward)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
+              "pipeline (heads would shard across GPUs with no exchange); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_video_sla_amd.inputs import WORKLOADS
+
+    if args.lvsa:
+        run_lvsa(args)
+        return
+    if args.sta:
+        run_sta(args)
+        return
+    wl = WORKLOADS[args.workload]
+    if args.backward:
+        run_backward(args, wl)
+        return
+    if args.quality:
+        run_quality(args, wl)
+        return
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    if args.all:
+        sparse_ms = None
+        for cid, rc, rn in ALL_SETTINGS:
+            line, ms = run_forward(args, cid, rc, rn, flush)
+            if cid == 4 and rc < 1.0:
+                sparse_ms = ms
+            if cid == 4 and rc == 1.0 and sparse_ms:
+                # the analogue of the SLA article's kernel-against-dense comparison (context only)
+                line["dense_over_sparse_time"] = round(ms / sparse_ms, 2)
+            print(json.dumps(line), flush=True)
+        return
+    rc = args.crit if args.crit is not None else wl.fracs[0][0]
+    rn = args.negl if args.negl is not None else wl.fracs[0][1]
+    line, _ = run_forward(args, args.workload, rc, rn, flush)
     print(json.dumps(line), flush=True)
 
 

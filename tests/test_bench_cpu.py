@@ -20,13 +20,20 @@ def test_source_sha_covers_included_headers(tmp_path, monkeypatch):
     assert bench.source_sha("k.hip") != first
 
 
-def test_fused_traffic_needs_matching_sha(tmp_path, monkeypatch):
-    (tmp_path / "k.hip").write_bytes(b"// kernel\n")
-    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+def test_profile_traffic_keyed_on_kernel_workload_and_sha(tmp_path, monkeypatch):
+    (tmp_path / "csrc").mkdir()
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "csrc" / "k.hip").write_bytes(b"// kernel\n")
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path / "csrc"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     sha = bench.source_sha("k.hip")
-    prof = tmp_path / "p.md"
-    prof.write_text("k_kernel HBM bytes per launch: 1234 (source sha256 %s)\n" % sha)
-    assert bench.fused_traffic(str(prof), "k_kernel", "k.hip") == 1234
-    prof.write_text("k_kernel HBM bytes per launch: 1234 (source sha256 %s)\n" % ("0" * 16))
-    assert bench.fused_traffic(str(prof), "k_kernel", "k.hip") is None
-    assert bench.fused_traffic(str(tmp_path / "missing.md"), "k_kernel", "k.hip") is None
+    prof = tmp_path / "profiles" / "k_w1_stats.md"
+    line = "traffic: kernel=k_kernel workload=%s bytes_per_launch=%d source=k.hip sha256=%s\n"
+    prof.write_text(line % ("w1", 1234, sha) + line % ("w2", 99, sha))
+    assert bench.profile_traffic("k_kernel", "w1", "k.hip") == 1234
+    assert bench.profile_traffic("k_kernel", "w2", "k.hip") == 99
+    assert bench.profile_traffic("k_kernel", "w3", "k.hip") is None          # no summary for that workload
+    assert bench.profile_traffic("other_kernel", "w1", "k.hip") is None
+    prof.write_text(line % ("w1", 1234, "0" * 16))
+    assert bench.profile_traffic("k_kernel", "w1", "k.hip") is None          # counters of another source
+    assert bench.profile_traffic("k_kernel", "w1", "missing.hip") is None

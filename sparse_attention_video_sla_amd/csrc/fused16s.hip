@@ -4,7 +4,7 @@
 // marginal states, with the learnable projection folded into them).
 //
 // One workgroup of 4 waves per query block i of one head, three workgroups
-// per compute unit (48 KB of LDS and at most 168 registers per lane each, so
+// per compute unit (50 KB of LDS and at most 168 registers per lane each, so
 // every SIMD runs three independent waves).  Wave (qh, kh): query rows
 // 32qh .. +31 against keys 32kh .. +31 of every critical block of row i, with
 // its own online softmax (running max m, output O, row sum l); the two key
@@ -22,12 +22,14 @@
 // two-slot ring, V through one slot, with two barriers per block (after the
 // scores: V(c) and K(c+1) visible, K(c)'s slot free for K(c+2); after the
 // accumulation: V's slot free for V(c+1)), so each load has a phase or two
-// to land.  Both tiles are stored by rows with their 16-byte chunks
-// swizzled by row, K by kswz (its row reads touch every bank once) and V by
-// vswz (its transposing reads, 8 rows x 4 chunks per instruction, touch
-// every bank twice, the minimum); the loads into LDS read whole rows.  (A V
-// layout of 4-row groups stored chunk-major, also free of conflicts, was
-// 12 % slower here: each of its loads gathers 16-byte pieces of four rows.)
+// to land.  K rows are padded by one 16-byte chunk (its row reads touch
+// every bank once, and one register holds a lane's read offset for every
+// channel step: the steps differ by constants); V rows have their 16-byte
+// chunks swizzled by vswz (its transposing reads, 8 rows x 4 chunks per
+// instruction, touch every bank twice, the minimum); the loads into LDS read
+// whole rows, through a buffer resource per key block.  (A V layout of
+// 4-row groups stored chunk-major, also free of conflicts, was 12 % slower
+// here: each of its loads gathers 16-byte pieces of four rows.)
 // Every
 // workgroup reads its own tiles; with three workgroups per compute unit the
 // softmax of one overlaps the matrix work of another without any schedule
@@ -71,12 +73,19 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
                                                           int per_xcd, int N, int Nb, float sl2) {
     static_assert(__is_same(T, bf16), "bf16 inputs");
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
+    // K tiles: rows padded by one 16-byte chunk (KRS elements), so that the
+    // 16 lanes of a row read touch all banks and the read offsets of the 8
+    // (4) channel steps differ by constants
+    constexpr int KRS = D + 8, KCPR = D / 8 + 1, KTILE = 64 * KRS;
+    constexpr int KDMA = 64 * KCPR / 64;                 // 1 KB loads into LDS per K tile (17, or 9 for d = 64)
+    constexpr int KPW = (KDMA + 3) / 4;                  // per wave, at most
     constexpr float NEG_INF = -__builtin_inff();
     // Lazy rescale threshold: P may reach 2^TAU; P is bf16 (the float exponent
     // range) and O and l accumulate in fp32 over at most 64 * Nb < 2^18 keys,
     // so every value stays below 2^90.
     constexpr float TAU = 64.f;
-    __shared__ __attribute__((aligned(1024))) T Kk[2][TILE];
+    static_assert(KTILE * 2 >= D * KRS, "the marginal state fits the K ring");
+    __shared__ __attribute__((aligned(1024))) T Kk[2][KTILE];
     __shared__ __attribute__((aligned(1024))) T Vk[TILE];
     __shared__ __attribute__((aligned(16))) S Zl[D];        // the row's Ẑ_i
 
@@ -125,15 +134,14 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // a padding half: this row has no block in the slot (no load, no work)
     auto pad = [&](int c) __attribute__((always_inline)) { return SLOTS && marks_of(c) == 0xFu; };
     const int qpart = (MARKS && fp > 0 && 32 * qh + l32 >= frame_split(i, fp)) ? 1 : 0;
-    const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * N * (long)D, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * N * (long)D, head_bytes);
-    int koff[NS];                                        // K operand reads: key row 32kh + l32
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int r = 32 * kh + l32;
-        koff[s] = r * D + ((2 * s + hh) ^ kswz<D>(r)) * 8;
-    }
+    // A buffer resource per key block: a ragged last block, and the pad
+    // chunks of the K tile (offsets past the resource), read zeros.
+    auto blk_rsrc = [&](const T *base, int j) __attribute__((always_inline)) {
+        const int rows = min(64, N - 64 * j);
+        return make_rsrc(base + (bh * N + 64L * j) * D, (uint32_t)(rows * D * sizeof(T)));
+    };
+    // K operand reads: key row 32kh + l32, channels 16 s + 8 hh .. +7 at +16 s
+    const int kbase = (32 * kh + l32) * KRS + 8 * hh;
     // V transposing reads (V-swizzled rows): the second run of a step lies
     // 8 rows below the first at the same swizzle, 8D elements further on
     int toff[NCT][2];
@@ -141,27 +149,32 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     int tv[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) tv[ct] = toff[ct][0];
-    uint32_t ok_[NBW];
+    // loads of a K tile into LDS: wave w takes the 1 KB pieces w, w + 4, ...;
+    // lane l of piece t fills chunk 64 t + l of the padded tile, which is row
+    // (64 t + l) / KCPR, chunk (64 t + l) % KCPR of the block (the last chunk
+    // of a row is the pad: an offset past the tile, which reads zero)
+    uint32_t kdo[KPW];
 #pragma unroll
-    for (int u = 0; u < NBW; ++u) ok_[u] = off_klayout<D>((wave * NBW + u) * 1024 + 16 * lane);
+    for (int u = 0; u < KPW; ++u) {
+        const int pos = 64 * (wave + 4 * u) + lane, row = pos / KCPR, ch = pos % KCPR;
+        kdo[u] = ch < D / 8 ? (uint32_t)(row * D * 2 + ch * 16) : 0x40000000u;
+    }
     // V: the swizzle only depends on the row modulo 4 (d = 128) or 8 (d = 64),
     // which a 1 KB piece (4 or 8 rows) does not change: piece u is piece 0
     // plus u KB
     const uint32_t ov0 = off_klayout<D, true>(wave * NBW * 1024 + 16 * lane);
-    // this wave's NBW 1 KB pieces of the K or V tile of block c of the list;
-    // the tile offset goes into the per-lane offset, which the buffer's bounds
-    // check covers (a ragged last tile reads zeros)
     auto load_k = [&](int c, int slot) __attribute__((always_inline)) {
         if (pad(c)) return;
-        const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
+        const __amdgpu_buffer_rsrc_t r = blk_rsrc(k, blk_of(c));
 #pragma unroll
-        for (int u = 0; u < NBW; ++u) dma16(rk, &Kk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
+        for (int u = 0; u < KPW; ++u)
+            if (wave + 4 * u < KDMA) dma16(r, &Kk[slot][(wave + 4 * u) * 512], kdo[u], 0);
     };
     auto load_v = [&](int c) __attribute__((always_inline)) {
         if (pad(c)) return;
-        const uint32_t off = (uint32_t)(64L * blk_of(c) * D * sizeof(T));
+        const __amdgpu_buffer_rsrc_t r = blk_rsrc(v, blk_of(c));
 #pragma unroll
-        for (int u = 0; u < NBW; ++u) dma16(rv, &Vk[(wave * NBW + u) * 512], ov0 + off + 1024 * u, 0);
+        for (int u = 0; u < NBW; ++u) dma16(r, &Vk[(wave * NBW + u) * 512], ov0 + 1024 * u, 0);
     };
     // the row's marginal state Ĥ_i^T ([c][a], D rows of 2D bytes, stored in
     // the K ring with the K layout's chunk swizzle once the loop is done) and
@@ -169,13 +182,15 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // it inside the last block instead spills registers in the loop)
     const S *hr = hhat + rid * (long)Lp;
     auto load_hhat = [&]() __attribute__((always_inline)) {
-        constexpr int NBH = D * D * 2 / 1024 / 4;        // 1 KB pieces per wave
-        const __amdgpu_buffer_rsrc_t rh = make_rsrc(hr, (uint32_t)((D * D + D) * sizeof(S)));
+        constexpr int HDMA = D * KCPR / 64;              // 1 KB pieces of the padded D x D state (34 or 9)
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(hr, (uint32_t)(D * D * sizeof(S)));
         T *dst = &Kk[0][0];
-#pragma unroll
-        for (int u = 0; u < NBH; ++u)
-            dma16(rh, dst + (wave * NBH + u) * 512, off_klayout<D>((wave * NBH + u) * 1024 + 16 * lane), 0);
-        if (wave == 0 && lane < D / 8) dma16(rh, Zl, (uint32_t)(D * D * sizeof(S)) + 16 * lane, 0);
+        for (int t = wave; t < HDMA; t += 4) {
+            const int pos = 64 * t + lane, row = pos / KCPR, ch = pos % KCPR;
+            dma16(rh, dst + t * 512, ch < D / 8 ? (uint32_t)(row * D * 2 + ch * 16) : 0x40000000u, 0);
+        }
+        if (wave == 0 && lane < D / 8)
+            dma16(make_rsrc(hr, (uint32_t)((D * D + D) * sizeof(S))), Zl, (uint32_t)(D * D * sizeof(S)) + 16 * lane, 0);
     };
     v8<T> pb[2];
     // S^T = K Q^T of block c and its softmax: P^T in pb
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const int j = blk_of(c);
         v8<T> ak[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ak[s] = ld8<T>(&Kk[slot][koff[s]]);
+        for (int s = 0; s < NS; ++s) ak[s] = ld8<T>(&Kk[slot][kbase + 16 * s]);
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
 #pragma unroll
             for (int r = 0; r < 16; ++r) yl[t][r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) mma16(yl[t], ld8<S>(&Hs[c * D + ((2 * s + hh) ^ kswz<D>(c)) * 8]), ph[s]);
+            for (int s = 0; s < NS; ++s) mma16(yl[t], ld8<S>(&Hs[c * KRS + 16 * s + 8 * hh]), ph[s]);
         }
     }
     lds_barrier();                                       // the ring is free for the exchange

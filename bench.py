@@ -61,6 +61,7 @@ bf16 MFMA roofline, with the fp64 oracle timed on a sample of rows.
 import argparse
 import ctypes
 import json
+import math
 import os
 import sys
 import time
@@ -546,13 +547,25 @@ def clock_sampler():
         return None
     samples, stop = [], threading.Event()
 
+    def read():
+        # the mean over the eight XCDs where the metrics table has them
+        try:
+            clks = amdsmi.amdsmi_get_gpu_metrics_info(handle)["current_gfxclks"]
+            clks = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 65535]
+            if clks:
+                return sum(clks) / len(clks)
+        except Exception:
+            pass
+        try:
+            return float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+        except Exception:
+            return None
+
     def run():
         while not stop.is_set():
-            try:
-                info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
-                samples.append(float(info["clk"]))
-            except Exception:
-                pass
+            c = read()
+            if c is not None:
+                samples.append(c)
             stop.wait(0.02)
     th = threading.Thread(target=run, daemon=True)
     th.start()
@@ -564,17 +577,20 @@ def clock_sampler():
     return finish
 
 
-def busy_clock(step, seconds=0.8):
+def busy_clock(step, call_ms, seconds=0.8):
     """The graphics clock (MHz) sampled while the GPU runs `step` back to
-    back for about `seconds`; the first fifth of the samples (the clock
-    ramping up) is dropped."""
+    back for about `seconds`; calls are enqueued in batches of about 50 ms
+    of GPU work between synchronisations, so that short calls do not leave
+    the GPU idle (and clocked down) while the host waits; the first fifth
+    of the samples (the clock ramping up) is dropped."""
     import torch
     finish = clock_sampler()
     if finish is None:
         return []
+    batch = max(4, int(math.ceil(50.0 / max(call_ms, 1e-3))))
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        for _ in range(4):
+        for _ in range(batch):
             step()
         torch.cuda.synchronize()
     samples = finish()
@@ -637,7 +653,7 @@ def run_forward(args, cid, rc, rn, flush, cpu=True):
     t1 = time.perf_counter()
     warm = per_call_ms(step, args.calls)
     flushed = per_call_ms(step, args.calls, flush)
-    clocks = busy_clock(step)
+    clocks = busy_clock(step, sorted(warm)[len(warm) // 2])
     # per-stage times (HIP events around each kernel, on the stream it runs
     # on) in a separate pass, so that the event records stay out of the
     # timed steps

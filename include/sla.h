@@ -251,9 +251,9 @@ sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int 
 /* Stage timing, for profiling.  While enabled on a thread, every sla_forward
  * call of that thread records HIP events around each of its kernels, on the
  * stream the kernel runs on: 0 pool, 1 classify, 2 state, 3 assemble, 4 fused
- * (a stage that does not run records zero time).  The state stage runs
- * concurrently with pool and classify, so stage times do not add up to the
- * time of a call.  sla_stage_times waits for the recorded
+ * (a stage that does not run records zero time).  The stages run one
+ * after another on the caller's stream, so with timing on their times add
+ * up to about the time of a call.  sla_stage_times waits for the recorded
  * events, writes the summed milliseconds per stage to ms[0..4] and the number
  * of calls summed to *calls, and forgets them.  Events are created on first
  * use and kept per thread.  Disabled by default.  sla_forward_lists,

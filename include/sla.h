@@ -130,6 +130,25 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
                        void *out, int8_t *mask_out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* sla_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc).  Arguments and results
+ * are those of sla_forward.  The scratch memory is a static device array of
+ * SLA_NOALLOC_SCRATCH_BYTES inside the library: each GPU holds its own copy
+ * from the first call on it (its address is looked up then, with that
+ * device current) until the process ends.  A call whose sla_workspace_size()
+ * exceeds SLA_NOALLOC_SCRATCH_BYTES returns SLA_ERR_WORKSPACE before any
+ * launch (512 MiB holds B=1, H=12, N=32760, d=128 at the default shares:
+ * 403 MiB).  Every call on one GPU uses the same array: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller; nothing needs clearing between calls. */
+#define SLA_NOALLOC_SCRATCH_BYTES ((size_t)512 << 20)
+sla_status sla_forward_noalloc(const void *q, const void *k, const void *v, const float *w_proj,
+                               sla_dtype in_dtype, sla_dtype out_dtype,
+                               int B, int H, int N, int d, int block,
+                               double crit_frac, double negl_frac, sla_phi phi,
+                               void *out, int8_t *mask_out, void *stream);
+
 /* Gradients of sla_forward (SLA article, section 三: FlashAttention
  * gradients for the sparse part, linear-attention gradients for the linear
  * part).  The block labels are those sla_forward forms from the same q, k

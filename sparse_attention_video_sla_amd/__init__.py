@@ -146,6 +146,33 @@ def forward(q, k, v, w, crit_frac: float = 0.05, negl_frac: float = 0.10, block:
     return (out, mask) if return_mask else out
 
 
+def forward_noalloc(q, k, v, w, out, crit_frac: float = 0.05, negl_frac: float = 0.10, block: int = 64,
+                    mask_out=None):
+    """sla_forward_noalloc: the forward pass of `forward` into the caller's
+    `out` (and optional int8 `mask_out` [B,H,Nb,Nb]), with the library's
+    static scratch array instead of a workspace; nothing is allocated."""
+    torch = _torch()
+    _check_gpu(q, k, v, w, out)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one shape and dtype")
+    B, H, N, d = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (d, d):
+        raise ValueError("w must be float32 [d, d]")
+    if out.shape != q.shape or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous [B,H,N,d] tensor on q's device")
+    Nb = -(-N // block)
+    if mask_out is not None and (tuple(mask_out.shape) != (B, H, Nb, Nb) or mask_out.dtype != torch.int8
+                                 or not mask_out.is_contiguous()):
+        raise ValueError("mask_out must be a contiguous int8 [B,H,Nb,Nb] tensor")
+    out_code = _lib.SLA_F32 if out.dtype == torch.float32 else _dtype_code(out)
+    _lib.check(_lib.load().sla_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(),
+                                               _dtype_code(q), out_code, B, H, N, d, block, crit_frac, negl_frac,
+                                               _lib.SLA_PHI_SOFTMAX, out.data_ptr(),
+                                               mask_out.data_ptr() if mask_out is not None else None,
+                                               _stream_ptr(q.device)))
+    return out
+
+
 def lvsa_plan(T: int, C: int, W: int):
     """(T_per, |G_s|, frames per set) of the LVSA frame sets (host arithmetic)."""
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()

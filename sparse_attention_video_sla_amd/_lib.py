@@ -14,10 +14,11 @@ LIB_PATH = os.path.join(HERE, "libsla.so")
 SLA_OK, SLA_ERR_INVALID_ARG, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_DEVICE = range(5)
 SLA_F32, SLA_BF16 = 0, 1
 SLA_PHI_SOFTMAX = 0
+NOALLOC_SCRATCH_BYTES = 512 << 20   # SLA_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/sla.h declares
 EXPORTS = ("sla_version", "sla_counts", "sla_workspace_size", "sla_pool", "sla_classify",
-           "sla_forward", "sla_lists_workspace_size", "sla_forward_lists", "sla_lvsa_plan", "sla_lvsa_sets",
+           "sla_forward", "sla_forward_noalloc", "sla_lists_workspace_size", "sla_forward_lists", "sla_lvsa_plan", "sla_lvsa_sets",
            "sla_lvsa_workspace_size", "sla_forward_lvsa", "sla_sta_tile_order",
            "sla_sta_workspace_size", "sla_forward_sta", "sla_backward_workspace_size",
            "sla_backward", "sla_block_mass", "sla_mask_stats", "sla_set_stage_timing", "sla_stage_times",
@@ -56,6 +57,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.sla_classify.argtypes = [P, P, I, I, I, I, D, D, P, P, P, P, P]
     L.sla_forward.restype = I
     L.sla_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, D, I, P, P, P, SZ, P]
+    L.sla_forward_noalloc.restype = I
+    L.sla_forward_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, D, I, P, P, P]
     L.sla_lists_workspace_size.restype = I
     L.sla_lists_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     L.sla_forward_lists.restype = I

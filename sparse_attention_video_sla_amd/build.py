@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsla.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "pool.hip", "classify.hip", "state.hip", "assemble.hip", "fused.hip", "fused16s.hip", "mass.hip", "lists.hip", "lvsa.hip", "sta.hip", "backward.hip"]
+SOURCES = ["api.hip", "pool.hip", "classify.hip", "state.hip", "assemble.hip", "fused.hip", "fused16s.hip", "mass.hip", "lists.hip", "lvsa.hip", "sta.hip", "backward.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -148,6 +148,20 @@ void mark_unused_stages(StageEvents *ev, hipStream_t s) {
 
 }  // namespace
 
+namespace sla {
+// Sets the thread's error text (sla_last_error) for entry points defined in
+// other source files, and returns st.
+sla_status set_error(sla_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+}  // namespace sla
+
 extern "C" {
 
 sla_status sla_set_stage_timing(int enable) {

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sla.h"
+
 namespace sla {
 
 struct ClassifyArgs {
@@ -125,6 +127,9 @@ hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st);       // 
 hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st);  // linear rows + transposed sums
 hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st);  // linear keys + dW
 hipError_t launch_zero(float *p, long n, hipStream_t st);
+
+// Sets the thread's error text (sla_last_error); returns st.
+sla_status set_error(sla_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // STA tiles: tile sizes, windows, tile grid, tile volume and the largest
 // |delta| per axis worth testing (2*delta*t <= W)

@@ -210,3 +210,27 @@ def test_lists_entry_points_reject(lib):
     assert call(a3=_lib.SLA_F32) == _lib.SLA_ERR_UNSUPPORTED      # float inputs
     assert call(a12=40) == _lib.SLA_ERR_INVALID_ARG              # kmax > Nb
     assert call() == _lib.SLA_ERR_WORKSPACE                      # no room for the schedule
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """sla_forward_noalloc checks its arguments like sla_forward, and rejects
+    sizes whose workspace exceeds its static scratch before any device call."""
+    def call(B=1, H=2, N=3000, d=128, ind=_lib.SLA_BF16, rc=0.05, rn=0.10, q=FAKE):
+        return lib.sla_forward_noalloc(q, FAKE, FAKE, FAKE, ind, _lib.SLA_F32, B, H, N, d, 64, rc, rn,
+                                       _lib.SLA_PHI_SOFTMAX, FAKE, None, None)
+    assert call(B=1, H=24, N=118800) == _lib.SLA_ERR_WORKSPACE          # 3048 MiB of workspace
+    assert b"static scratch" in lib.sla_last_error()
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(1, 12, 32760, 128, 64, _lib.SLA_BF16, 0.05, 0.10, ctypes.byref(n)) == 0
+    assert n.value <= _lib.NOALLOC_SCRATCH_BYTES                          # the Wan2.1 480p shape fits
+    assert call(N=0) == _lib.SLA_ERR_INVALID_ARG
+    assert call(d=96) == _lib.SLA_ERR_UNSUPPORTED
+    assert call(ind=7) == _lib.SLA_ERR_UNSUPPORTED
+    assert call(rc=0.7, rn=0.4) == _lib.SLA_ERR_INVALID_ARG
+    assert call(q=None) == _lib.SLA_ERR_INVALID_ARG
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES

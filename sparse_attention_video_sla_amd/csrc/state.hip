@@ -157,16 +157,60 @@ __global__ __launch_bounds__(2 * D) void state_kernel(const T *__restrict__ k, c
 }
 
 // workgroup barrier that leaves global loads in flight (the prefetched block)
+// Reductions over aligned groups of W = 8 or 16 lanes (a token row's
+// channel chunks) with DPP moves instead of LDS permutes: after the two quad
+// steps every lane of a quad holds the quad's result; a mirror inside each
+// half row (row) then pairs every lane with one of the other quad (half).
+__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
+    int r;
+    switch (ctrl_sel) {                      // the control word must be a constant
+    case 0: r = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false); break; // row_mirror
+    }
+    return __int_as_float(r);
+}
+template <int W> __device__ __forceinline__ float group_max(float x) {
+    static_assert(W == 8 || W == 16, "8- or 16-lane groups");
+#pragma unroll
+    for (int t = 0; t < (W == 16 ? 4 : 3); ++t) x = fmaxf(x, dpp_f(x, t));
+    return x;
+}
+template <int W> __device__ __forceinline__ float group_sum(float x) {
+    static_assert(W == 8 || W == 16, "8- or 16-lane groups");
+#pragma unroll
+    for (int t = 0; t < (W == 16 ? 4 : 3); ++t) x += dpp_f(x, t);
+    return x;
+}
+
+// Sum over the lanes l, l ^ W, l ^ 2W, ... of a wave (W = 8 or 16): the
+// lanes that hold the same channel chunk of different token rows.  Each
+// swap of rows (16-lane groups) or halves gives every lane the pair's other
+// value.
+template <int W> __device__ __forceinline__ float column_sum(float x) {
+    static_assert(W == 8 || W == 16, "8- or 16-lane groups");
+    if constexpr (W == 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));   // row_ror:8
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
 __device__ __forceinline__ void st_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
 }
 
 // bf16 inputs, fp16 states: a persistent grid of two workgroups per CU, each
-// walking the key blocks b = blockIdx.x, + gridDim.x, ...  W stays in LDS for
-// the workgroup's lifetime.  The next block's K and V are loaded into the
-// registers that held the current block's as soon as phi and V are in LDS, so
-// the loads run under the products and stores of the current block.  The
+// zeroing its share of the padding rows, then walking the real key blocks
+// b = bh * Nb + j = blockIdx.x, + gridDim.x, ...  W stays in LDS for the
+// workgroup's lifetime.  The next block's K and V are loaded (buffer loads:
+// pad rows read zero, no per-lane branch) into the registers that held the
+// current block's as soon as phi and V are in LDS, so the loads run under the
+// products of the current block; they are waited for before the block's
+// stores, so that the stores drain under the next block's work.  z comes
+// from per-thread partial sums of phi, reduced across lanes and waves.  The
 // state h'^T goes out through LDS (8-byte units swizzled by row) as whole
 // contiguous rows.
 template <int D>
@@ -184,7 +228,9 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
     __shared__ __attribute__((aligned(16))) f16 Vs[64 * SSTR];
     __shared__ __attribute__((aligned(16))) f16 Ph[64 * PSTR];
     __shared__ __attribute__((aligned(16))) f16 Ws[D * WSTR];
+    __shared__ __attribute__((aligned(16))) float Zp[NT / 64][D];   // z partial sums per wave
     static_assert(32 * D * 2 <= 64 * SSTR * 2 && 32 * D * 2 <= 64 * PSTR * 2, "staging fits");
+    static_assert(NCH * NT == 64 * CPR && 64 % (NT / CPR) == 0, "thread t holds rows t / CPR + (NT / CPR) u");
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,10 +240,13 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
     }
 
     Chunk kc[NCH], vc[NCH];
-    auto load = [&](long bb) {
-        const int j = (int)(bb % Nbc);
-        const long bh = bb / Nbc;
-        const int n = j < Nb ? min(64, N - 64 * j) : 0;
+    // buffer loads over the block's valid rows: pad rows (and padding
+    // blocks) read zeros without a per-lane branch, so the prefetched
+    // registers are the same on every path
+    auto load = [&](long bb) {                // bb = bh * Nb + j, a real block
+        const int j = (int)(bb % Nb);
+        const long bh = bb / Nb;
+        const int n = min(64, N - 64 * j);
         const bf16 *kb = k + (bh * N + 64L * j) * D;
         const bf16 *vb = v + (bh * N + 64L * j) * D;
 #pragma unroll
@@ -208,24 +257,30 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
             vc[u] = ok ? ld_chunk(vb + (long)row * D + cc * 8) : zero_chunk();
         }
     };
-    long b = blockIdx.x;
     const long G = gridDim.x;
+    // rows of the padding blocks (Nb <= j < Nbc) are zero
+    const int npad = Nbc - Nb;
+    for (long p = blockIdx.x; p < total / Nb * npad; p += G) {
+        f16 *hsb = hs + ((p / npad) * Nbc + Nb + p % npad) * (long)Lp;
+        for (int x = tid; x < Lp; x += NT) hsb[x] = (f16)0.f;
+    }
+    long b = blockIdx.x;
     if (b < total) load(b);
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the loop's head then never waits for memory
     st_barrier();                            // W in LDS
 
     constexpr float LOG2E = 1.4426950408889634f;
     const float scale = 1.f / 64.f;
-    for (; b < total; b += G) {
-        const int j = (int)(b % Nbc);
-        f16 *hsb = hs + b * (long)Lp;
-        if (j >= Nb) {                       // padding block: a zero row (uniform branch, no LDS)
-            for (int x = tid; x < Lp; x += NT) hsb[x] = (f16)0.f;
-            if (b + G < total) load(b + G);
-            continue;
-        }
+    for (; b < total; b += G) {              // the real blocks b = bh * Nb + j
+        const int j = (int)(b % Nb);
+        f16 *hsb = hs + ((b / Nb) * Nbc + j) * (long)Lp;
         const int n = min(64, N - 64 * j);
         // phi(K) per token row (the CPR threads of a row are consecutive lanes);
-        // phi and V to LDS in fp16
+        // phi and V to LDS in fp16; zp: this thread's share of z (its rows,
+        // channel chunk tid % CPR), summed from the fp16 phi values
+        float zp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zp[e] = 0.f;
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
             const int ch = tid + NT * u, row = ch / CPR, cc = ch % CPR;
@@ -234,13 +289,11 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
             float mx = -__builtin_inff();
 #pragma unroll
             for (int e = 0; e < 8; ++e) { xf[e] = (float)x[e]; mx = fmaxf(mx, xf[e]); }
-#pragma unroll
-            for (int off = 1; off < CPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            mx = group_max<CPR>(mx);
             float sum = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { xf[e] = fast_exp2((xf[e] - mx) * LOG2E); sum += xf[e]; }
-#pragma unroll
-            for (int off = 1; off < CPR; off <<= 1) sum += __shfl_xor(sum, off, 64);
+            sum = group_sum<CPR>(sum);
             const float inv = (row < n) ? 1.f / sum : 0.f;
             f16 ph[8], vv[8];
             const bf16 *y = reinterpret_cast<const bf16 *>(&vc[u]);
@@ -248,9 +301,18 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
             for (int e = 0; e < 8; ++e) {
                 ph[e] = (f16)(xf[e] * inv);
                 vv[e] = (f16)(float)y[e];
+                zp[e] += (float)ph[e];
             }
             __builtin_memcpy(&Ph[row * PSTR + cc * 8], ph, sizeof(ph));
             __builtin_memcpy(&Vs[row * SSTR + cc * 8], vv, sizeof(vv));
+        }
+        // z over the wave's rows: lanes l, l ^ CPR, ... hold the same channels
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zp[e] = column_sum<CPR>(zp[e]);
+        if (lane < CPR) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 4)
+                *reinterpret_cast<f32x4 *>(&Zp[wave][lane * 8 + e]) = f32x4{zp[e], zp[e + 1], zp[e + 2], zp[e + 3]};
         }
         st_barrier();
         if (b + G < total) load(b + G);      // next block, under this block's products and stores
@@ -287,9 +349,10 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
                 mma16(acch[mt], cat8<f16>(lds_col4<f16>(Ph, PSTR, k0, n0, lane), lds_col4<f16>(Ph, PSTR, k0 + 8, n0, lane)), bv);
             }
         }
-        if (tid < D) {                       // z = sum over the block's tokens of phi
-            float z = 0.f;
-            for (int t = 0; t < 64; ++t) z += (float)Ph[t * PSTR + tid];
+        if (tid < D) {                       // z = sum over the block's tokens of phi: the waves' shares in order
+            float z = Zp[0][tid];
+#pragma unroll
+            for (int w = 1; w < NT / 64; ++w) z += Zp[w][tid];
             hsb[D * D + tid] = (f16)(z * scale);
         }
         for (int x = D * D + D + tid; x < Lp; x += NT) hsb[x] = (f16)0.f;
@@ -309,6 +372,12 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
                 for (int e = 0; e < 4; ++e) y[e] = (f16)(acch[mt][4 * g + e] * scale);
                 __builtin_memcpy(&stg[l32 * D + 4 * (u ^ (l32 % UPR))], &y, sizeof(y));
             }
+        // The next block's K and V (loaded since the first barrier) are
+        // waited for here, before this block's stores: loads and stores share
+        // one counter, so a wait after the stores would also wait for the
+        // writes to complete; this way the stores drain under the next
+        // block's softmax and products.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         f16 *orow = hsb + (long)(32 * wave) * D;
 #pragma unroll
         for (int x = 0; x < 32 / RPI; ++x) {
@@ -328,8 +397,8 @@ static hipError_t launch_state16_t(const StateArgs &a, hipStream_t st) {
     int dev = 0, cus = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    const long total = a.BH * a.Nbc;
-    const long grid = std::min<long>(total, 2L * cus);
+    const long total = a.BH * a.Nb;          // real blocks; the kernel also zeroes the padding rows
+    const long grid = std::min<long>(std::max<long>(total, a.BH * (a.Nbc - a.Nb)), 2L * cus);
     state16_kernel<D><<<(unsigned)grid, 2 * D, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, (const f16 *)a.wstate,
                                                         a.N, a.Nb, a.Nbc, total, (f16 *)a.hs, a.Lp);
     return hipGetLastError();

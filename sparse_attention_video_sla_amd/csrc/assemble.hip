@@ -20,9 +20,12 @@
 // workgroup, 4 waves of 128 x 64, K-steps of 32 key blocks double-buffered
 // through registers and LDS.
 //
-// fp16 path: one workgroup of 8 waves owns 128 state columns and up to 512
-// query-block rows (64 per wave), so a head's states stream from memory into
-// LDS once per 512 rows.  The K-steps (64 key blocks, 16 KB of Hs) go through
+// fp16 path: one workgroup of 4 waves owns 128 state columns and up to 256
+// query-block rows (64 per wave); two workgroups share a CU (72 KB of LDS
+// and up to 256 registers per lane each), so one's barrier waits, prologue
+// and epilogue run under the other's products.  The two row tiles of a
+// column slice are neighbours in the launch order and read the slice's
+// states through the same L2.  The K-steps (64 key blocks, 16 KB of Hs) go through
 // a ring of four LDS stages filled by loads that go straight from memory into
 // LDS: three steps are in flight while the fourth is multiplied, with one
 // barrier per step.  A stage also holds the step's indicator words of the
@@ -56,18 +59,21 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void *lds, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
 }
 
+constexpr int AT_W = 4;                                  // waves per workgroup, 64 rows each
 constexpr int AT_TM = 128;                               // state columns per workgroup
-constexpr int AT_TN = 512;                               // query-block rows per workgroup (8 waves x 64)
+constexpr int AT_TN = 64 * AT_W;                         // query-block rows per workgroup (256)
 constexpr int AT_TK = 64;                                // key blocks per step
 constexpr int AT_HS = AT_TK * AT_TM;                     // Hs elements of one step (16 KB)
-constexpr int AT_STAGE = AT_HS + 2 * AT_TN * 2;          // one LDS stage in f16 units: Hs, then 2 x 512 words
-constexpr int AT_NA = AT_HS * 2 / 1024 / 8;              // 1 KB Hs loads per wave per step (2)
-constexpr int AT_NW = 2 * AT_TN * 4 / 256 / 8;           // 256-byte indicator loads per wave per step (2)
+constexpr int AT_STAGE = AT_HS + 2 * AT_TN * 2;          // one LDS stage in f16 units: Hs, then 2 x AT_TN words
+constexpr int AT_NA = AT_HS * 2 / 1024 / AT_W;           // 1 KB Hs loads per wave per step (4)
+constexpr int AT_NW = 2 * AT_TN * 4 / 256 / AT_W;        // 256-byte indicator loads per wave per step (2)
 constexpr int AT_VM = AT_NA + AT_NW;                     // memory operations per wave per step
+static_assert(2 * AT_VM < 16, "the stage wait's count fits the low vmcnt field");
+static_assert(AT_STAGE >= 2 * 4096, "a stage holds the epilogue slices of two waves");
 
-// one K-step into a stage: this wave's two 1 KB pieces of the Hs rows (four
-// 256-byte rows each) and its two 256-byte pieces of the indicator words
-// (word h of rows 64 i .. 64 i + 63 of the tile at 64 (8 h + i))
+// one K-step into a stage: this wave's AT_NA 1 KB pieces of the Hs rows (four
+// 256-byte rows each) and its AT_NW 256-byte pieces of the indicator words
+// (word h of rows 64 g .. 64 g + 63 of the tile at 64 (AT_W h + g))
 template <typename T>
 __device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rb, T *S,
                                          const uint32_t (&va)[AT_NA], const uint32_t (&vw)[AT_NW], int w,
@@ -79,16 +85,33 @@ __device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buf
     for (int u = 0; u < AT_NW; ++u) dma4(rb, W + 64 * (AT_NW * w + u), vw[u] + woff);
 }
 
-// 8 indicator bits -> 8 16-bit values 0 or 1 (1.0 = 0x3C00 in fp16, 0x3F80
-// in bf16): each dword takes two bits y, spread to bit 0 and bit 16 by
-// (y * 0x8001) & 0x10001, times the bits of 1.0
+// 8 indicator bits -> 8 16-bit B values, 0 or ONE.
+// fp16: ONE = 2^-14 (0x0400, the smallest normal: high byte 0x04, low byte
+// 0), so a value is a byte: each nibble spreads to bit 2 of four bytes by one
+// multiply (bit i of n lands at i + 2 + 7k for k = 0..3, distinct positions,
+// so no carries; byte k keeps bit k), and byte permutes put byte e in the
+// high byte of half e: ten operations for the eight values.  The products
+// h * 2^-14 and their fp32 sums are those of ONE = 1 scaled by 2^-14 exactly
+// (no value comes near the bottom of the fp32 range), and the output scale
+// takes the 2^14 back.
+// bf16: ONE = 1.0 (0x3F80): each dword takes two bits y, spread to bit 0 and
+// bit 16 by (y * 0x8001) & 0x10001, times the bits of 1.0.
+template <typename T> constexpr float kOneInv = __is_same(T, f16) ? 16384.f : 1.f;   // 1 / ONE
 template <typename T> __device__ __forceinline__ v8<T> expand_bits(uint32_t x) {
-    constexpr uint32_t one = __is_same(T, f16) ? 0x3C00u : 0x3F80u;
     uint32_t d[4];
+    if constexpr (__is_same(T, f16)) {
+        const uint32_t wa = __umul24(x & 0xFu, 0x810204u) & 0x04040404u;          // bits 0..3 -> bytes 0..3
+        const uint32_t wb = __umul24((x >> 4) & 0xFu, 0x810204u) & 0x04040404u;   // bits 4..7 -> bytes 4..7
+        d[0] = __builtin_amdgcn_perm(wb, wa, 0x010C000Cu);   // byte sel 12 reads as 0x00
+        d[1] = __builtin_amdgcn_perm(wb, wa, 0x030C020Cu);
+        d[2] = __builtin_amdgcn_perm(wb, wa, 0x050C040Cu);
+        d[3] = __builtin_amdgcn_perm(wb, wa, 0x070C060Cu);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t y = (x >> (2 * e)) & 3u;
-        d[e] = __umul24(__umul24(y, 0x8001u) & 0x10001u, one);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t y = (x >> (2 * e)) & 3u;
+            d[e] = __umul24(__umul24(y, 0x8001u) & 0x10001u, 0x3F80u);
+        }
     }
     v8<T> r;
     __builtin_memcpy(&r, d, sizeof(r));
@@ -134,7 +157,7 @@ __device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int 
 // through LDS) or float (written from the accumulators as they are, 16 bytes
 // per lane)
 template <typename T, typename O>
-__global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restrict__ mbits,
+__global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t *__restrict__ mbits,
                                                          const T *__restrict__ hs,
                                                          const int32_t *__restrict__ mcount,
                                                          O *__restrict__ hhat, int Nb, int Nbc, int Nbp, int Lp,
@@ -167,8 +190,8 @@ __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restr
     }
 #pragma unroll
     for (int u = 0; u < AT_NW; ++u) {
-        const int i = AT_NW * wave + u;                  // word i / 8 of rows 64 (i % 8) + lane
-        vw[u] = (uint32_t)(((long)(i >> 3) * Nbp + row0 + 64 * (i & 7) + lane) * 4);
+        const int i = AT_NW * wave + u;                  // word i / AT_W of rows 64 (i % AT_W) + lane
+        vw[u] = (uint32_t)(((long)(i / AT_W) * Nbp + row0 + 64 * (i % AT_W) + lane) * 4);
     }
     const uint32_t astep = (uint32_t)AT_TK * Lp * 2, wstep = (uint32_t)Nbp * 8;
 
@@ -212,7 +235,7 @@ __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restr
             const int i = wrow + 32 * nt + l32;
             if (i >= Nb) continue;
             const int mc = mcount[bh * Nb + i];
-            const float sc = mc > 0 ? 64.f / (float)mc : 0.f;
+            const float sc = mc > 0 ? 64.f / (float)mc * kOneInv<T> : 0.f;
             O *orow = hhat + (bh * Nb + i) * (long)Lp + col0;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -228,13 +251,14 @@ __global__ __launch_bounds__(512) void assemble16_kernel(const uint32_t *__restr
 
     // epilogue: the wave's 32-row halves go through a private 8 KB LDS slice,
     // 8-byte unit u of row r at unit u ^ r (conflict-free both ways)
+    static_assert(AT_W <= 8, "four stages hold the slices of up to eight waves");
     T *stg0 = (wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) + (wave & 1) * 4096;
     O *stg = reinterpret_cast<O *>(stg0);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int i = wrow + 32 * nt + l32;
         const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
-        const float sc = mc > 0 ? 64.f / (float)mc : 0.f;
+        const float sc = mc > 0 ? 64.f / (float)mc * kOneInv<T> : 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -380,11 +404,11 @@ hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st) {
         const long G = a.BH * tiles_m * tiles_n;
         const int per = (int)((G + 7) / 8);
         if (a.bf16_f32)
-            assemble16_kernel<bf16, float><<<(unsigned)(8L * per), 512, 0, st>>>(
+            assemble16_kernel<bf16, float><<<(unsigned)(8L * per), 64 * AT_W, 0, st>>>(
                 a.mbits, (const bf16 *)a.hs, a.mcount, (float *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G,
                 per);
         else
-            assemble16_kernel<f16, f16><<<(unsigned)(8L * per), 512, 0, st>>>(
+            assemble16_kernel<f16, f16><<<(unsigned)(8L * per), 64 * AT_W, 0, st>>>(
                 a.mbits, (const f16 *)a.hs, a.mcount, (f16 *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G,
                 per);
     }

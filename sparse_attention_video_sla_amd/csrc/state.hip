@@ -205,17 +205,18 @@ __device__ __forceinline__ void st_barrier() {
 // bf16 inputs, fp16 states: a persistent grid of two workgroups per CU, each
 // zeroing its share of the padding rows, then walking the real key blocks
 // b = bh * Nb + j = blockIdx.x, + gridDim.x, ...  W stays in LDS for the
-// workgroup's lifetime.  The next block's K and V are loaded (buffer loads:
-// pad rows read zero, no per-lane branch) into the registers that held the
-// current block's as soon as phi and V are in LDS, so the loads run under the
+// workgroup's lifetime (each workgroup converts the float W itself).  The
+// next block's K and V are loaded into the registers that held the current
+// block's as soon as phi and V are in LDS, so the loads run under the
 // products of the current block; they are waited for before the block's
-// stores, so that the stores drain under the next block's work.  z comes
+// stores (and once before the loop), so that no wait in the loop counts the
+// stores: these drain under the next block's work.  z comes
 // from per-thread partial sums of phi, reduced across lanes and waves.  The
 // state h'^T goes out through LDS (8-byte units swizzled by row) as whole
 // contiguous rows.
 template <int D>
 __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-                                                          const f16 *__restrict__ w, int N, int Nb, int Nbc,
+                                                          const float *__restrict__ w, int N, int Nb, int Nbc,
                                                           long total, f16 *__restrict__ hs, int Lp) {
     constexpr int NT = 2 * D;
     constexpr int CPR = D / 8;               // 16-byte chunks per token row
@@ -234,9 +235,14 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int x = tid; x < D * CPR; x += NT) {
+    for (int x = tid; x < D * CPR; x += NT) {   // W (float) to LDS in fp16
         const int r = x / CPR, c = x % CPR;
-        st_chunk(&Ws[r * WSTR + 8 * c], ld_chunk(w + (long)r * D + 8 * c));
+        const Chunk a = ld_chunk(w + (long)r * D + 8 * c), b = ld_chunk(w + (long)r * D + 8 * c + 4);
+        const float *fa = reinterpret_cast<const float *>(&a), *fb = reinterpret_cast<const float *>(&b);
+        f16 h[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { h[e] = (f16)fa[e]; h[e + 4] = (f16)fb[e]; }
+        __builtin_memcpy(&Ws[r * WSTR + 8 * c], h, sizeof(h));
     }
 
     Chunk kc[NCH], vc[NCH];
@@ -391,15 +397,13 @@ __global__ __launch_bounds__(2 * D, 2) void state16_kernel(const bf16 *__restric
 
 template <int D>
 static hipError_t launch_state16_t(const StateArgs &a, hipStream_t st) {
-    w_to_state_kernel<f16><<<(D * D + 255) / 256, 256, 0, st>>>(a.w, (f16 *)a.wstate, D * D);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     int dev = 0, cus = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     const long total = a.BH * a.Nb;          // real blocks; the kernel also zeroes the padding rows
     const long grid = std::min<long>(std::max<long>(total, a.BH * (a.Nbc - a.Nb)), 2L * cus);
-    state16_kernel<D><<<(unsigned)grid, 2 * D, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, (const f16 *)a.wstate,
+    state16_kernel<D><<<(unsigned)grid, 2 * D, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w,
                                                         a.N, a.Nb, a.Nbc, total, (f16 *)a.hs, a.Lp);
     return hipGetLastError();
 }

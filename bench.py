@@ -14,7 +14,8 @@ attention in the same kernels).
 Printed: one JSON line per setting.  `value` is effective TFLOP/s over the
 whole call, counting the method's work F = 4*64*64*d per critical block pair
 + 4*64*d*d per query block with marginal blocks, and `ms_per_step` the mean
-of the K timed steps.  `timing` gives the median, p10 and p90 of 100 calls
+of the K timed steps.  Before the W warm-up steps, untimed calls run for
+about 0.2 s, so that the GPU clock has ramped up from idle.  `timing` gives the median, p10 and p90 of 100 calls
 timed one by one with HIP events on the call's stream, with the 256 MB
 last-level cache (MALL) warm and flushed before each call (a 512 MB fill),
 and the GPU clock sampled through amdsmi while calls run back to back.  `roofline`
@@ -120,7 +121,10 @@ def source_sha(source):
         if name in seen:
             return
         seen.add(name)
-        src = open(os.path.join(CSRC, name), "rb").read()
+        path = os.path.join(CSRC, name)
+        if not os.path.exists(path):
+            path = os.path.join(ROOT, "include", name)
+        src = open(path, "rb").read()
         h.update(src)
         for inc in re.findall(rb'^#include "([^"]+)"', src, re.M):
             add(inc.decode())
@@ -256,6 +260,7 @@ def run_lvsa(args):
     def step():
         sla.forward_lvsa(q, k, v, T, wl.C, wl.W, wl.step, out=out, workspace=ws)
 
+    prewarm(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -362,6 +367,7 @@ def run_sta(args):
     def step():
         sla.forward_sta(q, k, v, grid, tile, window, out=out, workspace=ws)
 
+    prewarm(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -450,6 +456,7 @@ def run_backward(args, wl):
     def step():
         sla.backward(q, k, v, w, dout, rc, rn, workspace=ws)
 
+    prewarm(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -597,6 +604,19 @@ def busy_clock(step, call_ms, seconds=0.8):
     return samples[len(samples) // 5:]
 
 
+def prewarm(step, seconds=0.2, cap=2000):
+    """Untimed calls for about `seconds` before the warm-up steps: the GPU's
+    clock takes several milliseconds of load to ramp up from idle, which a
+    few warm-up steps of a sub-millisecond call do not cover."""
+    import torch
+    t0, n = time.perf_counter(), 0
+    while n < cap and time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+
+
 def per_call_ms(step, n, flush=None):
     """n calls timed one by one with HIP events on torch's current stream
     (the stream the library enqueues on); with `flush` a fill kernel runs
@@ -643,6 +663,7 @@ def run_forward(args, cid, rc, rn, flush, cpu=True):
     def step():
         sla.forward(q, k, v, w, rc, rn, out=out, workspace=ws)
 
+    prewarm(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -717,8 +738,10 @@ def run_forward(args, cid, rc, rn, flush, cpu=True):
         "dense_equivalent_tflops": round(4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 3),
         "stages": stages,
     }
-    if clk:
-        # the nominal peak is quoted at 2.4 GHz; the same peak at the sampled clock
+    if clk and clk["median_mhz"] >= 1000.0:
+        # the nominal peak is quoted at 2.4 GHz; the same peak at the sampled
+        # clock (not given when the sampled clock shows a mostly idle GPU, as
+        # for calls too short to keep it busy from the host)
         line["roofline"]["frac_at_measured_clock"] = round(achieved / (peak * clk["median_mhz"] / 2400.0), 4)
     if cpu and not args.no_cpu:
         # bounded samples: whole heads for the small workloads, 64 query
@@ -732,6 +755,22 @@ def run_forward(args, cid, rc, rn, flush, cpu=True):
 
 ALL_SETTINGS = [(0, 0.05, 0.10), (1, 0.05, 0.10), (2, 0.025, 0.10), (2, 0.05, 0.10), (2, 0.10, 0.10),
                 (3, 0.05, 0.10), (4, 0.05, 0.10), (4, 1.0, 0.0)]
+
+
+def copy_calibration(calls=5):
+    """A plain elementwise kernel of known traffic (torch.neg on 2^28 float32:
+    1 GiB read, 1 GiB written per launch): its FETCH_SIZE and WRITE_SIZE
+    readings give the factors that turn those counters into HBM bytes."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(calls):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch.neg float32 elementwise", "elements": n,
+                                           "bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+                                           "launches": calls}}), flush=True)
 
 
 def main():
@@ -750,6 +789,8 @@ def main():
     ap.add_argument("--lvsa", action="store_true", help="LVSA frame-level sparse attention line (long-video workload)")
     ap.add_argument("--sta", action="store_true", help="sliding tile attention line (HunyuanVideo-sized latent)")
     ap.add_argument("--backward", action="store_true", help="SLA backward line (same workload as the forward)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain elementwise copy of known size (for scaling the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the SLA forward here is a single-GPU kernel "
@@ -760,6 +801,9 @@ def main():
     import torch
     from sparse_attention_video_sla_amd.inputs import WORKLOADS
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.lvsa:
         run_lvsa(args)
         return

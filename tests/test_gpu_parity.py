@@ -134,6 +134,53 @@ def test_classify_ties(sla):
         assert np.array_equal(got["crit"].cpu().numpy(), ref["crit"])
 
 
+@pytest.mark.parametrize("Nb,d,dtype", [(150, 64, "f32"), (600, 128, "f32"), (1857, 128, "bf16"),
+                                        (2432, 64, "bf16")])
+def test_forward_labels_ties_and_near_ties(sla, Nb, d, dtype):
+    """The forward pass ranks on float32 scores and settles the keys near
+    each cut in fp64.  Its labels must equal the oracle's also on rows built
+    against float32: exact ties of many blocks (200 copies of one key block,
+    more than one wave's band), all-zero query blocks (every score 0), and
+    near ties below float32 resolution (float inputs: copies of a key block
+    with one element moved by one ulp), at several shares so that the groups
+    straddle the cuts."""
+    from sparse_attention_video_sla_amd.inputs import round_bf16
+    say("forward labels with ties", Nb, d, dtype)
+    N = 64 * Nb - 17
+    rng = np.random.default_rng(Nb + d)
+    H = 2
+    q = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    # head 0: key blocks 100..299 (or as many as there are) copy block 10;
+    # query blocks 0..20 are zero
+    hi = min(300, Nb - 1)
+    for j in range(100, hi):
+        k[0, 0, 64 * j:64 * j + 64] = k[0, 0, 640:704]
+    q[0, 0, :64 * 21] = 0.0
+    # head 1: key blocks 40..79 copy block 7 with one element moved by j ulps
+    for t, j in enumerate(range(40, 80)):
+        blk = k[0, 1, 448:512].copy()
+        blk[t % 64, t % d] = np.nextafter(blk[t % 64, t % d], np.float32(np.inf), dtype=np.float32)
+        for _ in range(t % 3):
+            blk[(t + 1) % 64, (t + 5) % d] = np.nextafter(blk[(t + 1) % 64, (t + 5) % d], np.float32(-np.inf),
+                                                          dtype=np.float32)
+        k[0, 1, 64 * j:64 * j + 64] = blk
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    w = (rng.standard_normal((d, d)) / np.sqrt(d)).astype(np.float32)
+    qp, kp = orc.pool(q), orc.pool(k)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    wd = torch.from_numpy(w).to("cuda")
+    for rc, rn in [(0.02, 0.05), (0.05, 0.10), (0.13, 0.2), (0.3, 0.3), (0.5, 0.45)]:
+        ref = orc.classify(qp, kp, rc, rn)
+        _, mask = sla.forward(qd, kd, vd, wd, rc, rn, return_mask=True)
+        torch.cuda.synchronize()
+        got = mask.cpu().numpy()
+        bad = np.argwhere((got != ref["mask"]).any(axis=-1))
+        assert bad.size == 0, "rows with other labels (b, h, i): %s" % bad[:5].tolist()
+
+
 # ------------------------------------------------------------------ forward, small
 
 

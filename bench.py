@@ -42,13 +42,16 @@ latent: 30x48x80 tokens (N = 115200, tile-major), tiles (6, 8, 8), window
 pair.
 
 With --backward it prints instead one JSON line for the SLA backward pass
-(sla_backward: the forward recomputed inside, then dQ, dK, dV, dW) on the
-same Wan2.1 480p workload; `value` counts the forward's F plus 10*64*64*d per
-critical pair (five products), 6*64*d*d per query block and 10*64*d*d per
-key block of the linear branch, and (d*d + d) per marginal pair (the
-transposed sums).  Its `roofline` is for the slowest stage; `traffic` is
-filled from the backward's counter summary when that stage is one kernel
-(dQ, dK/dV or the linear keys).
+on the same Wan2.1 480p workload: `value` and `ms_per_step` are those of
+sla_backward_saved (dQ, dK, dV, dW from the state sla_forward_save left, as
+a training step runs it), counting 10*64*64*d per critical pair (five
+products), 6*64*d*d per query block and 10*64*d*d per key block of the
+linear branch, and (d*d + d) per marginal pair (the transposed sums);
+`recompute` gives sla_backward (the forward run again inside, its F counted
+too) and `training_step_ms` sla_forward_save + sla_backward_saved.  Its
+`roofline` is for the slowest stage; `traffic` is filled from the
+backward's counter summary when that stage is one kernel (dQ, dK/dV or the
+linear keys).
 
 With --quality it prints instead one JSON line for the mask-quality
 diagnostics (sla_block_mass + sla_mask_stats) on the same workload: the
@@ -452,26 +455,42 @@ def run_backward(args, wl):
     Nb = -(-N // 64)
     kc, kn = sla.counts(Nb, rc, rn)
     ws = torch.empty(sla.backward_workspace_size(B, H, N, d, rc, rn), dtype=torch.uint8, device=dev)
+    _, saved = sla.forward_save(q, k, v, w, rc, rn)
+    saved_ws = torch.empty_like(ws)
 
-    def step():
+    def recompute():
         sla.backward(q, k, v, w, dout, rc, rn, workspace=ws)
 
-    prewarm(step)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    def step():
+        sla.backward_saved(saved, q, k, v, w, dout)
+
+    def train_step():
+        sla.forward_save(q, k, v, w, rc, rn, saved=saved_train)
+        sla.backward_saved(saved_train, q, k, v, w, dout)
+
+    saved_train = sla.SavedForward(saved_ws, q.shape, rc, rn, 64)
+
+    def timed(fn):
+        prewarm(fn)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms = timed(step)
+    ms_recompute = timed(recompute)
+    ms_train = timed(train_step)
     L = _lib.load()
     L.sla_set_stage_timing(1)
     ms_buf = (ctypes.c_float * 5)()
     calls = ctypes.c_int()
     L.sla_stage_times(ms_buf, ctypes.byref(calls))
     for _ in range(args.steps):
-        step()
+        recompute()
     _lib.check(L.sla_stage_times(ms_buf, ctypes.byref(calls)))
     L.sla_set_stage_timing(0)
     st_ms = {name: ms_buf[i] / max(calls.value, 1) for i, name in enumerate(BWD_STAGES)}
@@ -483,9 +502,8 @@ def run_backward(args, wl):
     f_rows = 6.0 * 64 * d * d * marg_rows
     f_keys = 10.0 * 64 * d * d * B * H * Nb if lin else 0.0
     f_sums = float(marg_pairs) * (d * d + d)
-    total = f_fwd + f_sparse + f_rows + f_keys + f_sums
-    ms = (t1 - t0) * 1e3 / args.steps
-    value = total / (ms * 1e-3) / 1e12
+    grads = f_sparse + f_rows + f_keys + f_sums
+    value = grads / (ms * 1e-3) / 1e12
     per_stage = {
         "forward": (f_fwd, "mfma"), "dq": (6.0 * 64 * 64 * d * pairs, "mfma"), "dkv": (8.0 * 64 * 64 * d * pairs, "mfma"),
         "linear_rows": (f_rows + f_sums, "mfma"), "linear_keys": (f_keys, "mfma")}
@@ -494,12 +512,13 @@ def run_backward(args, wl):
         fl, bound = per_stage[name]
         stages[name] = {"ms": round(st_ms[name], 4),
                         "TFLOP/s": round(fl / max(st_ms[name], 1e-9) / 1e9, 1), "bound": bound}
-    dom = max(BWD_STAGES, key=lambda n: st_ms[n])
+    dom = max((n for n in BWD_STAGES if n != "forward"), key=lambda n: st_ms[n])   # the saved path's stages
     fl, bound = per_stage[dom]
     peak = PEAK_BF16_TFLOPS
     achieved = fl / max(st_ms[dom], 1e-9) / 1e9
     line = {
-        "metric": "effective TFLOP/s + ms/call of the SLA backward (forward recomputed + dQ, dK, dV, dW) at N=32760",
+        "metric": "effective TFLOP/s + ms/call of the SLA backward (dQ, dK, dV, dW from the saved forward state) "
+                  "at N=32760",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded; local sinusoid Q/K + noise, V ~ N(0,1); dO ~ N(0,1))",
@@ -512,6 +531,11 @@ def run_backward(args, wl):
                      "kernel": "backward stage " + dom,
                      "flops_per_launch": fl, "avg_launch_ms": round(st_ms[dom], 4)},
         "stages": stages,
+        "stages_of": "sla_backward (stage forward: the forward run again inside)",
+        "recompute": {"ms": round(ms_recompute, 4),
+                      "TFLOP/s": round((f_fwd + grads) / (ms_recompute * 1e-3) / 1e12, 3),
+                      "what": "sla_backward: the forward run again inside, then the same gradient kernels"},
+        "training_step_ms": round(ms_train, 4),
     }
     if not args.no_cpu:
         from oracle import backward as ob
@@ -532,7 +556,8 @@ def run_backward(args, wl):
         line["cpu_baseline"] = {"value": round(fs / t / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
                                 "kind": "oracle", "seconds": round(t, 3),
                                 "sample": "the first %d tokens of heads 0-%d (the token-level oracle is quadratic in N): "
-                                          "labels, then autograd of the fp64 forward; F counted the same way"
+                                          "labels, then autograd of the fp64 forward; F counts the forward's and the gradients' "
+                                          "flops, both of which the oracle computes"
                                           % (n_tok, heads - 1)}
     print(json.dumps(line), flush=True)
 

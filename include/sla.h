@@ -166,6 +166,32 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
                         double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* The same gradients without running the forward pass again, for training
+ * loops that run the forward anyway (SLA article, section 三: the forward
+ * keeps what the backward's split needs).
+ * sla_forward_save is sla_forward for bf16 inputs (same arguments, same
+ * output bits, the same kernels) that also leaves in `saved` everything the
+ * backward reads: the labels, critical lists, marginal-state products and
+ * counts, the sparse part of the output alone (float32) and its rows'
+ * log-sum-exp.  `saved`: sla_backward_workspace_size() bytes, 256-byte
+ * aligned, owned by the caller; mask_out, if not NULL, gets a copy of the
+ * labels.
+ * sla_backward_saved takes the arguments of sla_backward, with `saved` as its
+ * workspace; it must hold what sla_forward_save wrote for the same q, k, v,
+ * w_proj, shapes and fractions, untouched since (nothing checks this: other
+ * contents give wrong gradients, not an error).  Its gradients are those of
+ * sla_backward bit for bit.  It overwrites the gradient scratch parts of
+ * `saved` and keeps the forward's parts, so it can run again on the same
+ * saved state (with another dout). */
+sla_status sla_forward_save(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
+                            sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                            double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *saved,
+                            size_t saved_bytes, void *stream);
+sla_status sla_backward_saved(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                              sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                              double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *saved,
+                              size_t saved_bytes, void *stream);
+
 /* Sparse attention over block lists given by the caller, with the linear
  * branch off (a mask source other than the scores, e.g. the LVSA page's
  * frame-level sets A(t) = G_s U W(t) turned into key blocks; block-sparse
@@ -281,7 +307,8 @@ sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int 
  * stages zero.  sla_backward calls record: 0 the forward recomputed inside,
  * 1 the transposed lists and dQ of the sparse part, 2 dK and dV of the
  * sparse part, 3 the linear part's rows and transposed sums, 4 its keys and
- * dW. */
+ * dW; sla_backward_saved calls the same with stage 0 zero; sla_forward_save
+ * calls are recorded as forward calls. */
 #define SLA_NUM_STAGES 5
 sla_status sla_set_stage_timing(int enable);
 sla_status sla_stage_times(float *ms, int *calls);

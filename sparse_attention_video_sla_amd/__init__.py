@@ -16,7 +16,7 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa", "sta_tile_order", "forward_sta", "backward",
+__all__ = ["counts", "workspace_size", "pool", "classify", "forward", "forward_lists", "lvsa_plan", "lvsa_sets", "forward_lvsa", "sta_tile_order", "forward_sta", "backward", "forward_save", "backward_saved", "SavedForward",
            "block_mass", "mask_stats", "version",
            "SlaError"]
 
@@ -289,6 +289,69 @@ def backward(q, k, v, w, dout, crit_frac: float = 0.05, negl_frac: float = 0.10,
                               B, H, N, d, block, crit_frac, negl_frac, _lib.SLA_PHI_SOFTMAX, dq.data_ptr(),
                               dk.data_ptr(), dv.data_ptr(), dw.data_ptr(), workspace.data_ptr(), workspace.numel(),
                               _stream_ptr(q.device)))
+    return dq, dk, dv, dw
+
+
+class SavedForward:
+    """What sla_forward_save leaves for sla_backward_saved: the device buffer
+    and the arguments it was made with."""
+
+    def __init__(self, buffer, shape, crit_frac, negl_frac, block):
+        self.buffer, self.shape = buffer, tuple(shape)
+        self.crit_frac, self.negl_frac, self.block = crit_frac, negl_frac, block
+
+
+def forward_save(q, k, v, w, crit_frac: float = 0.05, negl_frac: float = 0.10, block: int = 64, out_dtype=None,
+                 return_mask: bool = False, saved=None):
+    """sla_forward_save: the output of `forward` (bf16 inputs) and a
+    SavedForward for backward_saved.  `saved` may be an earlier SavedForward
+    of the same sizes, whose buffer is then reused."""
+    torch = _torch()
+    _check_gpu(q, k, v, w)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have one shape and dtype")
+    B, H, N, d = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (d, d):
+        raise ValueError("w must be float32 [d, d]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_code = _lib.SLA_F32 if out_dtype == torch.float32 else _dtype_code(torch.empty(0, dtype=out_dtype))
+    dev = q.device
+    out = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    Nb = -(-N // block)
+    mask = torch.empty((B, H, Nb, Nb), dtype=torch.int8, device=dev) if return_mask else None
+    L = _lib.load()
+    n = ctypes.c_size_t()
+    _lib.check(L.sla_backward_workspace_size(B, H, N, d, block, crit_frac, negl_frac, ctypes.byref(n)))
+    buf = saved.buffer if saved is not None and saved.buffer.numel() >= n.value else \
+        torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    _lib.check(L.sla_forward_save(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(), _dtype_code(q), out_code,
+                                  B, H, N, d, block, crit_frac, negl_frac, _lib.SLA_PHI_SOFTMAX, out.data_ptr(),
+                                  mask.data_ptr() if mask is not None else None, buf.data_ptr(), buf.numel(),
+                                  _stream_ptr(dev)))
+    ctx = SavedForward(buf, q.shape, crit_frac, negl_frac, block)
+    return (out, mask, ctx) if return_mask else (out, ctx)
+
+
+def backward_saved(saved, q, k, v, w, dout):
+    """sla_backward_saved: the gradients of `backward` (dq, dk, dv, dw) from
+    the state forward_save left in `saved` for these same q, k, v, w."""
+    torch = _torch()
+    _check_gpu(q, k, v, w, dout)
+    if not (q.shape == k.shape == v.shape == dout.shape) or not (q.dtype == k.dtype == v.dtype == dout.dtype):
+        raise ValueError("q, k, v, dout must have one shape and dtype")
+    if tuple(q.shape) != saved.shape:
+        raise ValueError("the saved forward state is for shape %s, not %s" % (saved.shape, tuple(q.shape)))
+    B, H, N, d = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (d, d):
+        raise ValueError("w must be float32 [d, d]")
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    dw = torch.empty((d, d), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.load().sla_backward_saved(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(), dout.data_ptr(), _dtype_code(q), B, H, N, d,
+        saved.block, saved.crit_frac, saved.negl_frac, _lib.SLA_PHI_SOFTMAX, dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), dw.data_ptr(), saved.buffer.data_ptr(), saved.buffer.numel(), _stream_ptr(q.device)))
     return dq, dk, dv, dw
 
 

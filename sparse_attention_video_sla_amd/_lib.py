@@ -18,7 +18,7 @@ NOALLOC_SCRATCH_BYTES = 512 << 20   # SLA_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/sla.h declares
 EXPORTS = ("sla_version", "sla_counts", "sla_workspace_size", "sla_pool", "sla_classify",
-           "sla_forward", "sla_forward_noalloc", "sla_lists_workspace_size", "sla_forward_lists", "sla_lvsa_plan", "sla_lvsa_sets",
+           "sla_forward", "sla_forward_noalloc", "sla_forward_save", "sla_backward_saved", "sla_lists_workspace_size", "sla_forward_lists", "sla_lvsa_plan", "sla_lvsa_sets",
            "sla_lvsa_workspace_size", "sla_forward_lvsa", "sla_sta_tile_order",
            "sla_sta_workspace_size", "sla_forward_sta", "sla_backward_workspace_size",
            "sla_backward", "sla_block_mass", "sla_mask_stats", "sla_set_stage_timing", "sla_stage_times",
@@ -83,6 +83,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.sla_backward_workspace_size.argtypes = [I, I, I, I, I, D_, D_, ctypes.POINTER(SZ)]
     L.sla_backward.restype = I
     L.sla_backward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D_, D_, I, P, P, P, P, P, SZ, P]
+    L.sla_forward_save.restype = I
+    L.sla_forward_save.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D_, D_, I, P, P, P, SZ, P]
+    L.sla_backward_saved.restype = I
+    L.sla_backward_saved.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D_, D_, I, P, P, P, P, P, SZ, P]
     L.sla_block_mass.restype = I
     L.sla_block_mass.argtypes = [P, P, I, I, I, I, I, I, P, P]
     L.sla_mask_stats.restype = I

@@ -519,13 +519,14 @@ sla_status sla_classify(const float *q_pool, const float *k_pool, int B, int H, 
 }
 
 // The forward pass; with lse_out the fused kernel also writes each row's
-// log-sum-exp, and with linear_off it leaves the linear branch out of `out`
-// (the states and the marginal sums are still formed), as the backward needs.
+// log-sum-exp, with os_out the sparse part of the output alone (float32),
+// and with linear_off it leaves the linear branch out of `out` (the states
+// and the marginal sums are still formed), as the backward needs.
 static sla_status forward_impl(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
                                sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
                                double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *workspace,
                                size_t workspace_bytes, void *stream, float *lse_out, bool linear_off,
-                               bool timed = true) {
+                               bool timed = true, float *os_out = nullptr) {
     if (!q || !k || !v || !w_proj || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
     sla_status st = check_shape(B, H, N, d, block);
     if (st != SLA_OK) return st;
@@ -604,7 +605,7 @@ static sla_status forward_impl(const void *q, const void *k, const void *v, cons
     fa.q = q; fa.k = k; fa.v = v; fa.ulist = (const uint32_t *)(ws + L.ulist);
     fa.ucount = (const int32_t *)(ws + L.ucount); fa.kc = kc;
     fa.hhat = ws + L.hhat; fa.mcount = states && !linear_off ? mcount : nullptr; fa.Lp = L.Lp;
-    fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d; fa.lse = lse_out;
+    fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d; fa.lse = lse_out; fa.os = os_out;
     fa.bf16_in = !f32; fa.bf16_out = out_dtype == SLA_BF16;
     fa.crit = (const int32_t *)(ws + L.crit);
     st = device_status(f32 ? sla::launch_fused(fa, s) : sla::launch_fused16s(fa, s), "fused launch");
@@ -664,37 +665,34 @@ sla_status sla_backward_workspace_size(int B, int H, int N, int d, int block, do
     return SLA_OK;
 }
 
-sla_status sla_backward(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
-                        sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
-                        double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+// Checks shared by the backward entry points; the layout of the workspace.
+static sla_status backward_checks(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                                  sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                                  double negl_frac, sla_phi phi, const float *dq, const float *dk, const float *dv,
+                                  const float *dw, const void *workspace, size_t workspace_bytes, BwdLayout *o,
+                                  Layout *L, int *kc, int *kn) {
     if (!q || !k || !v || !w_proj || !dout || !dq || !dk || !dv || !dw)
         return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
     if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs");
     if (phi != SLA_PHI_SOFTMAX) return fail(SLA_ERR_UNSUPPORTED, "feature map %d not supported", (int)phi);
-    BwdLayout o;
-    Layout L;
-    int kc, kn;
-    sla_status st = bwd_layout(B, H, N, d, block, crit_frac, negl_frac, &o, &L, &kc, &kn);
+    sla_status st = bwd_layout(B, H, N, d, block, crit_frac, negl_frac, o, L, kc, kn);
     if (st != SLA_OK) return st;
     if (!workspace) return fail(SLA_ERR_INVALID_ARG, "null workspace");
-    if (workspace_bytes < o.total)
-        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, o.total);
+    if (workspace_bytes < o->total)
+        return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, o->total);
     if (((uintptr_t)workspace & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    char *ws = (char *)workspace;
-    hipStream_t s = (hipStream_t)stream;
+    return SLA_OK;
+}
+
+// The gradient stages, from the forward's labels, lists, marginal states,
+// sparse output and log-sum-exp in the workspace (timed as stages 1-4).
+static sla_status backward_grads(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                                 int B, int H, int N, int d, float *dq, float *dk, float *dv, float *dw, char *ws,
+                                 const BwdLayout &o, const Layout &L, int kc, int kn, hipStream_t s, StageEvents *ev) {
     const int Nb = (N + 63) / 64;
-    float *o_s = (float *)(ws + o.o_s), *lse = (float *)(ws + o.lse);
-    StageEvents *ev = timed_call();
-    // the forward again: labels, critical lists, marginal states, and the
-    // sparse output with its log-sum-exp
-    mark_stage(ev, 0, 0, s);
-    st = forward_impl(q, k, v, w_proj, SLA_BF16, SLA_F32, B, H, N, d, block, crit_frac, negl_frac, phi, o_s, nullptr,
-                      ws, L.total, stream, lse, true, false);
-    mark_stage(ev, 0, 1, s);
-    if (st != SLA_OK) return st;
     sla::BackwardArgs a{};
-    a.q = q; a.k = k; a.v = v; a.dout = dout; a.w = w_proj; a.o_s = o_s; a.lse = lse;
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.w = w_proj;
+    a.o_s = (const float *)(ws + o.o_s); a.lse = (const float *)(ws + o.lse);
     a.crit = (const int32_t *)(ws + L.crit); a.kc = kc; a.mask = (const int8_t *)(ws + L.mask);
     a.hhat = ws + L.hhat; a.mcount = (const int32_t *)(ws + L.mcount);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbuf = (float *)(ws + o.dbuf);
@@ -703,7 +701,7 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
     a.dh2 = ws + o.dh2; a.dhs = (float *)(ws + o.dhs); a.dwp = (float *)(ws + o.dwp);
     a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Nbp = L.Nbp; a.Lp = L.Lp; a.D = d;
     mark_stage(ev, 1, 0, s);
-    st = device_status(sla::launch_backward_dq(a, s), "backward dq launch");
+    sla_status st = device_status(sla::launch_backward_dq(a, s), "backward dq launch");
     mark_stage(ev, 1, 1, s);
     if (st != SLA_OK) return st;
     mark_stage(ev, 2, 0, s);
@@ -720,6 +718,77 @@ sla_status sla_backward(const void *q, const void *k, const void *v, const float
     if (linear) st = device_status(sla::launch_backward_lin_keys(a, s), "backward linear keys launch");
     mark_stage(ev, 4, 1, s);
     return st;
+}
+
+sla_status sla_backward(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                        sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                        double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    BwdLayout o;
+    Layout L;
+    int kc, kn;
+    sla_status st = backward_checks(q, k, v, w_proj, dout, in_dtype, B, H, N, d, block, crit_frac, negl_frac, phi, dq,
+                                    dk, dv, dw, workspace, workspace_bytes, &o, &L, &kc, &kn);
+    if (st != SLA_OK) return st;
+    char *ws = (char *)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    StageEvents *ev = timed_call();
+    // the forward again: labels, critical lists, marginal states, and the
+    // sparse output with its log-sum-exp
+    mark_stage(ev, 0, 0, s);
+    st = forward_impl(q, k, v, w_proj, SLA_BF16, SLA_F32, B, H, N, d, block, crit_frac, negl_frac, phi,
+                      ws + o.o_s, nullptr, ws, L.total, stream, (float *)(ws + o.lse), true, false);
+    mark_stage(ev, 0, 1, s);
+    if (st != SLA_OK) return st;
+    return backward_grads(q, k, v, w_proj, dout, B, H, N, d, dq, dk, dv, dw, ws, o, L, kc, kn, s, ev);
+}
+
+sla_status sla_forward_save(const void *q, const void *k, const void *v, const float *w_proj, sla_dtype in_dtype,
+                            sla_dtype out_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                            double negl_frac, sla_phi phi, void *out, int8_t *mask_out, void *saved,
+                            size_t saved_bytes, void *stream) {
+    if (!q || !k || !v || !w_proj || !out) return fail(SLA_ERR_INVALID_ARG, "null tensor pointer");
+    if (in_dtype != SLA_BF16) return fail(SLA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs");
+    if (out_dtype != SLA_F32 && out_dtype != SLA_BF16)
+        return fail(SLA_ERR_UNSUPPORTED, "output dtype must be F32 or the input dtype");
+    if (phi != SLA_PHI_SOFTMAX) return fail(SLA_ERR_UNSUPPORTED, "feature map %d not supported", (int)phi);
+    BwdLayout o;
+    Layout L;
+    int kc, kn;
+    sla_status st = bwd_layout(B, H, N, d, block, crit_frac, negl_frac, &o, &L, &kc, &kn);
+    if (st != SLA_OK) return st;
+    if (!saved) return fail(SLA_ERR_INVALID_ARG, "null saved-state buffer");
+    if (saved_bytes < o.total)
+        return fail(SLA_ERR_WORKSPACE, "saved-state buffer of %zu bytes is smaller than the %zu required", saved_bytes,
+                    o.total);
+    if (((uintptr_t)saved & 255) != 0) return fail(SLA_ERR_INVALID_ARG, "saved-state buffer must be 256-byte aligned");
+    char *ws = (char *)saved;
+    hipStream_t s = (hipStream_t)stream;
+    // the labels stay in the buffer (the backward reads them there); a
+    // caller's mask_out gets a copy
+    st = forward_impl(q, k, v, w_proj, in_dtype, out_dtype, B, H, N, d, block, crit_frac, negl_frac, phi, out, nullptr,
+                      ws, L.total, stream, (float *)(ws + o.lse), false, true, (float *)(ws + o.o_s));
+    if (st != SLA_OK || !mask_out) return st;
+    const size_t mask_bytes = (size_t)B * H * ((N + 63) / 64) * ((N + 63) / 64);
+    return device_status(hipMemcpyAsync(mask_out, ws + L.mask, mask_bytes, hipMemcpyDeviceToDevice, s),
+                         "mask copy");
+}
+
+sla_status sla_backward_saved(const void *q, const void *k, const void *v, const float *w_proj, const void *dout,
+                              sla_dtype in_dtype, int B, int H, int N, int d, int block, double crit_frac,
+                              double negl_frac, sla_phi phi, float *dq, float *dk, float *dv, float *dw, void *saved,
+                              size_t saved_bytes, void *stream) {
+    BwdLayout o;
+    Layout L;
+    int kc, kn;
+    sla_status st = backward_checks(q, k, v, w_proj, dout, in_dtype, B, H, N, d, block, crit_frac, negl_frac, phi, dq,
+                                    dk, dv, dw, saved, saved_bytes, &o, &L, &kc, &kn);
+    if (st != SLA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    StageEvents *ev = timed_call();
+    mark_stage(ev, 0, 0, s);                             // no forward stage
+    mark_stage(ev, 0, 1, s);
+    return backward_grads(q, k, v, w_proj, dout, B, H, N, d, dq, dk, dv, dw, (char *)saved, o, L, kc, kn, s, ev);
 }
 
 }  // extern "C"

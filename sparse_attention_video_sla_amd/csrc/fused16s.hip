@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
                                                           const int32_t *__restrict__ pcount, int bcast, int fp,
                                                           const S *__restrict__ hhat,
                                                           const int32_t *__restrict__ mcount, int Lp,
-                                                          TO *__restrict__ out, float *__restrict__ lse, long G,
+                                                          TO *__restrict__ out, float *__restrict__ lse,
+                                                          float *__restrict__ os, long G,
                                                           int per_xcd, int N, int Nb, float sl2) {
     static_assert(__is_same(T, bf16), "bf16 inputs");
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
@@ -381,6 +382,20 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     }
     if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * (64L * Nb) + qrow] = __builtin_inff();
 
+    // the sparse part alone, for a backward pass that reuses this forward
+    // (critical lists only)
+    if (!SLOTS && os && qvalid) {
+        float *srow = os + (bh * N + qrow) * (long)D;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const int c0 = 32 * (NCH * kh + t);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store4s<float>(srow + c0 + 8 * g + 4 * hh, mine[t][4 * g], mine[t][4 * g + 1], mine[t][4 * g + 2],
+                               mine[t][4 * g + 3]);
+        }
+    }
+
     if (lin) {
 #pragma unroll
         for (int t = 0; t < NCH; ++t)
@@ -408,7 +423,7 @@ static hipError_t launch_fused16s_t(const FusedArgs &a, hipStream_t st) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
     fused16s_kernel<bf16, f16, D, TO, SLOTS, MARKS><<<(unsigned)(8L * per), 256, 0, st>>>(
         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.crit, a.kc, a.slots, a.pcount, a.bcast ? 1 : 0,
-        a.fp, (const f16 *)a.hhat, a.mcount, a.Lp, (TO *)a.out, a.lse, G, per, a.N, a.Nb, sl2);
+        a.fp, (const f16 *)a.hhat, a.mcount, a.Lp, (TO *)a.out, a.lse, a.os, G, per, a.N, a.Nb, sl2);
     return hipGetLastError();
 }
 

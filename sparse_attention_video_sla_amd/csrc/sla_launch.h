@@ -59,6 +59,7 @@ struct FusedArgs {
     bool bcast;              // one schedule shared by every head
     int fp;                  // tokens per frame for the frame marks in the slots (0: no marks)
     float *lse;              // nullable: [BH][64 Nb] log-sum-exp of each row's sparse softmax (log2 units)
+    float *os;               // nullable: [BH][N][D] float32 sparse part of the output (before the linear read-out)
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere
     int Lp;

@@ -182,6 +182,46 @@ def test_backward_rejects_before_launch(lib):
     assert bwd(lib, ws=FAKE + 8, wsb=n.value) == _lib.SLA_ERR_INVALID_ARG   # misaligned workspace
 
 
+def bwd_saved(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, do=FAKE, ind=_lib.SLA_BF16, B=1, H=1, N=128, d=128, block=64,
+             rc=0.05, rn=0.10, phi=0, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.sla_backward_saved(a["q"], a["k"], a["v"], a["w"], a["do"], a["ind"], a["B"], a["H"], a["N"], a["d"],
+                                  a["block"], a["rc"], a["rn"], a["phi"], a["dq"], a["dk"], a["dv"], a["dw"], a["ws"],
+                                  a["wsb"], a["stream"])
+
+
+def fwd_save(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, ind=_lib.SLA_BF16, outd=_lib.SLA_F32, B=1, H=1, N=128, d=128, block=64,
+             rc=0.05, rn=0.10, phi=0, out=FAKE, mask=None, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.sla_forward_save(a["q"], a["k"], a["v"], a["w"], a["ind"], a["outd"], a["B"], a["H"], a["N"], a["d"],
+                                a["block"], a["rc"], a["rn"], a["phi"], a["out"], a["mask"], a["ws"], a["wsb"],
+                                a["stream"])
+
+
+def test_saved_backward_rejects_before_launch(lib):
+    """sla_forward_save and sla_backward_saved validate everything on the
+    host before any launch; the saved state is sla_backward's workspace."""
+    n = ctypes.c_size_t()
+    assert lib.sla_backward_workspace_size(1, 1, 128, 128, 64, 0.05, 0.10, ctypes.byref(n)) == 0
+    for call in (bwd_saved, fwd_save):
+        assert call(lib, q=None) == _lib.SLA_ERR_INVALID_ARG
+        assert call(lib, ind=_lib.SLA_F32) == _lib.SLA_ERR_UNSUPPORTED
+        assert call(lib, phi=1) == _lib.SLA_ERR_UNSUPPORTED
+        assert call(lib, d=96) == _lib.SLA_ERR_UNSUPPORTED
+        assert call(lib, N=0) == _lib.SLA_ERR_INVALID_ARG
+        assert call(lib, rc=0.7, rn=0.4) == _lib.SLA_ERR_INVALID_ARG
+        assert call(lib, ws=None, wsb=n.value) == _lib.SLA_ERR_INVALID_ARG
+        assert call(lib, wsb=16) == _lib.SLA_ERR_WORKSPACE
+        assert call(lib, wsb=n.value - 1) == _lib.SLA_ERR_WORKSPACE
+        assert call(lib, ws=FAKE + 8, wsb=n.value) == _lib.SLA_ERR_INVALID_ARG   # misaligned
+    assert bwd_saved(lib, do=None) == _lib.SLA_ERR_INVALID_ARG
+    assert bwd_saved(lib, dw=None) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd_save(lib, out=None) == _lib.SLA_ERR_INVALID_ARG
+    assert fwd_save(lib, outd=2) == _lib.SLA_ERR_UNSUPPORTED
+
+
 def test_backward_workspace_size(lib):
     """The backward workspace holds the forward's and grows with the sequence."""
     nf, nb, nb2 = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()

@@ -148,3 +148,60 @@ def test_backward_deterministic(sla):
     torch.cuda.synchronize()
     for name, x, y in zip(("dq", "dk", "dv", "dw"), a, b):
         assert torch.equal(x, y), name
+
+
+@pytest.mark.parametrize("B,H,N,d,rc,rn,out_bf16", [
+    (1, 2, 1000, 128, 0.25, 0.25, False),
+    (1, 1, 777, 64, 0.1, 0.2, True),      # ragged last block, bf16 output
+    (2, 1, 640, 128, 1.0, 0.0, False),    # dense: no linear branch
+    (1, 1, 600, 64, 0.0, 0.5, False),     # no critical block: linear branch only
+    (2, 2, 2100, 128, 0.05, 0.10, True),  # the default fractions, ragged
+])
+def test_backward_saved_equals_recompute(sla, B, H, N, d, rc, rn, out_bf16):
+    """sla_forward_save gives sla_forward's output and labels bit for bit,
+    and sla_backward_saved on what it saved gives sla_backward's gradients
+    bit for bit, also when run a second time on the same saved state with
+    another output gradient."""
+    say("saved", B, H, N, d, rc, rn, out_bf16)
+    inp = make_inputs(B, H, (1, 1, N), d, "bf16", seed=N + 3)
+    rng = np.random.default_rng(N + 4)
+    douts = [dev(round_bf16(rng.standard_normal((B, H, N, d)).astype(np.float32))) for _ in range(2)]
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w = torch.from_numpy(inp.w).cuda()
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    ref_out, ref_mask = sla.forward(q, k, v, w, rc, rn, out_dtype=odt, return_mask=True)
+    out, mask, saved = sla.forward_save(q, k, v, w, rc, rn, out_dtype=odt, return_mask=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    assert torch.equal(mask, ref_mask)
+    for t, dout in enumerate(douts):
+        a = sla.backward(q, k, v, w, dout, rc, rn)
+        b = sla.backward_saved(saved, q, k, v, w, dout)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dq", "dk", "dv", "dw"), a, b):
+            assert torch.equal(x, y), (name, t)
+
+
+@pytest.mark.timeout(300)
+def test_backward_saved_full_size(sla):
+    """The same identities at the Wan2.1 480p workload (B=1, H=12, N=32760,
+    d=128, 5 % / 10 %), as the backward bench runs it."""
+    from sparse_attention_video_sla_amd.inputs import make_workload
+    inp = make_workload(1)
+    B, H, N, d = inp.q.shape
+    rc, rn = 0.05, 0.10
+    rng = np.random.default_rng(78)
+    dout = dev(round_bf16(rng.standard_normal((B, H, N, d)).astype(np.float32)))
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w = torch.from_numpy(inp.w).cuda()
+    say("saved full size", B, H, N, d)
+    ref_out = sla.forward(q, k, v, w, rc, rn)
+    out, saved = sla.forward_save(q, k, v, w, rc, rn)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    del ref_out, out
+    a = sla.backward(q, k, v, w, dout, rc, rn)
+    b = sla.backward_saved(saved, q, k, v, w, dout)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv", "dw"), a, b):
+        assert torch.equal(x, y), name

@@ -624,7 +624,7 @@ sla_status sla_forward(const void *q, const void *k, const void *v, const float 
 // ---- backward ----------------------------------------------------------------
 
 struct BwdLayout {
-    size_t fwd, o_s, lse, dbuf, tlist, tcnt, mbitsT, unit, dh2, dhs, dwp, total;
+    size_t fwd, o_s, lse, dbuf, tlist, tcnt, mbitsT, dhr, dexp, kbyte, hexp, dhs, dwp, total;
 };
 
 static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_frac, double negl_frac,
@@ -644,10 +644,12 @@ static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_
     o->dbuf = take(sizeof(float) * BH * 64 * Nb);
     o->tlist = take(sizeof(uint16_t) * BH * Nb * Nb);
     o->tcnt = take(sizeof(int32_t) * BH * Nb);
-    o->mbitsT = take(sizeof(uint32_t) * BH * (2 * L->Nbc / 32) * L->Nbp);
-    o->unit = take(sizeof(int32_t) * BH * Nb);
-    o->dh2 = take(sizeof(uint16_t) * BH * 2 * L->Nbc * L->Lp);
-    o->dhs = take(sizeof(float) * BH * Nb * L->Lp);
+    o->mbitsT = take(sizeof(uint32_t) * BH * (L->Nbc / 32) * L->Nbp);
+    o->dhr = take(sizeof(uint16_t) * BH * L->Nbc * L->Lp);
+    o->dexp = take(sizeof(int32_t) * BH * L->Nbc);
+    o->kbyte = take(BH * L->Nbc);
+    o->hexp = take(sizeof(int32_t) * BH);
+    o->dhs = take(sizeof(uint16_t) * BH * Nb * L->Lp);
     o->dwp = take(sizeof(float) * sla::backward_key_groups((long)BH, Nb, d) * d * d);
     o->total = off;
     return SLA_OK;
@@ -697,8 +699,9 @@ static sla_status backward_grads(const void *q, const void *k, const void *v, co
     a.hhat = ws + L.hhat; a.mcount = (const int32_t *)(ws + L.mcount);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbuf = (float *)(ws + o.dbuf);
     a.tlist = (uint16_t *)(ws + o.tlist); a.tcnt = (int32_t *)(ws + o.tcnt);
-    a.mbitsT = (uint32_t *)(ws + o.mbitsT); a.unit = (int32_t *)(ws + o.unit);
-    a.dh2 = ws + o.dh2; a.dhs = (float *)(ws + o.dhs); a.dwp = (float *)(ws + o.dwp);
+    a.mbitsT = (uint32_t *)(ws + o.mbitsT); a.dhr = ws + o.dhr; a.dexp = (int32_t *)(ws + o.dexp);
+    a.kbyte = (uint8_t *)(ws + o.kbyte); a.hexp = (int32_t *)(ws + o.hexp);
+    a.dhs = ws + o.dhs; a.dwp = (float *)(ws + o.dwp);
     a.BH = (long)B * H; a.N = N; a.Nb = Nb; a.Nbc = L.Nbc; a.Nbp = L.Nbp; a.Lp = L.Lp; a.D = d;
     mark_stage(ev, 1, 0, s);
     sla_status st = device_status(sla::launch_backward_dq(a, s), "backward dq launch");

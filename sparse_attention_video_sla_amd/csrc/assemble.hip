@@ -36,9 +36,14 @@
 // as bits (32 key blocks per word); each lane reads the words of its own
 // rows from the stage and expands them into the fp16 B operand in registers.  The output tile of a wave is
 // scaled, staged through LDS (8-byte units swizzled by row) and written as
-// whole contiguous row segments.  The same kernel takes bf16 rows with a
-// float output (the backward pass sums its state gradients this way, as
-// bf16 pairs hi + lo over twice the rows).
+// whole contiguous row segments.
+// Scaled mode (the backward pass sums its per-row state gradients this
+// way): input row k is stored as fp16 values x times 2^-E_k (|x| < 1), and
+// the B operand of (j, k) is 2^(E_k - R + 14) instead of 1 (R the largest
+// E_k of the head; rows more than 28 below it count as zero), given as the
+// fp16 exponent byte of each row; output row j is the sum times
+// 2^-(14 + c), c = ceil(log2 Nbc), which keeps it below 1 in magnitude: its
+// true value is that times 2^(R + c).
 #include "sla_device.h"
 #include "sla_launch.h"
 
@@ -70,6 +75,7 @@ constexpr int AT_NW = 2 * AT_TN * 4 / 256 / AT_W;        // 256-byte indicator l
 constexpr int AT_VM = AT_NA + AT_NW;                     // memory operations per wave per step
 static_assert(2 * AT_VM < 16, "the stage wait's count fits the low vmcnt field");
 static_assert(AT_STAGE >= 2 * 4096, "a stage holds the epilogue slices of two waves");
+constexpr int AT_KB_MAX = 4096;                          // scaled mode: rows (Nbc) at most
 
 // one K-step into a stage: this wave's AT_NA 1 KB pieces of the Hs rows (four
 // 256-byte rows each) and its AT_NW 256-byte pieces of the indicator words
@@ -85,42 +91,49 @@ __device__ __forceinline__ void at_issue(__amdgpu_buffer_rsrc_t rh, __amdgpu_buf
     for (int u = 0; u < AT_NW; ++u) dma4(rb, W + 64 * (AT_NW * w + u), vw[u] + woff);
 }
 
-// 8 indicator bits -> 8 16-bit B values, 0 or ONE.
-// fp16: ONE = 2^-14 (0x0400, the smallest normal: high byte 0x04, low byte
-// 0), so a value is a byte: each nibble spreads to bit 2 of four bytes by one
-// multiply (bit i of n lands at i + 2 + 7k for k = 0..3, distinct positions,
-// so no carries; byte k keeps bit k), and byte permutes put byte e in the
-// high byte of half e: ten operations for the eight values.  The products
-// h * 2^-14 and their fp32 sums are those of ONE = 1 scaled by 2^-14 exactly
-// (no value comes near the bottom of the fp32 range), and the output scale
-// takes the 2^14 back.
-// bf16: ONE = 1.0 (0x3F80): each dword takes two bits y, spread to bit 0 and
-// bit 16 by (y * 0x8001) & 0x10001, times the bits of 1.0.
-template <typename T> constexpr float kOneInv = __is_same(T, f16) ? 16384.f : 1.f;   // 1 / ONE
-template <typename T> __device__ __forceinline__ v8<T> expand_bits(uint32_t x) {
+// 8 indicator bits -> 8 fp16 B values, 0 or ONE = 2^-14 (0x0400, the
+// smallest normal: high byte 0x04, low byte 0), so a value is a byte: each
+// nibble spreads to bit 2 of four bytes by one multiply (bit i of n lands at
+// i + 2 + 7k for k = 0..3, distinct positions, so no carries; byte k keeps
+// bit k), and byte permutes put byte e in the high byte of half e: ten
+// operations for the eight values.  The products h * 2^-14 and their fp32
+// sums are those of ONE = 1 scaled by 2^-14 exactly (no value comes near the
+// bottom of the fp32 range), and the output scale takes the 2^14 back.
+constexpr float kOneInv = 16384.f;                       // 1 / ONE
+__device__ __forceinline__ v8<f16> expand_bits(uint32_t x) {
+    const uint32_t wa = __umul24(x & 0xFu, 0x810204u) & 0x04040404u;          // bits 0..3 -> bytes 0..3
+    const uint32_t wb = __umul24((x >> 4) & 0xFu, 0x810204u) & 0x04040404u;   // bits 4..7 -> bytes 4..7
     uint32_t d[4];
-    if constexpr (__is_same(T, f16)) {
-        const uint32_t wa = __umul24(x & 0xFu, 0x810204u) & 0x04040404u;          // bits 0..3 -> bytes 0..3
-        const uint32_t wb = __umul24((x >> 4) & 0xFu, 0x810204u) & 0x04040404u;   // bits 4..7 -> bytes 4..7
-        d[0] = __builtin_amdgcn_perm(wb, wa, 0x010C000Cu);   // byte sel 12 reads as 0x00
-        d[1] = __builtin_amdgcn_perm(wb, wa, 0x030C020Cu);
-        d[2] = __builtin_amdgcn_perm(wb, wa, 0x050C040Cu);
-        d[3] = __builtin_amdgcn_perm(wb, wa, 0x070C060Cu);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t y = (x >> (2 * e)) & 3u;
-            d[e] = __umul24(__umul24(y, 0x8001u) & 0x10001u, 0x3F80u);
-        }
-    }
-    v8<T> r;
+    d[0] = __builtin_amdgcn_perm(wb, wa, 0x010C000Cu);   // byte sel 12 reads as 0x00
+    d[1] = __builtin_amdgcn_perm(wb, wa, 0x030C020Cu);
+    d[2] = __builtin_amdgcn_perm(wb, wa, 0x050C040Cu);
+    d[3] = __builtin_amdgcn_perm(wb, wa, 0x070C060Cu);
+    v8<f16> r;
     __builtin_memcpy(&r, d, sizeof(r));
     return r;
 }
-
-// the 32 MFMAs of one K-step for a wave's 128 x 64 tile (rows 64 w .. 64 w + 63)
-template <typename T>
-__device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int w, int lane) {
+// Scaled mode: 8 indicator bits -> 8 fp16 B values, the row's exponent byte
+// (elo: rows 0..3, ehi: rows 4..7, one byte each, low two bits zero) or 0:
+// the spread bits (0x04 per byte) times 63 give a 0xFC mask per set byte
+// (no carry between bytes; the top byte's borrow leaves the word).
+__device__ __forceinline__ v8<f16> expand_bits_scaled(uint32_t x, uint32_t elo, uint32_t ehi) {
+    uint32_t wa = __umul24(x & 0xFu, 0x810204u) & 0x04040404u;
+    uint32_t wb = __umul24((x >> 4) & 0xFu, 0x810204u) & 0x04040404u;
+    wa = ((wa << 6) - wa) & elo;
+    wb = ((wb << 6) - wb) & ehi;
+    uint32_t d[4];
+    d[0] = __builtin_amdgcn_perm(wb, wa, 0x010C000Cu);
+    d[1] = __builtin_amdgcn_perm(wb, wa, 0x030C020Cu);
+    d[2] = __builtin_amdgcn_perm(wb, wa, 0x050C040Cu);
+    d[3] = __builtin_amdgcn_perm(wb, wa, 0x070C060Cu);
+    v8<f16> r;
+    __builtin_memcpy(&r, d, sizeof(r));
+    return r;
+}
+// the 32 MFMAs of one K-step for a wave's 128 x 64 tile (rows 64 w .. 64 w + 63);
+// kb: scaled mode's exponent bytes of the step's 64 rows (else null)
+template <typename T, bool SCALED>
+__device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int w, int lane, const uint32_t *kb) {
     const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4, L = lane & 15;
     const T *A = S;
     const uint32_t *W = reinterpret_cast<const uint32_t *>(S + AT_HS);
@@ -132,9 +145,16 @@ __device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int 
 #pragma unroll
     for (int s = 0; s < AT_TK / 16; ++s) {
         v8<T> b[2];
+        if constexpr (SCALED) {
+            const uint32_t elo = kb[4 * s + 2 * hh], ehi = kb[4 * s + 2 * hh + 1];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)                  // key blocks 16 s + 8 hh .. + 7 of the lane's row
-            b[nt] = expand_bits<T>(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
+            for (int nt = 0; nt < 2; ++nt)
+                b[nt] = expand_bits_scaled(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)), elo, ehi);
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)              // key blocks 16 s + 8 hh .. + 7 of the lane's row
+                b[nt] = expand_bits(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
+        }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int n = 32 * mt + 16 * (grp & 1) + 4 * (L & 3);              // state column of this lane's run
@@ -153,18 +173,21 @@ __device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int 
 
 }  // namespace
 
-// T: the 16-bit type of the states; O: f16 (rows scaled by 64 / m_i, staged
-// through LDS) or float (written from the accumulators as they are, 16 bytes
-// per lane)
-template <typename T, typename O>
+// T: the 16-bit type of the states; O: f16 (rows scaled by 64 / m_i, or in
+// scaled mode by 2^-oshift; staged through LDS) or float (written from the
+// accumulators as they are, 16 bytes per lane)
+template <typename T, typename O, bool SCALED>
 __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t *__restrict__ mbits,
                                                          const T *__restrict__ hs,
                                                          const int32_t *__restrict__ mcount,
+                                                         const uint8_t *__restrict__ kbyte, int oshift,
                                                          O *__restrict__ hhat, int Nb, int Nbc, int Nbp, int Lp,
                                                          int tiles_m, int tiles_n, long G, int per_xcd) {
     // four stages; separate arrays so that reads of one stage never wait for
     // loads still landing in another
     __shared__ __attribute__((aligned(1024))) T S0[AT_STAGE], S1[AT_STAGE], S2[AT_STAGE], S3[AT_STAGE];
+    // scaled mode: the exponent bytes of the head's Nbc rows
+    __shared__ __attribute__((aligned(16))) uint32_t Kb[SCALED ? AT_KB_MAX / 4 : 1];
 
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
@@ -176,6 +199,13 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wrow = row0 + 64 * wave;                   // first row of this wave
+    if constexpr (SCALED) {
+        // before the first loads into LDS, so that this wait covers only these;
+        // visible after the first barrier of the step loop
+        const uint8_t *kr = kbyte + bh * (long)Nbc;
+        for (int x = tid; x < Nbc / 16; x += 64 * AT_W)
+            *reinterpret_cast<Chunk *>(&Kb[4 * x]) = *reinterpret_cast<const Chunk *>(kr + 16 * x);
+    }
 
     // buffer resources over one head: Hs rows and indicator words past the
     // end read as zeros
@@ -218,7 +248,7 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * AT_VM));   // vmcnt(8)
         lds_barrier();
         at_issue(rh, rb, Sn, va, vw, wave, (uint32_t)(st + 3) * astep, (uint32_t)(st + 3) * wstep);
-        if (active && st < nst) at_compute(S, acc, wave, lane);
+        if (active && st < nst) at_compute<T, SCALED>(S, acc, wave, lane, SCALED ? &Kb[16 * st] : nullptr);
     };
     for (int st = 0; st < nst; st += 4) {
         stage(st, S0, S3);
@@ -229,26 +259,6 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
     __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
     lds_barrier();                                       // every wave is done with the stages
     if (!active) return;
-    if constexpr (sizeof(O) == 4) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int i = wrow + 32 * nt + l32;
-            if (i >= Nb) continue;
-            const int mc = mcount[bh * Nb + i];
-            const float sc = mc > 0 ? 64.f / (float)mc * kOneInv<T> : 0.f;
-            O *orow = hhat + (bh * Nb + i) * (long)Lp + col0;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 y = {acc[mt][nt][4 * g] * sc, acc[mt][nt][4 * g + 1] * sc,
-                                     acc[mt][nt][4 * g + 2] * sc, acc[mt][nt][4 * g + 3] * sc};
-                    *reinterpret_cast<f32x4 *>(orow + 32 * mt + 8 * g + 4 * hh) = y;
-                }
-        }
-        return;
-    }
-
     // epilogue: the wave's 32-row halves go through a private 8 KB LDS slice,
     // 8-byte unit u of row r at unit u ^ r (conflict-free both ways)
     static_assert(AT_W <= 8, "four stages hold the slices of up to eight waves");
@@ -257,8 +267,13 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int i = wrow + 32 * nt + l32;
-        const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
-        const float sc = mc > 0 ? 64.f / (float)mc * kOneInv<T> : 0.f;
+        float sc;
+        if constexpr (SCALED) {
+            sc = ldexpf(1.f, -oshift);
+        } else {
+            const int mc = (i < Nb) ? mcount[bh * Nb + i] : 0;
+            sc = mc > 0 ? 64.f / (float)mc * kOneInv : 0.f;
+        }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -403,14 +418,16 @@ hipError_t launch_assemble(const AssembleArgs &a, hipStream_t st) {
         const int tiles_n = (a.Nb + AT_TN - 1) / AT_TN;
         const long G = a.BH * tiles_m * tiles_n;
         const int per = (int)((G + 7) / 8);
-        if (a.bf16_f32)
-            assemble16_kernel<bf16, float><<<(unsigned)(8L * per), 64 * AT_W, 0, st>>>(
-                a.mbits, (const bf16 *)a.hs, a.mcount, (float *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G,
-                per);
-        else
-            assemble16_kernel<f16, f16><<<(unsigned)(8L * per), 64 * AT_W, 0, st>>>(
-                a.mbits, (const f16 *)a.hs, a.mcount, (f16 *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m, tiles_n, G,
-                per);
+        if (a.kbyte) {
+            if (a.Nbc > AT_KB_MAX) return hipErrorInvalidValue;
+            assemble16_kernel<f16, f16, true><<<(unsigned)(8L * per), 64 * AT_W, 0, st>>>(
+                a.mbits, (const f16 *)a.hs, nullptr, a.kbyte, a.oshift, (f16 *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp,
+                tiles_m, tiles_n, G, per);
+        } else {
+            assemble16_kernel<f16, f16, false><<<(unsigned)(8L * per), 64 * AT_W, 0, st>>>(
+                a.mbits, (const f16 *)a.hs, a.mcount, nullptr, 0, (f16 *)a.hhat, a.Nb, a.Nbc, a.Nbp, a.Lp, tiles_m,
+                tiles_n, G, per);
+        }
     }
     return hipGetLastError();
 }

@@ -23,8 +23,9 @@
 //   phi = softmax over channels: dx = phi * (dphi - phi . dphi).
 // Every product of the linear part runs on fp16 MFMA with fp32 accumulation;
 // operands derived from dO (dO, dh'_j, dv') carry a power of two per block
-// that puts the block's largest magnitude in [0.5, 1), and the per-row state
-// gradients are summed over the rows as bf16 pairs hi + lo.
+// that puts the block's largest magnitude in [0.5, 1); the per-row state
+// gradients dĤ'_i are stored as fp16 with such an exponent per row, and the
+// transposed sum applies the exponents in its 0/1 operand.
 #include "sla_device.h"
 #include "sla_launch.h"
 #include "tile_common.h"
@@ -35,6 +36,7 @@ namespace sla {
 
 namespace {
 constexpr float NEG_INF_B = -__builtin_inff();
+constexpr int EXP_ZERO = -(1 << 20);                     // exponent of an all-zero state-gradient row
 }
 
 // ---- transposed lists and indicator ------------------------------------------
@@ -60,22 +62,19 @@ __global__ __launch_bounds__(256) void bwd_tlists_kernel(const int8_t *__restric
     if (lane == 0) tcnt[t] = c;
 }
 
-// mbits[bh][w][j] (w < 2 Nbc / 32, j < Nbp): bit b set when key block j is
-// marginal for query block i = 32 (w mod Nbc / 32) + b (i, j < Nb): the
-// transposed marginal indicator as bits, its words repeated for the lo rows
-// of the state gradients; unit[bh][j] = 64 so that the product applies no
-// row scale
+// mbits[bh][w][j] (w < Nbc / 32, j < Nbp): bit b set when key block j is
+// marginal for query block i = 32 w + b (i, j < Nb): the transposed marginal
+// indicator as bits
 __global__ __launch_bounds__(256) void bwd_mbitsT_kernel(const int8_t *__restrict__ mask, long BH, int Nb, int Nbc,
-                                                         int Nbp, uint32_t *__restrict__ mbits,
-                                                         int32_t *__restrict__ unit) {
+                                                         int Nbp, uint32_t *__restrict__ mbits) {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    const int nw = 2 * Nbc / 32;
+    const int nw = Nbc / 32;
     if (t >= BH * nw * (long)Nbp) return;
     const int j = (int)(t % Nbp);
     const long r = t / Nbp;
     const int wd = (int)(r % nw);
     const long bh = r / nw;
-    const int i0 = 32 * (wd % (Nbc / 32));
+    const int i0 = 32 * wd;
     uint32_t bits = 0;
     if (j < Nb)
         for (int b = 0; b < 32; ++b) {
@@ -83,7 +82,30 @@ __global__ __launch_bounds__(256) void bwd_mbitsT_kernel(const int8_t *__restric
             if (i < Nb && mask[(bh * Nb + i) * (long)Nb + j] == 0) bits |= 1u << b;
         }
     mbits[t] = bits;
-    if (wd == 0 && j < Nb) unit[bh * Nb + j] = 64;
+}
+
+// one workgroup per head: R = the largest exponent of the head's state-
+// gradient rows; per row k its fp16 exponent byte for the transposed sum,
+// that of 2^(E_k - R + 14) (0 for rows more than 28 below R), and the
+// head's output exponent R + c, c = ceil(log2 Nbc)
+__global__ __launch_bounds__(256) void bwd_rowexp_kernel(const int32_t *__restrict__ dexp, int Nbc,
+                                                         uint8_t *__restrict__ kbyte, int32_t *__restrict__ hexp) {
+    __shared__ int Rw[4];
+    const long bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t *e = dexp + bh * (long)Nbc;
+    int r = EXP_ZERO;
+    for (int k = tid; k < Nbc; k += 256) r = max(r, e[k]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) r = max(r, __shfl_xor(r, o));
+    if (lane == 0) Rw[wave] = r;
+    __syncthreads();
+    const int R = max(max(Rw[0], Rw[1]), max(Rw[2], Rw[3]));
+    for (int k = tid; k < Nbc; k += 256) {
+        const int dlt = e[k] - R;
+        kbyte[bh * Nbc + k] = dlt >= -28 ? (uint8_t)((dlt + 29) << 2) : (uint8_t)0;
+    }
+    if (tid == 0) hexp[bh] = R + (32 - __clz(Nbc - 1));
 }
 
 __global__ __launch_bounds__(256) void bwd_zero_kernel(float *__restrict__ p, long n) {
@@ -438,12 +460,6 @@ __device__ __forceinline__ float pow2_scale(float m) {
     frexpf(m, &ex);
     return ldexpf(1.f, -max(ex, -125));
 }
-// x as the pair hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void split_store(bf16 *hi, bf16 *lo, long at, float x) {
-    const bf16 h = (bf16)x;
-    hi[at] = h;
-    lo[at] = (bf16)(x - (float)h);
-}
 }  // namespace
 
 // One workgroup of 4 waves per query block i (blocks past Nb and rows without
@@ -455,14 +471,16 @@ __device__ __forceinline__ void split_store(bf16 *hi, bf16 *lo, long at, float x
 //     tokens of half rh) and s X^T = H^T (s dO)^T (channels a of half ch);
 //     per token g = dO.y, e_a = X_a - g Ẑ_a, t = Pn.e (the two channel halves
 //     summed through LDS), dq_a += Pn_a (e_a - den t).
-//  3. matrix core: dĤ'_i = dO^T Pn / m_i, VALU: dẐ_i = -g^T Pn / m_i, both
-//     written as bf16 pairs (hi in row i, lo in row Nbc + i of the head).
+//  3. matrix core: dĤ'_i = dO^T Pn / m_i, VALU: dẐ_i = -g^T Pn / m_i; with
+//     M = f 2^E (f in [0.5, 1)) the row's largest magnitude, written as fp16
+//     values times 2^-E, and E (EXP_ZERO for a zero row) in dexp.
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ dout,
                                                              const f16 *__restrict__ hhat,
                                                              const int32_t *__restrict__ mcount, int Lp,
-                                                             float *__restrict__ dq, bf16 *__restrict__ dh2, long BH,
-                                                             int N, int Nb, int Nbc) {
+                                                             float *__restrict__ dq, f16 *__restrict__ dhr,
+                                                             int32_t *__restrict__ dexp, long BH, int N, int Nb,
+                                                             int Nbc) {
     constexpr int STR = D + 8;                           // padded row stride of the f16 tiles
     constexpr int CPR = D / 8, RPP = 256 / CPR, NP = 64 / RPP;
     constexpr int NCT = D / 64;                          // 32-channel tiles per channel half
@@ -477,14 +495,11 @@ __global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restr
     const int i = (int)(blk % Nbc);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4;
-    bf16 *hi = dh2 + (bh * 2 * Nbc + i) * (long)Lp;
-    bf16 *lo = hi + (long)Nbc * Lp;
+    f16 *dh = dhr + (bh * Nbc + i) * (long)Lp;
     const int mc = i < Nb ? mcount[bh * Nb + i] : 0;
     if (mc == 0) {
-        for (int x = tid; x < Lp / 8; x += 256) {
-            st_chunk(hi + 8 * x, zero_chunk());
-            st_chunk(lo + 8 * x, zero_chunk());
-        }
+        for (int x = tid; x < Lp / 8; x += 256) st_chunk(dh + 8 * x, zero_chunk());
+        if (tid == 0) dexp[bh * Nbc + i] = EXP_ZERO;
         return;
     }
     const f16 *hr = hhat + (bh * Nb + i) * (long)Lp;
@@ -641,31 +656,54 @@ __global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restr
 
     // 3. dĤ'[c][a] = sum_r dO[r][c] Pn[r][a] / m: tiles (ct, at), K = the 64 tokens
     const float osc = 1.f / ((float)mc * sc), inv_m = 1.f / (float)mc;
+    f32x16 acc[TPW];
+    float vmax = 0.f;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int x = wave * TPW + t, ct = x / (D / 32), at = x % (D / 32);
         const int nc = 32 * ct + 16 * (grp & 1), na = 32 * at + 16 * (grp & 1);
-        f32x16 acc;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int k0 = 16 * s + 8 * hh;
-            mma16(acc, cat8<f16>(lds_col4<f16>(Ds, STR, k0, nc, lane), lds_col4<f16>(Ds, STR, k0 + 4, nc, lane)),
+            mma16(acc[t], cat8<f16>(lds_col4<f16>(Ds, STR, k0, nc, lane), lds_col4<f16>(Ds, STR, k0 + 4, nc, lane)),
                   cat8<f16>(lds_col4<f16>(Pn, STR, k0, na, lane), lds_col4<f16>(Pn, STR, k0 + 4, na, lane)));
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int c = 32 * ct + 8 * (e >> 2) + 4 * hh + (e & 3);
-            split_store(hi, lo, (long)c * D + 32 * at + l32, acc[e] * osc);
+            acc[t][e] *= osc;
+            vmax = fmaxf(vmax, fabsf(acc[t][e]));
         }
     }
+    float z = 0.f;
     if (tid < D) {
-        float z = 0.f;
         for (int r2 = 0; r2 < 64; ++r2) z += Gr[r2] * (float)Pn[r2 * STR + tid];
-        split_store(hi, lo, D * D + tid, -z * inv_m);
+        z = -z * inv_m;
+        vmax = fmaxf(vmax, fabsf(z));
     }
-    for (int x = D * D + D + tid; x < Lp; x += 256) hi[x] = lo[x] = (bf16)0.f;
+    vmax = wave_max(vmax);
+    if (lane == 0) Red[wave] = vmax;                     // its earlier reads ended two barriers ago
+    __syncthreads();
+    const float M = fmaxf(fmaxf(Red[0], Red[1]), fmaxf(Red[2], Red[3]));
+    int E = EXP_ZERO;
+    if (M > 0.f) {
+        frexpf(M, &E);
+        E = min(max(E, -125), 125);
+    }
+    const float xs = M > 0.f ? ldexpf(1.f, -E) : 0.f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int x = wave * TPW + t, ct = x / (D / 32), at = x % (D / 32);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int c = 32 * ct + 8 * (e >> 2) + 4 * hh + (e & 3);
+            dh[(long)c * D + 32 * at + l32] = (f16)(acc[t][e] * xs);
+        }
+    }
+    if (tid < D) dh[D * D + tid] = (f16)(z * xs);
+    for (int x = D * D + D + tid; x < Lp; x += 256) dh[x] = (f16)0.f;
+    if (tid == 0) dexp[bh * Nbc + i] = E;
 }
 
 // Linear part, keys: persistent workgroups of D/16 waves over the key blocks
@@ -679,15 +717,18 @@ __global__ __launch_bounds__(256, 2) void bwd_lin_row_kernel(const bf16 *__restr
 //     (e tile x), dW tiles += s dv'^T V / s; VALU: dphi = (.)/s + dz,
 //     pd = phi.dphi (tiles summed through LDS), dk += phi (dphi - pd),
 //     dv += (.)/s.
+// dh'_j comes as fp16 values x with dh'_j = x 2^Q, Q the head's output
+// exponent of the transposed sum.
 template <int D>
 __global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-                                                            const float *__restrict__ w, const float *__restrict__ dhs,
-                                                            int Lp, float *__restrict__ dk, float *__restrict__ dv,
+                                                            const float *__restrict__ w, const f16 *__restrict__ dhs,
+                                                            const int32_t *__restrict__ hexp, int Lp,
+                                                            float *__restrict__ dk, float *__restrict__ dv,
                                                             float *__restrict__ dwp, long BH, int N, int Nb) {
     constexpr int NT = 4 * D, NW = NT / 64;              // threads, waves (2 tiles of tokens x D/32 of channels)
     constexpr int STR = D + 8;
     constexpr int CPR = D / 8, RPP = NT / CPR, NP = 64 / RPP;
-    constexpr int HPT = D * D / 4 / NT;                  // float4 of dh' per thread
+    constexpr int HPT = D * D / 8 / NT;                  // 8-value chunks of dh' per thread
     constexpr int TPW = (D / 32) * (D / 32) / NW;        // dW tiles per wave
     __shared__ __attribute__((aligned(16))) f16 Wh[D * STR];
     __shared__ __attribute__((aligned(16))) f16 Dh[D * STR];
@@ -711,17 +752,19 @@ __global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restri
     for (long blk = blockIdx.x; blk < total; blk += gridDim.x) {
         const long bh = blk / Nb;
         const int j = (int)(blk % Nb);
-        const float *hrow = dhs + blk * (long)Lp;
+        const f16 *hrow = dhs + blk * (long)Lp;
+        const int Q = hexp[bh];
         __syncthreads();                                 // the previous block's reads of the tiles are done
-        f32x4 hv[HPT];
+        Chunk hv[HPT];
         float hmax = 0.f;
 #pragma unroll
         for (int x = 0; x < HPT; ++x) {
-            hv[x] = *reinterpret_cast<const f32x4 *>(hrow + 4 * (tid + NT * x));
+            hv[x] = ld_chunk(hrow + 8 * (tid + NT * x));
+            const f16 *hx = reinterpret_cast<const f16 *>(&hv[x]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hmax = fmaxf(hmax, fabsf(hv[x][e]));
+            for (int e = 0; e < 8; ++e) hmax = fmaxf(hmax, fabsf((float)hx[e]));
         }
-        if (tid < D) Dz[tid] = hrow[D * D + tid];
+        if (tid < D) Dz[tid] = ldexpf((float)hrow[D * D + tid], Q);
         // 1. phi(k_u), v_u
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
@@ -764,14 +807,17 @@ __global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restri
         float bm = Red[0];
 #pragma unroll
         for (int x = 1; x < NW; ++x) bm = fmaxf(bm, Red[x]);
-        const float sc = pow2_scale(bm), isc = 1.f / sc;
+        // the fp16 copy x sc (exact: sc is a power of two that brings the
+        // largest |x| into [0.5, 1)); the true values are the copy / sc 2^Q
+        const float sc = pow2_scale(bm), isc = ldexpf(1.f / sc, Q);
 #pragma unroll
         for (int x = 0; x < HPT; ++x) {
-            const int e0 = 4 * (tid + NT * x);
-            v4<f16> h;
+            const int e0 = 8 * (tid + NT * x);
+            const f16 *hx = reinterpret_cast<const f16 *>(&hv[x]);
+            f16 h[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = (f16)(hv[x][e] * sc);
-            __builtin_memcpy(&Dh[(e0 / D) * STR + e0 % D], &h, sizeof(h));
+            for (int e = 0; e < 8; ++e) h[e] = (f16)((float)hx[e] * sc);
+            __builtin_memcpy(&Dh[(e0 / D) * STR + e0 % D], h, sizeof(h));
         }
         __syncthreads();
 
@@ -925,23 +971,27 @@ hipError_t launch_backward_dkv(const BackwardArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_backward_lin_rows(const BackwardArgs &a, hipStream_t st) {
-    // the transposed indicator bits and unit counts
-    const long nt = a.BH * (2 * a.Nbc / 32) * (long)a.Nbp;
-    bwd_mbitsT_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, st>>>(a.mask, a.BH, a.Nb, a.Nbc, a.Nbp, a.mbitsT, a.unit);
+    // the transposed indicator bits
+    const long nt = a.BH * (a.Nbc / 32) * (long)a.Nbp;
+    bwd_mbitsT_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, st>>>(a.mask, a.BH, a.Nb, a.Nbc, a.Nbp, a.mbitsT);
     const unsigned rows = (unsigned)(a.BH * a.Nbc);
     if (a.D == 64)
         bwd_lin_row_kernel<64><<<rows, 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.dout, (const f16 *)a.hhat,
-                                                     a.mcount, a.Lp, a.dq, (bf16 *)a.dh2, a.BH, a.N, a.Nb, a.Nbc);
+                                                     a.mcount, a.Lp, a.dq, (f16 *)a.dhr, a.dexp, a.BH, a.N, a.Nb,
+                                                     a.Nbc);
     else
         bwd_lin_row_kernel<128><<<rows, 256, 0, st>>>((const bf16 *)a.q, (const bf16 *)a.dout, (const f16 *)a.hhat,
-                                                      a.mcount, a.Lp, a.dq, (bf16 *)a.dh2, a.BH, a.N, a.Nb, a.Nbc);
+                                                      a.mcount, a.Lp, a.dq, (f16 *)a.dhr, a.dexp, a.BH, a.N, a.Nb,
+                                                      a.Nbc);
+    bwd_rowexp_kernel<<<(unsigned)a.BH, 256, 0, st>>>(a.dexp, a.Nbc, a.kbyte, a.hexp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // dh'_j = sum over the query blocks i with j marginal of (hi_i + lo_i):
-    // the 0/1 product over the 2 Nbc rows of hi and lo pairs
+    // dh'_j = sum over the query blocks i with j marginal of dĤ'_i: the 0/1
+    // product in scaled mode (each row's exponent in its B values)
     AssembleArgs as{};
-    as.mbits = a.mbitsT; as.hs = a.dh2; as.mcount = a.unit; as.hhat = a.dhs;
-    as.BH = a.BH; as.Nb = a.Nb; as.Nbc = 2 * a.Nbc; as.Nbp = a.Nbp; as.Lp = a.Lp; as.bf16_f32 = true;
+    as.mbits = a.mbitsT; as.hs = a.dhr; as.hhat = a.dhs; as.kbyte = a.kbyte;
+    as.oshift = 14 + (32 - __builtin_clz((unsigned)a.Nbc - 1));
+    as.BH = a.BH; as.Nb = a.Nb; as.Nbc = a.Nbc; as.Nbp = a.Nbp; as.Lp = a.Lp;
     return launch_assemble(as, st);
 }
 
@@ -955,11 +1005,11 @@ long backward_key_groups(long BH, int Nb, int D) {
 hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st) {
     const unsigned gk = (unsigned)backward_key_groups(a.BH, a.Nb, a.D);
     if (a.D == 64)
-        bwd_lin_key_kernel<64><<<gk, 256, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk, a.dv,
-                                                   a.dwp, a.BH, a.N, a.Nb);
+        bwd_lin_key_kernel<64><<<gk, 256, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, (const f16 *)a.dhs,
+                                                   a.hexp, a.Lp, a.dk, a.dv, a.dwp, a.BH, a.N, a.Nb);
     else
-        bwd_lin_key_kernel<128><<<gk, 512, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, a.dhs, a.Lp, a.dk,
-                                                    a.dv, a.dwp, a.BH, a.N, a.Nb);
+        bwd_lin_key_kernel<128><<<gk, 512, 0, st>>>((const bf16 *)a.k, (const bf16 *)a.v, a.w, (const f16 *)a.dhs,
+                                                    a.hexp, a.Lp, a.dk, a.dv, a.dwp, a.BH, a.N, a.Nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long n = (long)a.D * a.D;

@@ -45,7 +45,8 @@ struct AssembleArgs {
     long BH;
     int Nb, Nbc, Nbp, Lp;
     bool f32;
-    bool bf16_f32;           // bf16 states, bits indicator, float output (no row scale with counts of 64)
+    const uint8_t *kbyte;    // nullable: scaled mode, [BH][Nbc] fp16 exponent byte of each input row (0: zero row)
+    int oshift;              // scaled mode: output rows are the sums times 2^-oshift
 };
 
 struct FusedArgs {
@@ -112,10 +113,12 @@ struct BackwardArgs {
     float *dbuf;                      // [BH][64 Nb] D_r = dO_r . O_s,r
     uint16_t *tlist;                  // [BH][Nb][Nb] transposed critical lists
     int32_t *tcnt;                    // [BH][Nb]
-    uint32_t *mbitsT;                 // [BH][2 Nbc / 32][Nbp] transposed marginal indicator bits
-    int32_t *unit;                    // [BH][Nb] = 64
-    void *dh2;                        // [BH][2 Nbc][Lp] bf16 per-row state gradients (hi rows, then lo rows)
-    float *dhs;                       // [BH][Nb][Lp] per-key-block state gradients
+    uint32_t *mbitsT;                 // [BH][Nbc / 32][Nbp] transposed marginal indicator bits
+    void *dhr;                        // [BH][Nbc][Lp] f16 per-row state gradients x 2^-dexp
+    int32_t *dexp;                    // [BH][Nbc] their exponents
+    uint8_t *kbyte;                   // [BH][Nbc] fp16 exponent bytes of the rows for the transposed sum
+    int32_t *hexp;                    // [BH] output exponent Q of the transposed sum
+    void *dhs;                        // [BH][Nb][Lp] f16 per-key-block state gradients x 2^-Q
     float *dwp;                       // [backward_key_groups][D][D] per-workgroup partial sums of dW
     long BH;
     int N, Nb, Nbc, Nbp, Lp, D;

@@ -86,7 +86,11 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // so every value stays below 2^90.
     constexpr float TAU = 64.f;
     static_assert(KTILE * 2 >= D * KRS, "the marginal state fits the K ring");
-    __shared__ __attribute__((aligned(1024))) T Kk[2][KTILE];
+    static_assert(2 * 4 * (D / 64) * 64 * 16 <= KTILE * 2, "two waves' exchange fits a K slot");
+    // the two K slots are separate arrays, so that the reads of one slot do
+    // not wait for loads still landing in the other or in the V tile
+    __shared__ __attribute__((aligned(1024))) T Kk0[KTILE];
+    __shared__ __attribute__((aligned(1024))) T Kk1[KTILE];
     __shared__ __attribute__((aligned(1024))) T Vk[TILE];
     __shared__ __attribute__((aligned(16))) S Zl[D];        // the row's Ẑ_i
 
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const __amdgpu_buffer_rsrc_t r = blk_rsrc(k, blk_of(c));
 #pragma unroll
         for (int u = 0; u < KPW; ++u)
-            if (wave + 4 * u < KDMA) dma16(r, &Kk[slot][(wave + 4 * u) * 512], kdo[u], 0);
+            if (wave + 4 * u < KDMA) dma16(r, (slot ? Kk1 : Kk0) + (wave + 4 * u) * 512, kdo[u], 0);
     };
     auto load_v = [&](int c) __attribute__((always_inline)) {
         if (pad(c)) return;
@@ -185,10 +189,11 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     auto load_hhat = [&]() __attribute__((always_inline)) {
         constexpr int HDMA = D * KCPR / 64;              // 1 KB pieces of the padded D x D state (34 or 9)
         const __amdgpu_buffer_rsrc_t rh = make_rsrc(hr, (uint32_t)(D * D * sizeof(S)));
-        T *dst = &Kk[0][0];
+        // rows 0..63 (KCPR pieces of 1 KB) in the first slot, the rest in the second
         for (int t = wave; t < HDMA; t += 4) {
             const int pos = 64 * t + lane, row = pos / KCPR, ch = pos % KCPR;
-            dma16(rh, dst + t * 512, ch < D / 8 ? (uint32_t)(row * D * 2 + ch * 16) : 0x40000000u, 0);
+            T *dst = t < KCPR ? Kk0 + t * 512 : Kk1 + (t - KCPR) * 512;
+            dma16(rh, dst, ch < D / 8 ? (uint32_t)(row * D * 2 + ch * 16) : 0x40000000u, 0);
         }
         if (wave == 0 && lane < D / 8)
             dma16(make_rsrc(hr, (uint32_t)((D * D + D) * sizeof(S))), Zl, (uint32_t)(D * D * sizeof(S)) + 16 * lane, 0);
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const int j = blk_of(c);
         v8<T> ak[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ak[s] = ld8<T>(&Kk[slot][kbase + 16 * s]);
+        for (int s = 0; s < NS; ++s) ak[s] = ld8<T>((slot ? Kk1 : Kk0) + kbase + 16 * s);
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
@@ -323,14 +328,14 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         }
         den = half_swap_sum(den);
         rden = 1.f / den;
-        const S *Hs = reinterpret_cast<const S *>(&Kk[0][0]);
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
             const int c = 32 * (NCH * kh + t) + l32;
+            const S *Hs = reinterpret_cast<const S *>(c < 64 ? Kk0 : Kk1) + (c & 63) * KRS;
 #pragma unroll
             for (int r = 0; r < 16; ++r) yl[t][r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) mma16(yl[t], ld8<S>(&Hs[c * KRS + 16 * s + 8 * hh]), ph[s]);
+            for (int s = 0; s < NS; ++s) mma16(yl[t], ld8<S>(&Hs[16 * s + 8 * hh]), ph[s]);
         }
     }
     lds_barrier();                                       // the ring is free for the exchange
@@ -338,7 +343,8 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // merge the two key halves: wave kh keeps channel tiles NCH*kh .. +NCH-1.
     // Exchange area: 4*NCH f32x4 per lane and wave in Kk, m and l in Vk.
     l = half_swap_sum(l);                                // the row sum over the wave's 32 keys
-    float *xo = reinterpret_cast<float *>(&Kk[0][0]);
+    // waves 0, 1 exchange through the first slot, waves 2, 3 through the second
+    float *xo = reinterpret_cast<float *>(wave < 2 ? Kk0 : Kk1);
     float *xm = reinterpret_cast<float *>(&Vk[0]);       // [4 waves][64]
     float *xl = xm + 4 * 64;
     const int partner = wave ^ 1;
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4 y = {give[t][4 * g], give[t][4 * g + 1], give[t][4 * g + 2], give[t][4 * g + 3]};
-                *reinterpret_cast<f32x4 *>(xo + ((wave * 4 * NCH + 4 * t + g) * 64 + lane) * 4) = y;
+                *reinterpret_cast<f32x4 *>(xo + (((wave & 1) * 4 * NCH + 4 * t + g) * 64 + lane) * 4) = y;
             }
         xm[wave * 64 + lane] = m;
         xl[wave * 64 + lane] = l;
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         for (int t = 0; t < NCH; ++t)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 y = *reinterpret_cast<const f32x4 *>(xo + ((partner * 4 * NCH + 4 * t + g) * 64 + lane) * 4);
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(xo + (((partner & 1) * 4 * NCH + 4 * t + g) * 64 + lane) * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mine[t][4 * g + e] = (mine[t][4 * g + e] * as + y[e] * ao) * inv;
             }

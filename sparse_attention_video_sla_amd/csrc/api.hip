@@ -642,7 +642,7 @@ static sla_status bwd_layout(int B, int H, int N, int d, int block, double crit_
     o->o_s = take(sizeof(float) * BH * N * d);
     o->lse = take(sizeof(float) * BH * 64 * Nb);       // rows padded to whole blocks (aligned runs)
     o->dbuf = take(sizeof(float) * BH * 64 * Nb);
-    o->tlist = take(sizeof(uint16_t) * BH * Nb * Nb);
+    o->tlist = take(sizeof(int32_t) * BH * Nb * Nb);
     o->tcnt = take(sizeof(int32_t) * BH * Nb);
     o->mbitsT = take(sizeof(uint32_t) * BH * (L->Nbc / 32) * L->Nbp);
     o->dhr = take(sizeof(uint16_t) * BH * L->Nbc * L->Lp);
@@ -698,7 +698,7 @@ static sla_status backward_grads(const void *q, const void *k, const void *v, co
     a.crit = (const int32_t *)(ws + L.crit); a.kc = kc; a.mask = (const int8_t *)(ws + L.mask);
     a.hhat = ws + L.hhat; a.mcount = (const int32_t *)(ws + L.mcount);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbuf = (float *)(ws + o.dbuf);
-    a.tlist = (uint16_t *)(ws + o.tlist); a.tcnt = (int32_t *)(ws + o.tcnt);
+    a.tlist = (int32_t *)(ws + o.tlist); a.tcnt = (int32_t *)(ws + o.tcnt);
     a.mbitsT = (uint32_t *)(ws + o.mbitsT); a.dhr = ws + o.dhr; a.dexp = (int32_t *)(ws + o.dexp);
     a.kbyte = (uint8_t *)(ws + o.kbyte); a.hexp = (int32_t *)(ws + o.hexp);
     a.dhs = ws + o.dhs; a.dwp = (float *)(ws + o.dwp);

@@ -43,20 +43,20 @@ constexpr int EXP_ZERO = -(1 << 20);                     // exponent of an all-z
 
 // one wave per (head, key block j): the query blocks i with j critical, ascending
 __global__ __launch_bounds__(256) void bwd_tlists_kernel(const int8_t *__restrict__ mask, long BH, int Nb,
-                                                         uint16_t *__restrict__ tlist, int32_t *__restrict__ tcnt) {
+                                                         int32_t *__restrict__ tlist, int32_t *__restrict__ tcnt) {
     const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= BH * Nb) return;
     const int lane = threadIdx.x & 63;
     const long bh = t / Nb;
     const int j = (int)(t % Nb);
     const int8_t *m = mask + bh * Nb * (long)Nb + j;
-    uint16_t *out = tlist + t * (long)Nb;
+    int32_t *out = tlist + t * (long)Nb;
     int c = 0;
     for (int i0 = 0; i0 < Nb; i0 += 64) {
         const int i = i0 + lane;
         const bool hit = i < Nb && m[(long)i * Nb] == 1;
         const uint64_t bal = __ballot(hit);
-        if (hit) out[c + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)i;
+        if (hit) out[c + __popcll(bal & ((1ull << lane) - 1))] = i;
         c += __popcll(bal);
     }
     if (lane == 0) tcnt[t] = c;
@@ -130,8 +130,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
                                                         int per_xcd, int N, int Nb, float sl2, float scale) {
     using T = bf16;
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
-    __shared__ __attribute__((aligned(1024))) T Kk[2][TILE];
-    __shared__ __attribute__((aligned(1024))) T Vk[2][TILE];
+    // each slot of the K and V rings is an array of its own, so that reads of
+    // one slot do not wait for loads still landing in the other
+    __shared__ __attribute__((aligned(1024))) T Kk0[TILE];
+    __shared__ __attribute__((aligned(1024))) T Kk1[TILE];
+    __shared__ __attribute__((aligned(1024))) T Vk0[TILE];
+    __shared__ __attribute__((aligned(1024))) T Vk1[TILE];
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
     const long bh = logical / Nb;
@@ -176,8 +180,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
         const uint32_t off = (uint32_t)(64L * cl[c] * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) {
-            dma16(rk, &Kk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
-            dma16(rv, &Vk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
+            dma16(rk, (slot ? Kk1 : Kk0) + (wave * NBW + u) * 512, ok_[u] + off, 0);
+            dma16(rv, (slot ? Vk1 : Vk0) + (wave * NBW + u) * 512, ok_[u] + off, 0);
         }
     };
     f32x16 dqt[NCT];
@@ -192,11 +196,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) a[s] = ld8<T>(&Kk[slot][koff[s]]);
+        for (int s = 0; s < NS; ++s) a[s] = ld8<T>((slot ? Kk1 : Kk0) + koff[s]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16(sacc, a[s], qf[s]);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) a[s] = ld8<T>(&Vk[slot][koff[s]]);
+        for (int s = 0; s < NS; ++s) a[s] = ld8<T>((slot ? Vk1 : Vk0) + koff[s]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16(pacc, a[s], df[s]);
         v8<T> dsb[2];
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
             dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - Dr));
         }
         v8<T> at[NCT][2];
-        read_tr<T, D>(Kk[slot], kh, toff, at);
+        read_tr<T, D>(slot ? Kk1 : Kk0, kh, toff, at);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -235,7 +239,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
     }
     wait_vm0();
     // sum the two key halves: wave kh keeps channel tiles NCH*kh .. +NCH-1
-    float *xo = reinterpret_cast<float *>(&Kk[0][0]);     // [4 waves][NCH*4][64] f32x4
+    // [2 waves][NCH*4][64] f32x4: waves 0, 1 in the first K slot, 2, 3 in the second
+    float *xo = reinterpret_cast<float *>(wave < 2 ? Kk0 : Kk1);
+    static_assert(2 * NCH * 4 * 64 * 16 <= TILE * 2, "two waves' exchange fits a slot");
     f32x16 mine[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 y = {give[4 * g], give[4 * g + 1], give[4 * g + 2], give[4 * g + 3]};
-            *reinterpret_cast<f32x4 *>(xo + ((wave * NCH * 4 + c * 4 + g) * 64 + lane) * 4) = y;
+            *reinterpret_cast<f32x4 *>(xo + (((wave & 1) * NCH * 4 + c * 4 + g) * 64 + lane) * 4) = y;
         }
     }
     lds_barrier();
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 y = *reinterpret_cast<const f32x4 *>(xo + ((partner * NCH * 4 + c * 4 + g) * 64 + lane) * 4);
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(xo + (((partner & 1) * NCH * 4 + c * 4 + g) * 64 + lane) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) mine[c][4 * g + e] += y[e];
         }
@@ -285,14 +291,17 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                                          const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
                                                          const float *__restrict__ lse, const float *__restrict__ dbuf,
-                                                         const uint16_t *__restrict__ tlist,
+                                                         const int32_t *__restrict__ tlist,
                                                          const int32_t *__restrict__ tcnt, float *__restrict__ dk,
                                                          float *__restrict__ dv, long G, int per_xcd, int N, int Nb,
                                                          float sl2, float scale) {
     using T = bf16;
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
-    __shared__ __attribute__((aligned(1024))) T Qk[2][TILE];
-    __shared__ __attribute__((aligned(1024))) T Ok[2][TILE];
+    // each ring slot an array of its own (see the dQ kernel)
+    __shared__ __attribute__((aligned(1024))) T Qk0[TILE];
+    __shared__ __attribute__((aligned(1024))) T Qk1[TILE];
+    __shared__ __attribute__((aligned(1024))) T Ok0[TILE];
+    __shared__ __attribute__((aligned(1024))) T Ok1[TILE];
     __shared__ __attribute__((aligned(16))) v8<T> PB[4][4][64];     // [wave][pb0, pb1, ds0, ds1][lane]
     const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
@@ -330,14 +339,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict_
     const uint32_t head_bytes = (uint32_t)((long)N * D * sizeof(T));
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + bh * N * (long)D, head_bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(dout + bh * N * (long)D, head_bytes);
-    const uint16_t *tl = tlist + (bh * Nb + j) * (long)Nb;
+    // 32-bit entries: uniform, so they come through the scalar cache and no
+    // wait for them waits for the tile loads in flight
+    const int32_t *tl = tlist + (bh * Nb + j) * (long)Nb;
     const int cnt = tcnt[bh * Nb + j];
     auto load = [&](int c, int slot) __attribute__((always_inline)) {
         const uint32_t off = (uint32_t)(64L * tl[c] * D * sizeof(T));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) {
-            dma16(rq, &Qk[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
-            dma16(ro, &Ok[slot][(wave * NBW + u) * 512], ok_[u] + off, 0);
+            dma16(rq, (slot ? Qk1 : Qk0) + (wave * NBW + u) * 512, ok_[u] + off, 0);
+            dma16(ro, (slot ? Ok1 : Ok0) + (wave * NBW + u) * 512, ok_[u] + off, 0);
         }
     };
     f32x16 dvt[NCH], dkt[NCH];
@@ -345,30 +356,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict_
     for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dvt[ct][r] = dkt[ct][r] = 0.f;
-    auto produce = [&](int c, int slot) __attribute__((always_inline)) {
-        const int i = tl[c];
-        // the rows of the accumulator this lane holds (four runs of four,
-        // 16-byte aligned in the per-head rows of 64 Nb), their lse and D
-        float lr[16], dr[16];
-        const long rb = bh * (64L * Nb) + 64 * i + 32 * rh + 4 * hh;
+    // the rows of the accumulator this lane holds (four runs of four, 16-byte
+    // aligned in the per-head rows of 64 Nb), their lse and D; issued before
+    // the next tile's loads, so that waiting for them does not wait for those
+    auto fetch = [&](int c, f32x4 (&lv)[4], f32x4 (&dv4)[4]) __attribute__((always_inline)) {
+        const long rb = bh * (64L * Nb) + 64 * tl[c] + 32 * rh + 4 * hh;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 lv = *reinterpret_cast<const f32x4 *>(lse + rb + 8 * g);
-            const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dbuf + rb + 8 * g);
+            lv[g] = *reinterpret_cast<const f32x4 *>(lse + rb + 8 * g);
+            dv4[g] = *reinterpret_cast<const f32x4 *>(dbuf + rb + 8 * g);
+        }
+        __builtin_amdgcn_sched_barrier(0);               // keep them ahead of the tile loads
+    };
+    auto produce = [&](int c, int slot, const f32x4 (&lv)[4], const f32x4 (&dv4)[4]) __attribute__((always_inline)) {
+        const int i = tl[c];
+        float lr[16], dr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool ok = 64 * i + 32 * rh + 8 * g + 4 * hh + e < N;
-                lr[4 * g + e] = ok ? lv[e] : __builtin_inff();
-                dr[4 * g + e] = ok ? dv4[e] : 0.f;
+                lr[4 * g + e] = ok ? lv[g][e] : __builtin_inff();
+                dr[4 * g + e] = ok ? dv4[g][e] : 0.f;
             }
-        }
         f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma16(sacc, ld8<T>(&Qk[slot][koff[s]]), kf[s]);
+        for (int s = 0; s < NS; ++s) mma16(sacc, ld8<T>((slot ? Qk1 : Qk0) + koff[s]), kf[s]);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) mma16(pacc, ld8<T>(&Ok[slot][koff[s]]), vf[s]);
+        for (int s = 0; s < NS; ++s) mma16(pacc, ld8<T>((slot ? Ok1 : Ok0) + koff[s]), vf[s]);
         v8<T> pb[2], dsb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -391,8 +408,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict_
             for (int c2 = 0; c2 < NCH; ++c2) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const T *bo = &Ok[slot][(32 * r2 + 16 * ks) * D];
-                    const T *bq = &Qk[slot][(32 * r2 + 16 * ks) * D];
+                    const T *bo = (slot ? Ok1 : Ok0) + (32 * r2 + 16 * ks) * D;
+                    const T *bq = (slot ? Qk1 : Qk0) + (32 * r2 + 16 * ks) * D;
                     mma16(dvt[c2], cat8<T>(lds_tr_raw<T>(bo + tofc[c2][0]), lds_tr_raw<T>(bo + tofc[c2][1])),
                           ks ? p1 : p0);
                     mma16(dkt[c2], cat8<T>(lds_tr_raw<T>(bq + tofc[c2][0]), lds_tr_raw<T>(bq + tofc[c2][1])),
@@ -406,25 +423,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const bf16 *__restrict_
         wait_vm0();
         lds_barrier();
         int c = 0;
+        f32x4 lv[4], dv4[4];
         for (; c + 1 < cnt; c += 2) {
+            fetch(c, lv, dv4);
             load(c + 1, 1);
-            produce(c, 0);
+            produce(c, 0, lv, dv4);
             lds_barrier();
             consume(0);
             wait_vm0();
             lds_barrier();
-            if (c + 2 < cnt) load(c + 2, 0);
-            produce(c + 1, 1);
+            fetch(c + 1, lv, dv4);
+            // past the end it loads the last block again (slot 0 is free):
+            // every path then has the same loads in flight, which keeps the
+            // compiler's waits for the rows partial
+            load(min(c + 2, cnt - 1), 0);
+            produce(c + 1, 1, lv, dv4);
             lds_barrier();
             consume(1);
             wait_vm0();
             lds_barrier();
         }
         if (c < cnt) {
-            produce(c, 0);
+            fetch(c, lv, dv4);
+            produce(c, 0, lv, dv4);
             lds_barrier();
             consume(0);
         }
+        wait_vm0();                                      // no load into LDS outlives the loop
     }
     if (!kvalid) return;
     float *vrow = dv + (bh * N + krow) * (long)D;

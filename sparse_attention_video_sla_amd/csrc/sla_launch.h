@@ -111,7 +111,7 @@ struct BackwardArgs {
     const int32_t *mcount;            // [BH][Nb] marginal tokens per row
     float *dq, *dk, *dv, *dw;         // gradients
     float *dbuf;                      // [BH][64 Nb] D_r = dO_r . O_s,r
-    uint16_t *tlist;                  // [BH][Nb][Nb] transposed critical lists
+    int32_t *tlist;                   // [BH][Nb][Nb] transposed critical lists
     int32_t *tcnt;                    // [BH][Nb]
     uint32_t *mbitsT;                 // [BH][Nbc / 32][Nbp] transposed marginal indicator bits
     void *dhr;                        // [BH][Nbc][Lp] f16 per-row state gradients x 2^-dexp

@@ -151,9 +151,11 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // 8 rows below the first at the same swizzle, 8D elements further on
     int toff[NCT][2];
     tr_offsets<D, true>(lane, toff);
+    // accumulator ct holds output channel tile ct ^ (NCH kh): tiles 0 .. NCH-1
+    // are the channels this wave keeps after the merge, the others its partner's
     int tv[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) tv[ct] = toff[ct][0];
+    for (int ct = 0; ct < NCT; ++ct) tv[ct] = kh ? toff[ct ^ NCH][0] : toff[ct][0];
     // loads of a K tile into LDS: wave w takes the 1 KB pieces w, w + 4, ...;
     // lane l of piece t fills chunk 64 t + l of the padded tile, which is row
     // (64 t + l) / KCPR, chunk (64 t + l) % KCPR of the block (the last chunk
@@ -293,7 +295,9 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     lds_barrier();                                       // Ĥ_i and Ẑ_i visible
 
     // linear read-out for this wave's output channels (tiles NCH*kh ..):
-    // y = Ĥ_i phi(q) / (phi(q).Ẑ_i), Ĥ_i rows from LDS
+    // y = Ĥ_i phi(q) / (phi(q).Ẑ_i), Ĥ_i rows from LDS.  phi(q) = x / sum(x)
+    // with x = exp(q - max q); the sum cancels between the two, so x itself
+    // (in (0, 1], as fp16) takes phi's place.
     f32x16 yl[NCH];
     float rden = 0.f;
     if (lin) {
@@ -303,26 +307,15 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) mq = fmaxf(mq, to_f32<T>(qf[s][e]));
-        mq = half_swap_max(mq);
-        v8<S> ph[NS];                                    // exp(q - max), then phi(q)
-        float se = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = fast_exp2((to_f32<T>(qf[s][e]) - mq) * LOG2E);
-                se += x;
-                ph[s][e] = from_f32<S>(x);
-            }
-        se = half_swap_sum(se);
-        const float inv_se = 1.f / se;
+        mq = half_swap_max(mq) * LOG2E;
+        v8<S> ph[NS];
         float den = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const v8<S> hz = ld8<S>(&Zl[16 * s + 8 * hh]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                ph[s][e] = from_f32<S>(to_f32<S>(ph[s][e]) * inv_se);
+                ph[s][e] = from_f32<S>(fast_exp2(__builtin_fmaf(to_f32<T>(qf[s][e]), LOG2E, -mq)));
                 den += to_f32<S>(ph[s][e]) * to_f32<S>(hz[e]);
             }
         }
@@ -351,8 +344,8 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     f32x16 mine[NCH], give[NCH];
 #pragma unroll
     for (int t = 0; t < NCH; ++t) {
-        mine[t] = kh == 0 ? o[t] : o[NCH + t];
-        give[t] = kh == 0 ? o[NCH + t] : o[t];
+        mine[t] = o[t];
+        give[t] = o[NCH + t];
     }
     if (kc > 0) {
 #pragma unroll
@@ -374,6 +367,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         const float ao = (mm == NEG_INF) ? 0.f : fast_exp2(mo - mm);
         const float lt = l * as + lo * ao;
         const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+        const float sa = as * inv, so = ao * inv;
         // log-sum-exp of the row's sparse softmax in the kernel's log2 units
         // (P = exp2(s * log2(e) / sqrt(d) - lse)), +inf for a row with no key
         if (lse && kh == 0 && hh == 0 && qvalid) lse[bh * (64L * Nb) + qrow] = lt > 0.f ? mm + __log2f(lt) : __builtin_inff();
@@ -383,21 +377,28 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
             for (int g = 0; g < 4; ++g) {
                 const f32x4 y = *reinterpret_cast<const f32x4 *>(xo + (((partner & 1) * 4 * NCH + 4 * t + g) * 64 + lane) * 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mine[t][4 * g + e] = (mine[t][4 * g + e] * as + y[e] * ao) * inv;
+                for (int e = 0; e < 4; ++e) mine[t][4 * g + e] = __builtin_fmaf(mine[t][4 * g + e], sa, y[e] * so);
             }
     }
     if (kc == 0 && lse && kh == 0 && hh == 0 && qvalid) lse[bh * (64L * Nb) + qrow] = __builtin_inff();
 
+    // the output row's offset, formed again here (the empty asm hides the
+    // lane index's origin) rather than kept in registers through the loop
+    int lane_e = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_e));
+    const int hh_e = lane_e >> 5;
+    const long orow_at = (bh * N + 64 * i + 32 * qh + (lane_e & 31)) * (long)D;
+
     // the sparse part alone, for a backward pass that reuses this forward
     // (critical lists only)
     if (!SLOTS && os && qvalid) {
-        float *srow = os + (bh * N + qrow) * (long)D;
+        float *srow = os + orow_at;
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
             const int c0 = 32 * (NCH * kh + t);
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                store4s<float>(srow + c0 + 8 * g + 4 * hh, mine[t][4 * g], mine[t][4 * g + 1], mine[t][4 * g + 2],
+                store4s<float>(srow + c0 + 8 * g + 4 * hh_e, mine[t][4 * g], mine[t][4 * g + 1], mine[t][4 * g + 2],
                                mine[t][4 * g + 3]);
         }
     }
@@ -410,13 +411,13 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     }
 
     if (qvalid) {
-        TO *orow = out + (bh * N + qrow) * (long)D;
+        TO *orow = out + orow_at;
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
             const int c0 = 32 * (NCH * kh + t);
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                store4s<TO>(orow + c0 + 8 * g + 4 * hh, mine[t][4 * g], mine[t][4 * g + 1], mine[t][4 * g + 2],
+                store4s<TO>(orow + c0 + 8 * g + 4 * hh_e, mine[t][4 * g], mine[t][4 * g + 1], mine[t][4 * g + 2],
                             mine[t][4 * g + 3]);
         }
     }

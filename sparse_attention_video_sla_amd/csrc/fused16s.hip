@@ -127,17 +127,23 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         hb = 16 * (i & 1);
         if (pcount) kc = __builtin_amdgcn_readfirstlane(min(max(pcount[pair], 0), kc));
     }
-    // key block of list entry c, and its frame marks (0xF: padding)
-    auto blk_of = [&](int c) __attribute__((always_inline)) {
-        if constexpr (SLOTS) return min((int)((sl[c] >> hb) & 0xFFFu), Nb - 1);
-        else return cl[c];
+    // list entry c as a word (read once, where no LDS read is in flight: a
+    // scalar load's wait also drains those), its key block and its frame
+    // marks (0xF: padding)
+    auto ent = [&](int c) __attribute__((always_inline)) {
+        if constexpr (SLOTS) return sl[c];
+        else return (uint32_t)cl[c];
     };
-    auto marks_of = [&](int c) __attribute__((always_inline)) {
-        if constexpr (SLOTS) return (sl[c] >> (hb + 12)) & 0xFu;
+    auto blk_of = [&](uint32_t w) __attribute__((always_inline)) {
+        if constexpr (SLOTS) return min((int)((w >> hb) & 0xFFFu), Nb - 1);
+        else return (int)w;
+    };
+    auto marks_of = [&](uint32_t w) __attribute__((always_inline)) {
+        if constexpr (SLOTS) return (w >> (hb + 12)) & 0xFu;
         else return 0u;
     };
     // a padding half: this row has no block in the slot (no load, no work)
-    auto pad = [&](int c) __attribute__((always_inline)) { return SLOTS && marks_of(c) == 0xFu; };
+    auto pad = [&](uint32_t w) __attribute__((always_inline)) { return SLOTS && marks_of(w) == 0xFu; };
     const int qpart = (MARKS && fp > 0 && 32 * qh + l32 >= frame_split(i, fp)) ? 1 : 0;
     // A buffer resource per key block: a ragged last block, and the pad
     // chunks of the K tile (offsets past the resource), read zeros.
@@ -170,16 +176,16 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // which a 1 KB piece (4 or 8 rows) does not change: piece u is piece 0
     // plus u KB
     const uint32_t ov0 = off_klayout<D, true>(wave * NBW * 1024 + 16 * lane);
-    auto load_k = [&](int c, int slot) __attribute__((always_inline)) {
-        if (pad(c)) return;
-        const __amdgpu_buffer_rsrc_t r = blk_rsrc(k, blk_of(c));
+    auto load_k = [&](uint32_t w, int slot) __attribute__((always_inline)) {
+        if (pad(w)) return;
+        const __amdgpu_buffer_rsrc_t r = blk_rsrc(k, blk_of(w));
 #pragma unroll
         for (int u = 0; u < KPW; ++u)
             if (wave + 4 * u < KDMA) dma16(r, (slot ? Kk1 : Kk0) + (wave + 4 * u) * 512, kdo[u], 0);
     };
-    auto load_v = [&](int c) __attribute__((always_inline)) {
-        if (pad(c)) return;
-        const __amdgpu_buffer_rsrc_t r = blk_rsrc(v, blk_of(c));
+    auto load_v = [&](uint32_t w) __attribute__((always_inline)) {
+        if (pad(w)) return;
+        const __amdgpu_buffer_rsrc_t r = blk_rsrc(v, blk_of(w));
 #pragma unroll
         for (int u = 0; u < NBW; ++u) dma16(r, &Vk[(wave * NBW + u) * 512], ov0 + 1024 * u, 0);
     };
@@ -202,8 +208,10 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     };
     v8<T> pb[2];
     // S^T = K Q^T of block c and its softmax: P^T in pb
-    auto score = [&](int c, int slot) __attribute__((always_inline)) {
-        const int j = blk_of(c);
+    // (last: entry c is the list's last, the only one a critical list can
+    // have on the ragged last key block, the lists being ascending)
+    auto score = [&](uint32_t w, int slot, bool last) __attribute__((always_inline)) {
+        const int j = blk_of(w);
         v8<T> ak[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) ak[s] = ld8<T>((slot ? Kk1 : Kk0) + kbase + 16 * s);
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16(sacc, ak[s], qf[s]);
         if constexpr (MARKS) {
-            const uint32_t marks = marks_of(c);
+            const uint32_t marks = marks_of(w);
             if (marks != 0u) {                           // a frame boundary hides some keys
                 const int ks = fp > 0 ? frame_split(j, fp) : 64;
                 const uint32_t hide = marks >> (2 * qpart);
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
                 }
             }
         }
-        if (64 * j + 64 > N) {                           // ragged last block: keys past N score -inf
+        if ((SLOTS || last) && 64 * j + 64 > N) {        // ragged last block: keys past N score -inf
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = 64 * j + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -267,28 +275,35 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     // both and barrier (V(c) visible, the K slot of c free), load K(c+2)
     // into it, accumulate, barrier (the V tile free), load V(c+1).  Each
     // load has a whole phase or two to land.
-    auto block = [&](int c, int slot) __attribute__((always_inline)) {
-        const bool work = !pad(c);                       // uniform across the workgroup
-        if (work) score(c, slot);
+    // w0, w1: the words of entries c and c + 1; returns that of c + 2, read
+    // after the first barrier, where no LDS read is in flight
+    auto block = [&](int c, int slot, uint32_t w0, uint32_t w1) __attribute__((always_inline)) {
+        const bool work = !pad(w0);                      // uniform across the workgroup
+        if (work) score(w0, slot, c == kc - 1);
         wait_vm0();
         lds_barrier();
-        if (c + 2 < kc) load_k(c + 2, slot);
+        const uint32_t w2 = c + 2 < kc ? ent(c + 2) : 0u;
+        if (c + 2 < kc) load_k(w2, slot);
         if (work) accumulate();
         lds_barrier();
-        if (c + 1 < kc) load_v(c + 1);
+        if (c + 1 < kc) load_v(w1);
+        return w2;
     };
     if (kc > 0) {
-        load_k(0, 0);
-        if (kc > 1) load_k(1, 1);
+        uint32_t w0 = ent(0), w1 = kc > 1 ? ent(1) : 0u;
+        load_k(w0, 0);
+        if (kc > 1) load_k(w1, 1);
         wait_vm0();
-        load_v(0);
+        load_v(w0);
         lds_barrier();
         int c = 0;
         for (; c + 1 < kc; c += 2) {
-            block(c, 0);
-            block(c + 1, 1);
+            const uint32_t w2 = block(c, 0, w0, w1);
+            const uint32_t w3 = block(c + 1, 1, w1, w2);
+            w0 = w2;
+            w1 = w3;
         }
-        if (c < kc) block(c, 0);
+        if (c < kc) block(c, 0, w0, w1);
     }
     if (lin) load_hhat();                                // the K ring is free once the loop is done
     wait_vm0();                                          // no load into LDS outlives the loop

@@ -190,7 +190,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqt[ct][r] = 0.f;
     auto compute = [&](int c, int slot) __attribute__((always_inline)) {
-        const int j = cl[c];
+        // only a list's last block can be the ragged last key block (the
+        // lists are ascending); its list entry is read only there
+        const bool rag = c == kc - 1 && 64 * cl[c] + 64 > N;
         v8<T> a[NS];
         f32x16 sacc, pacc;
 #pragma unroll
@@ -204,11 +206,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const bf16 *__restrict__
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16(pacc, a[s], df[s]);
         v8<T> dsb[2];
+        if (rag) {
+            const int lim = N - 64 * cl[c];              // keys of the block below N
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 64 * j + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float p = key < N ? fast_exp2(__builtin_fmaf(sacc[r], sl2, -lse2)) : 0.f;
-            dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - Dr));
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float p = key < lim ? fast_exp2(__builtin_fmaf(sacc[r], sl2, -lse2)) : 0.f;
+                dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - Dr));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[r], sl2, -lse2));
+                dsb[r >> 3][r & 7] = from_f32<T>(p * (pacc[r] - Dr));
+            }
         }
         v8<T> at[NCT][2];
         read_tr<T, D>(slot ? Kk1 : Kk0, kh, toff, at);

@@ -279,6 +279,19 @@ static int lvsa_kmax(int Nb, int P, int frames_per_set) {
     return (int)std::min<long>(Nb, bound);
 }
 
+// Long slot schedules run in chunks (each workgroup one chunk of its row's
+// slots, chunk-major order, so that the workgroups resident on an XCD share
+// one chunk's tiles through its L2), merged by their log-sum-exp afterwards.
+static constexpr int LVSA_CHUNK_MIN = 256;               // slots per row from which chunks are used
+static constexpr int LVSA_NCHUNK = 4;
+static int lvsa_nchunk(int kmax) { return kmax >= LVSA_CHUNK_MIN ? LVSA_NCHUNK : 1; }
+// float partial outputs (sized for d = 128, the largest d) and log-sum-exps
+static size_t lvsa_chunk_bytes(long BH, int Nb, int nchunk) {
+    if (nchunk <= 1) return 0;
+    return align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb * 128) +
+           align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb);
+}
+
 static sla_status lvsa_shape(int B, int H, int N, int d, int block, int T, int *P) {
     sla_status st = check_shape(B, H, N, d, block, MAX_NB_LISTS);
     if (st != SLA_OK) return st;
@@ -297,8 +310,9 @@ sla_status sla_lvsa_workspace_size(int B, int H, int N, int T, int C, int W, siz
     st = lvsa_params(T, C, W, 0, &p, &f);
     if (st != SLA_OK) return st;
     const int Nb = (N + 63) / 64, Np = (Nb + 1) / 2;
-    *bytes = align256(sizeof(int32_t) * 2 * (size_t)T) + align256(sizeof(uint32_t) * (size_t)Np * lvsa_kmax(Nb, P, f)) +
-             align256(sizeof(int32_t) * (size_t)Np);
+    const int kmax = lvsa_kmax(Nb, P, f);
+    *bytes = align256(sizeof(int32_t) * 2 * (size_t)T) + align256(sizeof(uint32_t) * (size_t)Np * kmax) +
+             align256(sizeof(int32_t) * (size_t)Np) + lvsa_chunk_bytes((long)B * H, Nb, lvsa_nchunk(kmax));
     return SLA_OK;
 }
 
@@ -340,8 +354,19 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount; fa.bcast = true; fa.fp = P;
     fa.out = out; fa.BH = (long)B * H; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
+    const int nchunk = lvsa_nchunk(kmax);
+    float *part = nullptr, *plse = nullptr;
+    if (nchunk > 1) {
+        part = (float *)((char *)pcount + align256(sizeof(int32_t) * (size_t)Np));
+        plse = (float *)((char *)part + align256(sizeof(float) * (size_t)nchunk * fa.BH * 64 * Nb * 128));
+        fa.nchunk = nchunk;
+        fa.out = part; fa.lse = plse; fa.bf16_out = false;
+    }
     mark_stage(ev, 4, 0, s);
     st = device_status(sla::launch_fused16s(fa, s), "fused launch");
+    if (st == SLA_OK && nchunk > 1)
+        st = device_status(sla::launch_chunk_merge(part, plse, nchunk, fa.BH, N, Nb, d, out, out_dtype == SLA_BF16, s),
+                           "chunk merge launch");
     mark_stage(ev, 4, 1, s);
     return st;
 }

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
                                                           const int32_t *__restrict__ mcount, int Lp,
                                                           TO *__restrict__ out, float *__restrict__ lse,
                                                           float *__restrict__ os, long G,
-                                                          int per_xcd, int N, int Nb, float sl2) {
+                                                          int per_xcd, int N, int Nb, float sl2, int nchunk) {
     static_assert(__is_same(T, bf16), "bf16 inputs");
     constexpr int TILE = 64 * D, NS = D / 16, NCT = D / 32, NCH = NCT / 2, NBW = D / 32;
     // K tiles: rows padded by one 16-byte chunk (KRS elements), so that the
@@ -94,8 +94,20 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
     __shared__ __attribute__((aligned(1024))) T Vk[TILE];
     __shared__ __attribute__((aligned(16))) S Zl[D];        // the row's Ẑ_i
 
-    const long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    long logical = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= G) return;
+    // chunked schedules: workgroup order chunk-major, then (head, query
+    // block); chunk ch takes the ch-th of nchunk equal shares of its row
+    // pair's slots and writes its own normalized output and log-sum-exp
+    // (merged afterwards)
+    int chunk = 0;
+    if (SLOTS && nchunk > 1) {
+        const long rows = G / nchunk;
+        chunk = (int)(logical / rows);
+        logical -= (long)chunk * rows;
+        out += (long)chunk * rows * 64 * D;              // [chunk][BH][64 Nb][D] (whole blocks of rows)
+        lse += (long)chunk * rows * 64;
+    }
     const long bh = logical / Nb;
     const int i = (int)(logical % Nb);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -126,6 +138,11 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
         sl = slots + pair * (long)kc;
         hb = 16 * (i & 1);
         if (pcount) kc = __builtin_amdgcn_readfirstlane(min(max(pcount[pair], 0), kc));
+        if (nchunk > 1) {                                // equal shares of this row pair's slots
+            const int share = (kc + nchunk - 1) / nchunk, c0 = chunk * share;
+            sl += c0;
+            kc = max(0, min(kc, c0 + share) - c0);
+        }
     }
     // list entry c as a word (read once, where no LDS read is in flight: a
     // scalar load's wait also drains those), its key block and its frame
@@ -440,12 +457,13 @@ __global__ __launch_bounds__(256, 3) void fused16s_kernel(const T *__restrict__ 
 
 template <int D, typename TO, bool SLOTS, bool MARKS>
 static hipError_t launch_fused16s_t(const FusedArgs &a, hipStream_t st) {
-    const long G = a.BH * a.Nb;
+    const int nchunk = a.nchunk > 1 ? a.nchunk : 1;
+    const long G = nchunk * a.BH * a.Nb;
     const int per = (int)((G + 7) / 8);
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
     fused16s_kernel<bf16, f16, D, TO, SLOTS, MARKS><<<(unsigned)(8L * per), 256, 0, st>>>(
         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.crit, a.kc, a.slots, a.pcount, a.bcast ? 1 : 0,
-        a.fp, (const f16 *)a.hhat, a.mcount, a.Lp, (TO *)a.out, a.lse, a.os, G, per, a.N, a.Nb, sl2);
+        a.fp, (const f16 *)a.hhat, a.mcount, a.Lp, (TO *)a.out, a.lse, a.os, G, per, a.N, a.Nb, sl2, nchunk);
     return hipGetLastError();
 }
 

@@ -155,4 +155,58 @@ hipError_t launch_lvsa_slots(const LvsaParams &p, int P, int N, int Nb, const in
     return hipGetLastError();
 }
 
+// out[t] = sum_m 2^(lse_m - L) O_m / sum_m 2^(lse_m - L), L the largest
+// finite lse_m of the token (a chunk with lse = +inf had no key: weight 0;
+// a token with no key in any chunk gets zeros).  One thread per 4 channels.
+template <typename TO>
+__global__ __launch_bounds__(256) void chunk_merge_kernel(const float *__restrict__ part,
+                                                          const float *__restrict__ plse, int nchunk, long BH, int N,
+                                                          int Nb, int D, TO *__restrict__ out) {
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    const int c4 = D / 4;
+    if (t >= BH * N * c4) return;
+    const long row = t / c4;
+    const int c = (int)(t % c4) * 4;
+    const long bh = row / N, tok = row % N;
+    const long lstride = BH * 64L * Nb, pstride = lstride * D;
+    float L = -__builtin_inff();
+    for (int m = 0; m < nchunk; ++m) {
+        const float x = plse[m * lstride + bh * 64L * Nb + tok];
+        if (x < __builtin_inff()) L = fmaxf(L, x);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (L > -__builtin_inff()) {
+        for (int m = 0; m < nchunk; ++m) {
+            const float x = plse[m * lstride + bh * 64L * Nb + tok];
+            if (!(x < __builtin_inff())) continue;
+            const float w = __builtin_amdgcn_exp2f(x - L);
+            const f32x4 o = *reinterpret_cast<const f32x4 *>(part + m * pstride + row * D + c);
+            den += w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, o[e], acc[e]);
+        }
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= inv;
+    }
+    if constexpr (__is_same(TO, float)) {
+        *reinterpret_cast<f32x4 *>(out + row * D + c) = acc;
+    } else {
+        v4<bf16> y = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+        __builtin_memcpy(out + row * D + c, &y, sizeof(y));
+    }
+}
+
+hipError_t launch_chunk_merge(const float *part, const float *plse, int nchunk, long BH, int N, int Nb, int D,
+                              void *out, bool bf16_out, hipStream_t st) {
+    const long n = BH * N * (D / 4);
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (bf16_out)
+        chunk_merge_kernel<bf16><<<grid, 256, 0, st>>>(part, plse, nchunk, BH, N, Nb, D, (bf16 *)out);
+    else
+        chunk_merge_kernel<float><<<grid, 256, 0, st>>>(part, plse, nchunk, BH, N, Nb, D, (float *)out);
+    return hipGetLastError();
+}
+
 }  // namespace sla

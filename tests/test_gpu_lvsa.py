@@ -64,7 +64,10 @@ def test_lvsa_sets_bit_exact(sla):
     (1, 1, 12, 97, 64, 6, 0, 5),        # W = 0, ragged last block
     (1, 1, 1, 300, 128, 3, 0, 0),       # one frame: dense attention
     (1, 1, 4, 70, 128, 21, 3, 0),       # T_per = 1: every frame global
+    (1, 1, 30, 640, 64, 21, 3, 0),      # 300 slots per row: the chunked schedule
+    (1, 1, 31, 620, 128, 21, 3, 1),     # chunked, frames straddling blocks, ragged last block
 ])
+@pytest.mark.timeout(600)
 def test_forward_lvsa_all_rows(sla, B, H, T, P, d, C, W, s):
     say("lvsa", B, H, T, P, d, C, W, s)
     inp = make_inputs(B, H, (T, 1, P), d, "bf16", seed=T * P + s)

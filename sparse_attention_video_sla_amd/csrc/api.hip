@@ -279,17 +279,34 @@ static int lvsa_kmax(int Nb, int P, int frames_per_set) {
     return (int)std::min<long>(Nb, bound);
 }
 
-// Long slot schedules run in chunks (each workgroup one chunk of its row's
-// slots, chunk-major order, so that the workgroups resident on an XCD share
-// one chunk's tiles through its L2), merged by their log-sum-exp afterwards.
-static constexpr int LVSA_CHUNK_MIN = 256;               // slots per row from which chunks are used
-static constexpr int LVSA_NCHUNK = 4;
-static int lvsa_nchunk(int kmax) { return kmax >= LVSA_CHUNK_MIN ? LVSA_NCHUNK : 1; }
+// Long slot schedules run in shares (each workgroup one share of its row
+// pair's slots, share-major order, so that the workgroups resident on an
+// XCD use one share's tiles through its L2), merged by their log-sum-exp.
+// (from 256 slots per row: shorter schedules, such as the sliding tiles', ran
+// slower in shares, their tiles staying in L2 without them)
+static int slot_nchunk(int kmax) { return kmax >= 256 ? 4 : 1; }
 // float partial outputs (sized for d = 128, the largest d) and log-sum-exps
-static size_t lvsa_chunk_bytes(long BH, int Nb, int nchunk) {
+static size_t slot_chunk_bytes(long BH, int Nb, int nchunk) {
     if (nchunk <= 1) return 0;
     return align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb * 128) +
            align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb);
+}
+// the fused launch over a slot schedule, in shares when it is long enough;
+// the partial buffers follow `tail` in the workspace
+static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void *out, bool bf16_out, hipStream_t s) {
+    const int nchunk = slot_nchunk(kmax);
+    float *part = nullptr, *plse = nullptr;
+    if (nchunk > 1) {
+        part = (float *)tail;
+        plse = (float *)(tail + align256(sizeof(float) * (size_t)nchunk * fa.BH * 64 * fa.Nb * 128));
+        fa.nchunk = nchunk;
+        fa.out = part; fa.lse = plse; fa.bf16_out = false;
+    }
+    sla_status st = device_status(sla::launch_fused16s(fa, s), "fused launch");
+    if (st == SLA_OK && nchunk > 1)
+        st = device_status(sla::launch_chunk_merge(part, plse, nchunk, fa.BH, fa.N, fa.Nb, fa.D, out, bf16_out, s),
+                           "chunk merge launch");
+    return st;
 }
 
 static sla_status lvsa_shape(int B, int H, int N, int d, int block, int T, int *P) {
@@ -312,7 +329,7 @@ sla_status sla_lvsa_workspace_size(int B, int H, int N, int T, int C, int W, siz
     const int Nb = (N + 63) / 64, Np = (Nb + 1) / 2;
     const int kmax = lvsa_kmax(Nb, P, f);
     *bytes = align256(sizeof(int32_t) * 2 * (size_t)T) + align256(sizeof(uint32_t) * (size_t)Np * kmax) +
-             align256(sizeof(int32_t) * (size_t)Np) + lvsa_chunk_bytes((long)B * H, Nb, lvsa_nchunk(kmax));
+             align256(sizeof(int32_t) * (size_t)Np) + slot_chunk_bytes((long)B * H, Nb, slot_nchunk(kmax));
     return SLA_OK;
 }
 
@@ -354,19 +371,9 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount; fa.bcast = true; fa.fp = P;
     fa.out = out; fa.BH = (long)B * H; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
-    const int nchunk = lvsa_nchunk(kmax);
-    float *part = nullptr, *plse = nullptr;
-    if (nchunk > 1) {
-        part = (float *)((char *)pcount + align256(sizeof(int32_t) * (size_t)Np));
-        plse = (float *)((char *)part + align256(sizeof(float) * (size_t)nchunk * fa.BH * 64 * Nb * 128));
-        fa.nchunk = nchunk;
-        fa.out = part; fa.lse = plse; fa.bf16_out = false;
-    }
     mark_stage(ev, 4, 0, s);
-    st = device_status(sla::launch_fused16s(fa, s), "fused launch");
-    if (st == SLA_OK && nchunk > 1)
-        st = device_status(sla::launch_chunk_merge(part, plse, nchunk, fa.BH, N, Nb, d, out, out_dtype == SLA_BF16, s),
-                           "chunk merge launch");
+    st = slots_attention(fa, kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)Np), out,
+                         out_dtype == SLA_BF16, s);
     mark_stage(ev, 4, 1, s);
     return st;
 }
@@ -430,7 +437,8 @@ sla_status sla_sta_workspace_size(int B, int H, int F, int Hh, int Ww, int tf, i
     sla_status st = sta_shape(F, Hh, Ww, tf, th, tw, wf, wh, ww, &sh);
     if (st != SLA_OK) return st;
     const size_t Np = (size_t)(sh.Nb + 1) / 2;
-    *bytes = align256(sizeof(uint32_t) * Np * sh.kmax) + align256(sizeof(int32_t) * Np);
+    *bytes = align256(sizeof(uint32_t) * Np * sh.kmax) + align256(sizeof(int32_t) * Np) +
+             slot_chunk_bytes((long)B * H, sh.Nb, slot_nchunk(sh.kmax));
     return SLA_OK;
 }
 
@@ -467,7 +475,8 @@ sla_status sla_forward_sta(const void *q, const void *k, const void *v, sla_dtyp
     fa.out = out; fa.BH = (long)B * H; fa.N = sh.N; fa.Nb = sh.Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
     mark_stage(ev, 4, 0, s);
-    st = device_status(sla::launch_fused16s(fa, s), "fused launch");
+    st = slots_attention(fa, sh.kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)Np), out,
+                         out_dtype == SLA_BF16, s);
     mark_stage(ev, 4, 1, s);
     return st;
 }

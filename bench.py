@@ -303,9 +303,11 @@ def run_lvsa(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profile_traffic("fused16s_kernel", wl.name, "fused16s.hip"),
-                     "kernel": "fused16s_kernel<bf16,f16,128,float,slots,frame marks>", "flops_per_launch": flops,
+                     "kernel": "fused16s_kernel<bf16,f16,128,float,slots,frame marks>, 4 shares per row pair (merged apart)",
+                     "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
-        "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
+        "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)},
+                   "merge": {"ms": round(stage_ms["assemble"], 4)}},
     }
     if not args.no_cpu:
         from oracle import lvsa as olv
@@ -409,7 +411,8 @@ def run_sta(args):
                      "traffic": profile_traffic("fused16s_kernel", wl["name"], "fused16s.hip"),
                      "kernel": "fused16s_kernel<bf16,f16,128,float,slots> (tile schedule)", "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
-        "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)}},
+        "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)},
+                   "merge": {"ms": round(stage_ms["assemble"], 4)}},
     }
     if not args.no_cpu:
         from oracle import sta as osta

@@ -303,8 +303,9 @@ sla_status sla_mask_stats(const float *mass, const int8_t *mask, long rows, int 
  * of calls summed to *calls, and forgets them.  Events are created on first
  * use and kept per thread.  Disabled by default.  sla_forward_lists,
  * sla_forward_lvsa and sla_forward_sta calls are recorded too: stage 1 is
- * building their block schedule, stage 4 their attention kernel, the other
- * stages zero.  sla_backward calls record: 0 the forward recomputed inside,
+ * building their block schedule, stage 4 their attention kernel, stage 3
+ * the merge of its shares (a schedule of 256 or more slots per row pair
+ * runs in four shares; zero otherwise), the other stages zero.  sla_backward calls record: 0 the forward recomputed inside,
  * 1 the transposed lists and dQ of the sparse part, 2 dK and dV of the
  * sparse part, 3 the linear part's rows and transposed sums, 4 its keys and
  * dW; sla_backward_saved calls the same with stage 0 zero; sla_forward_save

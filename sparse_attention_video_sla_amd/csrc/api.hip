@@ -138,9 +138,10 @@ StageEvents *timed_call() {
 }
 
 // Calls over a given block schedule: stage 1 is building the schedule, stage
-// 4 the attention kernel; pool, states and assembly do not run (zero time).
+// 4 the attention kernel, stage 3 the merge of its shares (when it runs in
+// shares); pool and states do not run (zero time).
 void mark_unused_stages(StageEvents *ev, hipStream_t s) {
-    for (int i : {0, 2, 3}) {
+    for (int i : {0, 2}) {
         mark_stage(ev, i, 0, s);
         mark_stage(ev, i, 1, s);
     }
@@ -293,7 +294,8 @@ static size_t slot_chunk_bytes(long BH, int Nb, int nchunk) {
 }
 // the fused launch over a slot schedule, in shares when it is long enough;
 // the partial buffers follow `tail` in the workspace
-static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void *out, bool bf16_out, hipStream_t s) {
+static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void *out, bool bf16_out, hipStream_t s,
+                                  StageEvents *ev) {
     const int nchunk = slot_nchunk(kmax);
     float *part = nullptr, *plse = nullptr;
     if (nchunk > 1) {
@@ -302,10 +304,14 @@ static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void 
         fa.nchunk = nchunk;
         fa.out = part; fa.lse = plse; fa.bf16_out = false;
     }
+    mark_stage(ev, 4, 0, s);
     sla_status st = device_status(sla::launch_fused16s(fa, s), "fused launch");
+    mark_stage(ev, 4, 1, s);
+    mark_stage(ev, 3, 0, s);
     if (st == SLA_OK && nchunk > 1)
         st = device_status(sla::launch_chunk_merge(part, plse, nchunk, fa.BH, fa.N, fa.Nb, fa.D, out, bf16_out, s),
                            "chunk merge launch");
+    mark_stage(ev, 3, 1, s);
     return st;
 }
 
@@ -371,11 +377,8 @@ sla_status sla_forward_lvsa(const void *q, const void *k, const void *v, sla_dty
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount; fa.bcast = true; fa.fp = P;
     fa.out = out; fa.BH = (long)B * H; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
-    mark_stage(ev, 4, 0, s);
-    st = slots_attention(fa, kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)Np), out,
-                         out_dtype == SLA_BF16, s);
-    mark_stage(ev, 4, 1, s);
-    return st;
+    return slots_attention(fa, kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)Np), out,
+                           out_dtype == SLA_BF16, s, ev);
 }
 
 // ---- STA tiles -----------------------------------------------------------
@@ -474,11 +477,8 @@ sla_status sla_forward_sta(const void *q, const void *k, const void *v, sla_dtyp
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = sh.kmax; fa.pcount = pcount; fa.bcast = true;
     fa.out = out; fa.BH = (long)B * H; fa.N = sh.N; fa.Nb = sh.Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
-    mark_stage(ev, 4, 0, s);
-    st = slots_attention(fa, sh.kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)Np), out,
-                         out_dtype == SLA_BF16, s);
-    mark_stage(ev, 4, 1, s);
-    return st;
+    return slots_attention(fa, sh.kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)Np), out,
+                           out_dtype == SLA_BF16, s, ev);
 }
 
 sla_status sla_block_mass(const void *q, const void *k, sla_dtype in_dtype, int B, int H, int N, int d, int block,

@@ -130,11 +130,27 @@ __device__ __forceinline__ v8<f16> expand_bits_scaled(uint32_t x, uint32_t elo, 
     __builtin_memcpy(&r, d, sizeof(r));
     return r;
 }
+// per-lane LDS element offsets of the A fragment reads: abase[mt] is the
+// first of the 4 consecutive state columns n = 32 mt + 16 (grp & 1) +
+// 4 (L & 3) in key block 8 (grp >> 1) + (L >> 2) of a stage; the block's two
+// low bits (L >> 2) pick the chunk swizzle, which the further blocks 16 s +
+// 4 x of the same lane keep, so those reads sit at constant offsets
+__device__ __forceinline__ void at_abase(int lane, int (&abase)[4]) {
+    const int grp = lane >> 4, L = lane & 15, kb = 8 * (grp >> 1) + (L >> 2), sw = 4 * (kb & 3);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int n = 32 * mt + 16 * (grp & 1) + 4 * (L & 3);
+        abase[mt] = kb * AT_TM + 8 * ((n >> 3) ^ sw) + (n & 7);
+    }
+}
 // the 32 MFMAs of one K-step for a wave's 128 x 64 tile (rows 64 w .. 64 w + 63);
-// kb: scaled mode's exponent bytes of the step's 64 rows (else null)
+// kb: scaled mode's exponent bytes of the step's 64 rows (else null).  The A
+// fragment of the next (s, mt) is read before the two MFMAs of the current
+// one, so each read has two MFMAs to land.
 template <typename T, bool SCALED>
-__device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int w, int lane, const uint32_t *kb) {
-    const int l32 = lane & 31, hh = lane >> 5, grp = lane >> 4, L = lane & 15;
+__device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int w, int lane, const uint32_t *kb,
+                                           const int (&abase)[4]) {
+    const int l32 = lane & 31, hh = lane >> 5;
     const T *A = S;
     const uint32_t *W = reinterpret_cast<const uint32_t *>(S + AT_HS);
     uint32_t bw[2][2];                                   // word h of row nt: key blocks 32 h .. 32 h + 31
@@ -142,9 +158,8 @@ __device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int 
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) bw[nt][h] = W[AT_TN * h + 64 * w + 32 * nt + l32];
-#pragma unroll
-    for (int s = 0; s < AT_TK / 16; ++s) {
-        v8<T> b[2];
+    // key blocks 16 s + 8 hh .. + 7 of the lane's row nt as the B operand
+    auto bop = [&](int s, v8<T> (&b)[2]) __attribute__((always_inline)) {
         if constexpr (SCALED) {
             const uint32_t elo = kb[4 * s + 2 * hh], ehi = kb[4 * s + 2 * hh + 1];
 #pragma unroll
@@ -152,21 +167,27 @@ __device__ __forceinline__ void at_compute(const T *S, f32x16 (&acc)[4][2], int 
                 b[nt] = expand_bits_scaled(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)), elo, ehi);
         } else {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)              // key blocks 16 s + 8 hh .. + 7 of the lane's row
-                b[nt] = expand_bits(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
+            for (int nt = 0; nt < 2; ++nt) b[nt] = expand_bits(bw[nt][s >> 1] >> (8 * (2 * (s & 1) + hh)));
         }
+    };
+    auto aop = [&](int s, int mt) __attribute__((always_inline)) {
+        const T *p = A + abase[mt] + 16 * s * AT_TM;
+        return cat8<T>(lds_tr_raw<T>(p), lds_tr_raw<T>(p + 4 * AT_TM));
+    };
+    v8<T> b[2];
+    bop(0, b);
+    v8<T> a = aop(0, 0);
+#pragma unroll
+    for (int s = 0; s < AT_TK / 16; ++s) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int n = 32 * mt + 16 * (grp & 1) + 4 * (L & 3);              // state column of this lane's run
-            v4<T> h[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int k = 16 * s + 8 * (grp >> 1) + 4 * x + (L >> 2);      // key block within the step
-                h[x] = lds_tr_raw<T>(&A[k * AT_TM + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7)]);
-            }
-            const v8<T> a = cat8<T>(h[0], h[1]);
+            v8<T> an = a;
+            if (mt < 3) an = aop(s, mt + 1);
+            else if (s + 1 < AT_TK / 16) an = aop(s + 1, 0);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) mma16(acc[mt][nt], a, b[nt]);
+            if (mt == 3 && s + 1 < AT_TK / 16) bop(s + 1, b);
+            a = an;
         }
     }
 }
@@ -224,6 +245,8 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
         vw[u] = (uint32_t)(((long)(i / AT_W) * Nbp + row0 + 64 * (i % AT_W) + lane) * 4);
     }
     const uint32_t astep = (uint32_t)AT_TK * Lp * 2, wstep = (uint32_t)Nbp * 8;
+    int abase[4];
+    at_abase(lane, abase);
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -248,7 +271,7 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * AT_VM));   // vmcnt(8)
         lds_barrier();
         at_issue(rh, rb, Sn, va, vw, wave, (uint32_t)(st + 3) * astep, (uint32_t)(st + 3) * wstep);
-        if (active && st < nst) at_compute<T, SCALED>(S, acc, wave, lane, SCALED ? &Kb[16 * st] : nullptr);
+        if (active && st < nst) at_compute<T, SCALED>(S, acc, wave, lane, SCALED ? &Kb[16 * st] : nullptr, abase);
     };
     for (int st = 0; st < nst; st += 4) {
         stage(st, S0, S3);
@@ -284,12 +307,17 @@ __global__ __launch_bounds__(64 * AT_W, 2) void assemble16_kernel(const uint32_t
                 for (int e = 0; e < 4; ++e) y[e] = (O)(acc[mt][nt][4 * g + e] * sc);
                 __builtin_memcpy(&stg[l32 * AT_TM + 4 * (u ^ l32)], &y, sizeof(y));
             }
+        // row 2 x + hh of the staged half, unit l32; one running pointer over
+        // the rows (no 64-bit products per store)
+        const int r0 = wrow + 32 * nt + hh;
+        O *orow = hhat + (bh * Nb + r0) * (long)Lp + col0 + 4 * l32;
+        const long rstep = 2L * Lp;
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-            const int r = 2 * x + hh, u = l32;           // row r, unit u of the staged half
-            const int ir = wrow + 32 * nt + r;
-            const v4<O> y = ld4<O>(&stg[r * AT_TM + 4 * (u ^ r)]);
-            if (ir < Nb) __builtin_memcpy(hhat + (bh * Nb + ir) * (long)Lp + col0 + 4 * u, &y, sizeof(y));
+            const int r = 2 * x + hh;
+            const v4<O> y = ld4<O>(&stg[r * AT_TM + 4 * (l32 ^ r)]);
+            if (r0 + 2 * x < Nb) __builtin_memcpy(orow, &y, sizeof(y));
+            orow += rstep;
         }
     }
 }

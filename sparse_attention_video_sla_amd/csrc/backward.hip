@@ -961,15 +961,25 @@ __global__ __launch_bounds__(4 * D) void bwd_lin_key_kernel(const bf16 *__restri
     }
 }
 
-// dW = the sum of the linear-keys workgroups' partials, in ascending
-// workgroup order (the same bits on every run)
+// dW = the sum of the linear-keys workgroups' partials in a fixed order (the
+// same bits on every run): for 64 consecutive elements, wave w adds the
+// partials of the w-th contiguous quarter of the workgroups in ascending
+// order, and the four quarter sums are added in ascending order (four
+// independent chains per element, loads of whole 256-byte rows)
 __global__ __launch_bounds__(256) void bwd_dw_reduce_kernel(const float *__restrict__ part, int groups, long n,
                                                             float *__restrict__ dw) {
-    const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    if (t >= n) return;
+    __shared__ float qs[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long t = (long)blockIdx.x * 64 + lane;
+    const int per = (groups + 3) / 4, g0 = w * per, g1 = min(groups, g0 + per);
     float s = 0.f;
-    for (int g = 0; g < groups; ++g) s += part[(long)g * n + t];
-    dw[t] = s;
+    if (t < n) {
+#pragma unroll 8
+        for (int g = g0; g < g1; ++g) s += part[(long)g * n + t];
+    }
+    qs[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && t < n) dw[t] = ((qs[0][lane] + qs[1][lane]) + qs[2][lane]) + qs[3][lane];
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -1049,7 +1059,7 @@ hipError_t launch_backward_lin_keys(const BackwardArgs &a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long n = (long)a.D * a.D;
-    bwd_dw_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.dwp, (int)gk, n, a.dw);
+    bwd_dw_reduce_kernel<<<(unsigned)((n + 63) / 64), 256, 0, st>>>(a.dwp, (int)gk, n, a.dw);
     return hipGetLastError();
 }
 

@@ -303,7 +303,7 @@ def run_lvsa(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profile_traffic("fused16s_kernel", wl.name, "fused16s.hip"),
-                     "kernel": "fused16s_kernel<bf16,f16,128,float,slots,frame marks>, 4 shares per row pair (merged apart)",
+                     "kernel": "fused16s_kernel<bf16,f16,128,f16,slots,frame marks>, 4 shares per row pair, fp16 partial outputs (merged apart)",
                      "flops_per_launch": flops,
                      "avg_launch_ms": round(stage_ms["fused"], 4)},
         "stages": {"schedule": {"ms": round(stage_ms["classify"], 4)}, "fused": {"ms": round(stage_ms["fused"], 4)},

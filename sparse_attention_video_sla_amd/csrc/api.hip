@@ -286,10 +286,11 @@ static int lvsa_kmax(int Nb, int P, int frames_per_set) {
 // (from 256 slots per row: shorter schedules, such as the sliding tiles', ran
 // slower in shares, their tiles staying in L2 without them)
 static int slot_nchunk(int kmax) { return kmax >= 256 ? 4 : 1; }
-// float partial outputs (sized for d = 128, the largest d) and log-sum-exps
+// fp16 partial outputs (normalized per share, so |values| <= max |V|; sized
+// for d = 128, the largest d) and float log-sum-exps
 static size_t slot_chunk_bytes(long BH, int Nb, int nchunk) {
     if (nchunk <= 1) return 0;
-    return align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb * 128) +
+    return align256(sizeof(uint16_t) * (size_t)nchunk * BH * 64 * Nb * 128) +
            align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb);
 }
 // the fused launch over a slot schedule, in shares when it is long enough;
@@ -297,10 +298,11 @@ static size_t slot_chunk_bytes(long BH, int Nb, int nchunk) {
 static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void *out, bool bf16_out, hipStream_t s,
                                   StageEvents *ev) {
     const int nchunk = slot_nchunk(kmax);
-    float *part = nullptr, *plse = nullptr;
+    _Float16 *part = nullptr;
+    float *plse = nullptr;
     if (nchunk > 1) {
-        part = (float *)tail;
-        plse = (float *)(tail + align256(sizeof(float) * (size_t)nchunk * fa.BH * 64 * fa.Nb * 128));
+        part = (_Float16 *)tail;
+        plse = (float *)(tail + align256(sizeof(uint16_t) * (size_t)nchunk * fa.BH * 64 * fa.Nb * 128));
         fa.nchunk = nchunk;
         fa.out = part; fa.lse = plse; fa.bf16_out = false;
     }

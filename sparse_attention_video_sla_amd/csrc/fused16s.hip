@@ -52,6 +52,10 @@ template <> __device__ __forceinline__ void store4s<bf16>(bf16 *p, float a, floa
     v4<bf16> v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
     __builtin_memcpy(p, &v, sizeof(v));
 }
+template <> __device__ __forceinline__ void store4s<f16>(f16 *p, float a, float b, float c, float d) {
+    v4<f16> v = {(f16)a, (f16)b, (f16)c, (f16)d};
+    __builtin_memcpy(p, &v, sizeof(v));
+}
 
 }  // namespace
 
@@ -469,6 +473,11 @@ static hipError_t launch_fused16s_t(const FusedArgs &a, hipStream_t st) {
 
 template <bool SLOTS, bool MARKS>
 static hipError_t launch_fused16s_m(const FusedArgs &a, hipStream_t st) {
+    if constexpr (SLOTS) {                               // the shares' normalized partial outputs, fp16
+        if (a.nchunk > 1)
+            return a.D == 64 ? launch_fused16s_t<64, f16, SLOTS, MARKS>(a, st)
+                             : launch_fused16s_t<128, f16, SLOTS, MARKS>(a, st);
+    }
     if (a.bf16_out)
         return a.D == 64 ? launch_fused16s_t<64, bf16, SLOTS, MARKS>(a, st)
                          : launch_fused16s_t<128, bf16, SLOTS, MARKS>(a, st);

@@ -156,56 +156,66 @@ hipError_t launch_lvsa_slots(const LvsaParams &p, int P, int N, int Nb, const in
 }
 
 // out[t] = sum_m 2^(lse_m - L) O_m / sum_m 2^(lse_m - L), L the largest
-// finite lse_m of the token (a chunk with lse = +inf had no key: weight 0;
-// a token with no key in any chunk gets zeros).  One thread per 4 channels.
-template <typename TO>
-__global__ __launch_bounds__(256) void chunk_merge_kernel(const float *__restrict__ part,
-                                                          const float *__restrict__ plse, int nchunk, long BH, int N,
+// finite lse_m of the token (a share with lse = +inf had no key: weight 0;
+// a token with no key in any share gets zeros).  One thread per 8 channels;
+// the NC shares' log-sum-exps and 16-byte pieces are all loaded before any
+// is used.
+template <typename TO, int NC>
+__global__ __launch_bounds__(256) void chunk_merge_kernel(const f16 *__restrict__ part,
+                                                          const float *__restrict__ plse, long BH, int N,
                                                           int Nb, int D, TO *__restrict__ out) {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    const int c4 = D / 4;
-    if (t >= BH * N * c4) return;
-    const long row = t / c4;
-    const int c = (int)(t % c4) * 4;
+    const int c8 = D / 8;
+    if (t >= BH * N * c8) return;
+    const long row = t / c8;
+    const int c = (int)(t % c8) * 8;
     const long bh = row / N, tok = row % N;
     const long lstride = BH * 64L * Nb, pstride = lstride * D;
-    float L = -__builtin_inff();
-    for (int m = 0; m < nchunk; ++m) {
-        const float x = plse[m * lstride + bh * 64L * Nb + tok];
-        if (x < __builtin_inff()) L = fmaxf(L, x);
+    float x[NC];
+    v8<f16> o[NC];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+        x[m] = plse[m * lstride + bh * 64L * Nb + tok];
+        o[m] = ld8<f16>(part + m * pstride + row * D + c);
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
+    float L = -__builtin_inff();
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+        if (x[m] < __builtin_inff()) L = fmaxf(L, x[m]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (L > -__builtin_inff()) {
-        for (int m = 0; m < nchunk; ++m) {
-            const float x = plse[m * lstride + bh * 64L * Nb + tok];
-            if (!(x < __builtin_inff())) continue;
-            const float w = __builtin_amdgcn_exp2f(x - L);
-            const f32x4 o = *reinterpret_cast<const f32x4 *>(part + m * pstride + row * D + c);
+        float den = 0.f;
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            const float w = x[m] < __builtin_inff() ? __builtin_amdgcn_exp2f(x[m] - L) : 0.f;
             den += w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, o[e], acc[e]);
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)o[m][e], acc[e]);
         }
         const float inv = 1.f / den;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= inv;
+        for (int e = 0; e < 8; ++e) acc[e] *= inv;
     }
     if constexpr (__is_same(TO, float)) {
-        *reinterpret_cast<f32x4 *>(out + row * D + c) = acc;
+        *reinterpret_cast<f32x4 *>(out + row * D + c) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4 *>(out + row * D + c + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     } else {
-        v4<bf16> y = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+        v8<bf16> y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)acc[e];
         __builtin_memcpy(out + row * D + c, &y, sizeof(y));
     }
 }
 
-hipError_t launch_chunk_merge(const float *part, const float *plse, int nchunk, long BH, int N, int Nb, int D,
+hipError_t launch_chunk_merge(const f16 *part, const float *plse, int nchunk, long BH, int N, int Nb, int D,
                               void *out, bool bf16_out, hipStream_t st) {
-    const long n = BH * N * (D / 4);
+    if (nchunk != 4) return hipErrorInvalidValue;        // the slot schedules are split in 4 shares
+    const long n = BH * N * (D / 8);
     const unsigned grid = (unsigned)((n + 255) / 256);
     if (bf16_out)
-        chunk_merge_kernel<bf16><<<grid, 256, 0, st>>>(part, plse, nchunk, BH, N, Nb, D, (bf16 *)out);
+        chunk_merge_kernel<bf16, 4><<<grid, 256, 0, st>>>(part, plse, BH, N, Nb, D, (bf16 *)out);
     else
-        chunk_merge_kernel<float><<<grid, 256, 0, st>>>(part, plse, nchunk, BH, N, Nb, D, (float *)out);
+        chunk_merge_kernel<float, 4><<<grid, 256, 0, st>>>(part, plse, BH, N, Nb, D, (float *)out);
     return hipGetLastError();
 }
 

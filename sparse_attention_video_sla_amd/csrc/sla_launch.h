@@ -62,7 +62,7 @@ struct FusedArgs {
     float *lse;              // nullable: [BH][64 Nb] log-sum-exp of each row's sparse softmax (log2 units)
     float *os;               // nullable: [BH][N][D] float32 sparse part of the output (before the linear read-out)
     int nchunk;              // slot schedules: nchunk > 1 splits each row pair's slots into nchunk equal shares;
-                             // out and lse are then [nchunk][BH][64 Nb][D] float32, [nchunk][BH][64 Nb] per share
+                             // out and lse are then [nchunk][BH][64 Nb][D] fp16, [nchunk][BH][64 Nb] float32
     const void *hhat;
     const int32_t *mcount;   // nullable: no marginal blocks anywhere
     int Lp;
@@ -93,7 +93,7 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t st);     // float inputs
 hipError_t launch_fused16s(const FusedArgs &a, hipStream_t st);
 // out[t] = the chunks' normalized outputs weighted by 2^lse (the chunks' log2
 // masses; +inf: an empty chunk), over the rows t of [BH][N]
-hipError_t launch_chunk_merge(const float *part, const float *plse, int nchunk, long BH, int N, int Nb, int D,
+hipError_t launch_chunk_merge(const _Float16 *part, const float *plse, int nchunk, long BH, int N, int Nb, int D,
                               void *out, bool bf16_out, hipStream_t st);  // bf16 inputs: critical lists, or a slot schedule
 hipError_t launch_block_mass(const MassArgs &a, hipStream_t st);
 hipError_t launch_lists_to_slots(const int32_t *lists, const int32_t *counts, int kmax, long BH, int Nb,

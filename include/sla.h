@@ -34,7 +34,10 @@
  *     is launched; a failed launch returns SLA_ERR_DEVICE.  sla_last_error()
  *     gives a thread-local message for the last non-OK status of the thread.
  *   - Inputs must be finite.  BF16 inputs: the linear branch stages values in
- *     fp16, so |V| and |V W^T| must stay below 65504.
+ *     fp16, so |V| and |V W^T| must stay below 65504; so does |V| for the
+ *     slot-schedule entry points (lists, LVSA, sliding tiles) when a row
+ *     pair's schedule has 256 or more slots, whose shares' normalized
+ *     outputs are staged in fp16.
  *   - Reentrant.  Mutable state: per thread, the error message and the
  *     optional stage-timing events.  Every kernel of a call runs on the
  *     caller's stream, in order.  Results are

@@ -209,7 +209,9 @@ sla_status sla_backward_saved(const void *q, const void *k, const void *v, const
  *   out_dtype (F32 or BF16).  workspace: sla_lists_workspace_size() bytes,
  *   256-byte aligned.  Rows 2p and 2p+1 share a schedule of slots (blocks
  *   both list, then their other blocks side by side); each row's cost
- *   follows the number of slots of its pair. */
+ *   follows the number of slots of its pair.  With kmax >= 256 each pair's
+ *   slots run in four shares whose normalized outputs (fp16) and
+ *   log-sum-exps are merged afterwards (the workspace holds them). */
 sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes);
 sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dtype in_dtype, sla_dtype out_dtype,
                              int B, int H, int N, int d, int block, const int32_t *lists, const int32_t *counts,

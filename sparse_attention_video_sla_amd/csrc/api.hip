@@ -191,6 +191,43 @@ sla_status sla_stage_times(float *ms, int *calls) {
 
 int sla_version(void) { return 100; }
 
+// Long slot schedules run in shares (each workgroup one share of its row
+// pair's slots, share-major order, so that the workgroups resident on an
+// XCD use one share's tiles through its L2), merged by their log-sum-exp.
+// (from 256 slots per row: shorter schedules, such as the sliding tiles', ran
+// slower in shares, their tiles staying in L2 without them)
+static int slot_nchunk(int kmax) { return kmax >= 256 ? 4 : 1; }
+// fp16 partial outputs (normalized per share, so |values| <= max |V|; sized
+// for d = 128, the largest d) and float log-sum-exps
+static size_t slot_chunk_bytes(long BH, int Nb, int nchunk) {
+    if (nchunk <= 1) return 0;
+    return align256(sizeof(uint16_t) * (size_t)nchunk * BH * 64 * Nb * 128) +
+           align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb);
+}
+// the fused launch over a slot schedule, in shares when it is long enough;
+// the partial buffers follow `tail` in the workspace
+static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void *out, bool bf16_out, hipStream_t s,
+                                  StageEvents *ev) {
+    const int nchunk = slot_nchunk(kmax);
+    _Float16 *part = nullptr;
+    float *plse = nullptr;
+    if (nchunk > 1) {
+        part = (_Float16 *)tail;
+        plse = (float *)(tail + align256(sizeof(uint16_t) * (size_t)nchunk * fa.BH * 64 * fa.Nb * 128));
+        fa.nchunk = nchunk;
+        fa.out = part; fa.lse = plse; fa.bf16_out = false;
+    }
+    mark_stage(ev, 4, 0, s);
+    sla_status st = device_status(sla::launch_fused16s(fa, s), "fused launch");
+    mark_stage(ev, 4, 1, s);
+    mark_stage(ev, 3, 0, s);
+    if (st == SLA_OK && nchunk > 1)
+        st = device_status(sla::launch_chunk_merge(part, plse, nchunk, fa.BH, fa.N, fa.Nb, fa.D, out, bf16_out, s),
+                           "chunk merge launch");
+    mark_stage(ev, 3, 1, s);
+    return st;
+}
+
 sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes) {
     if (!bytes) return fail(SLA_ERR_INVALID_ARG, "bytes must not be NULL");
     sla_status st = check_shape(B, H, N, 128, 64, MAX_NB_LISTS);
@@ -198,7 +235,8 @@ sla_status sla_lists_workspace_size(int B, int H, int N, int kmax, size_t *bytes
     const int Nb = (N + 63) / 64;
     if (kmax < 1 || kmax > Nb) return fail(SLA_ERR_INVALID_ARG, "kmax must lie in [1, Nb] (got %d, Nb = %d)", kmax, Nb);
     const size_t pairs = (size_t)B * H * ((Nb + 1) / 2);
-    *bytes = align256(sizeof(uint32_t) * pairs * kmax) + align256(sizeof(int32_t) * pairs);
+    *bytes = align256(sizeof(uint32_t) * pairs * kmax) + align256(sizeof(int32_t) * pairs) +
+             slot_chunk_bytes((long)B * H, Nb, slot_nchunk(kmax));
     return SLA_OK;
 }
 
@@ -232,10 +270,8 @@ sla_status sla_forward_lists(const void *q, const void *k, const void *v, sla_dt
     fa.q = q; fa.k = k; fa.v = v; fa.slots = slots; fa.kc = kmax; fa.pcount = pcount;
     fa.out = out; fa.BH = BH; fa.N = N; fa.Nb = Nb; fa.D = d;
     fa.bf16_in = true; fa.bf16_out = out_dtype == SLA_BF16;
-    mark_stage(ev, 4, 0, s);
-    st = device_status(sla::launch_fused16s(fa, s), "fused launch");
-    mark_stage(ev, 4, 1, s);
-    return st;
+    return slots_attention(fa, kmax, (char *)pcount + align256(sizeof(int32_t) * (size_t)BH * ((Nb + 1) / 2)), out,
+                           out_dtype == SLA_BF16, s, ev);
 }
 
 // ---- LVSA frame-level sets --------------------------------------------------
@@ -278,43 +314,6 @@ sla_status sla_lvsa_sets(int T, int C, int W, int step, int32_t *sets, int32_t *
 static int lvsa_kmax(int Nb, int P, int frames_per_set) {
     const long bound = 2L * frames_per_set * ((P + 63) / 64 + 1);
     return (int)std::min<long>(Nb, bound);
-}
-
-// Long slot schedules run in shares (each workgroup one share of its row
-// pair's slots, share-major order, so that the workgroups resident on an
-// XCD use one share's tiles through its L2), merged by their log-sum-exp.
-// (from 256 slots per row: shorter schedules, such as the sliding tiles', ran
-// slower in shares, their tiles staying in L2 without them)
-static int slot_nchunk(int kmax) { return kmax >= 256 ? 4 : 1; }
-// fp16 partial outputs (normalized per share, so |values| <= max |V|; sized
-// for d = 128, the largest d) and float log-sum-exps
-static size_t slot_chunk_bytes(long BH, int Nb, int nchunk) {
-    if (nchunk <= 1) return 0;
-    return align256(sizeof(uint16_t) * (size_t)nchunk * BH * 64 * Nb * 128) +
-           align256(sizeof(float) * (size_t)nchunk * BH * 64 * Nb);
-}
-// the fused launch over a slot schedule, in shares when it is long enough;
-// the partial buffers follow `tail` in the workspace
-static sla_status slots_attention(sla::FusedArgs fa, int kmax, char *tail, void *out, bool bf16_out, hipStream_t s,
-                                  StageEvents *ev) {
-    const int nchunk = slot_nchunk(kmax);
-    _Float16 *part = nullptr;
-    float *plse = nullptr;
-    if (nchunk > 1) {
-        part = (_Float16 *)tail;
-        plse = (float *)(tail + align256(sizeof(uint16_t) * (size_t)nchunk * fa.BH * 64 * fa.Nb * 128));
-        fa.nchunk = nchunk;
-        fa.out = part; fa.lse = plse; fa.bf16_out = false;
-    }
-    mark_stage(ev, 4, 0, s);
-    sla_status st = device_status(sla::launch_fused16s(fa, s), "fused launch");
-    mark_stage(ev, 4, 1, s);
-    mark_stage(ev, 3, 0, s);
-    if (st == SLA_OK && nchunk > 1)
-        st = device_status(sla::launch_chunk_merge(part, plse, nchunk, fa.BH, fa.N, fa.Nb, fa.D, out, bf16_out, s),
-                           "chunk merge launch");
-    mark_stage(ev, 3, 1, s);
-    return st;
 }
 
 static sla_status lvsa_shape(int B, int H, int N, int d, int block, int T, int *P) {

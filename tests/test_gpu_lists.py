@@ -118,3 +118,33 @@ def test_forward_lists_full_size_sampled(sla):
     for x, (bh, i) in enumerate(rows):
         r0, r1 = 64 * i, min(N, 64 * (i + 1))
         check(got[bh, r0:r1], ref[x, :r1 - r0])
+
+
+def test_forward_lists_shares_with_keyless_shares(sla):
+    """A schedule of 256 or more slots per row pair runs in four shares whose
+    normalized outputs (fp16) are merged by their log-sum-exps.  Row 0 lists
+    300 blocks; row 1 lists 4 of them, which the pair's schedule places first,
+    so row 1 has no key in three of the four shares (weight 0 there); row 2
+    lists 260 blocks beside an empty row 3, whose output stays zero in every
+    share; the ragged last block is listed by row 0."""
+    N, d, kmax = 64 * 320 - 37, 64, 300
+    Nb = -(-N // 64)
+    say("lists in shares", N, d, kmax)
+    inp = make_inputs(1, 1, (1, 1, N), d, "bf16", seed=41)
+    rng = np.random.default_rng(41)
+    a = np.sort(np.append(rng.choice(Nb - 1, size=299, replace=False), Nb - 1)).astype(np.int32)
+    rows = {0: a, 1: a[[0, 5, 17, 42]], 2: np.sort(rng.choice(Nb, size=260, replace=False)).astype(np.int32),
+            3: np.zeros(0, np.int32)}
+    lists = np.zeros((1, 1, Nb, kmax), np.int32)
+    counts = np.zeros((1, 1, Nb), np.int32)
+    for i in range(Nb):
+        sel = rows.get(i)
+        if sel is None:
+            sel = np.sort(rng.choice(Nb, size=int(rng.integers(1, 9)), replace=False)).astype(np.int32)
+        lists[0, 0, i, :len(sel)] = sel
+        counts[0, 0, i] = len(sel)
+    out = sla.forward_lists(dev(inp.q), dev(inp.k), dev(inp.v), torch.from_numpy(lists).cuda(),
+                            torch.from_numpy(counts).cuda())
+    torch.cuda.synchronize()
+    check(out, ol.attention_lists(inp.q, inp.k, inp.v, lists, counts))
+    assert float(out[0, 0, 192:256].abs().max()) == 0.0

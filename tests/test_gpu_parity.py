@@ -199,6 +199,14 @@ SMALL = [
     (1, 1, 2080, 128, "bf16", 0.05, 0.1),
     (2, 2, 1100, 64, "bf16", 0.3, 0.2),
     (1, 1, 1050, 128, "bf16", 1.0, 0.0),
+    # degenerate sizes: one token (Nb = 1, its only block critical), one
+    # ragged block, a last block of one token, and linear attention over
+    # three blocks, the last of one token
+    (1, 2, 1, 128, "bf16", 0.05, 0.10),
+    (1, 1, 37, 64, "f32", 0.05, 0.10),
+    (1, 2, 65, 128, "bf16", 0.5, 0.5),
+    (1, 1, 65, 64, "f32", 1.0, 0.0),
+    (2, 1, 129, 64, "bf16", 0.0, 0.0),
 ]
 
 

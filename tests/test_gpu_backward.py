@@ -64,6 +64,11 @@ def check(name, g, ref):
     (1, 1, 600, 64, 0.0, 0.5),      # no critical block: linear branch only
     (1, 1, 2048, 128, 0.05, 0.10),  # the default fractions
     (2, 2, 700, 64, 0.2, 0.3),      # dW summed over batch and heads, ragged
+    # degenerate sizes (a single token is left out: its dq and dk are exactly
+    # zero, which products rounded to bf16 cannot cancel to the bit)
+    (1, 1, 65, 64, 0.5, 0.5),       # two blocks, the last of one token, no marginal block
+    (2, 1, 129, 128, 0.0, 0.0),     # linear only over three blocks, one-token tail
+    (1, 1, 37, 64, 1.0, 0.0),       # one ragged block, dense
 ])
 def test_backward_matches_oracle(sla, B, H, N, d, rc, rn):
     say("backward", B, H, N, d, rc, rn)
